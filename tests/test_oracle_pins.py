@@ -1,0 +1,458 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Each oracle function is checked against hand-derived fixtures (tests/golden),
+closed forms, exact rational brute force, an independent encoder, or a textbook
+sort.  ``test_mutants_fail`` plants plausible mistakes in copies of the oracle's
+functions (on the CPU) and shows that each one fails at least one pin.
+"""
+
+from __future__ import annotations
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import w4ref
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------------------- pin suites
+# Each suite takes the implementation under test and returns a list of failures, so the
+# same suite judges the real oracle (must be empty) and the planted mutants (must not).
+
+
+def pins_pack(pack, unpack):
+    fails = []
+    for c in _gold("pack_worked.json")["cases"]:
+        q = np.array([c["codes"]], dtype=np.uint8)
+        want = int(c["word"], 16)
+        got = int(np.asarray(pack(q))[0, 0])
+        if got != want:
+            fails.append(f"pack {c['codes']} -> {got:#x} != {want:#x}")
+        back = np.asarray(unpack(np.array([[want]], dtype=np.uint32)))[0].tolist()
+        if back != c["codes"]:
+            fails.append(f"unpack {want:#x} -> {back}")
+    return fails
+
+
+def _pattern(spec, k):
+    kind, *arg = spec.split()
+    kk = np.arange(k)
+    if kind == "const":
+        return np.full(k, float(arg[0]))
+    if kind == "mod16":
+        return (kk % 16).astype(float)
+    if kind == "rev16":
+        return (15 - kk % 16).astype(float)
+    if kind == "alt":
+        return np.where(kk % 2 == 0, 1.0, -1.0)
+    if kind == "onehot":
+        v = np.zeros(k)
+        v[int(arg[0])] = 1.0
+        return v
+    raise ValueError(spec)
+
+
+def gold_gemv_cases():
+    for c in _gold("gemv_handworked.json")["cases"]:
+        k = c["K"]
+        q = _pattern(c["q"], k).astype(np.uint8)[None, :]
+        s = np.array([c["s"]], dtype=np.float16)
+        b = np.array([c["b"]], dtype=np.float16)
+        x = np.stack([_pattern(p, k) for p in c["x"]]).astype(np.float16)
+        yield c["name"], q, s, b, x, np.array(c["y"], dtype=np.float64)[:, None]
+
+
+def pins_gemv(gemv, pack):
+    fails = []
+    for name, q, s, b, x, y_want in gold_gemv_cases():
+        y, _ = gemv(pack(q), s, b, x)
+        if not np.array_equal(np.asarray(y), y_want):
+            fails.append(f"{name}: {np.asarray(y).ravel()} != {y_want.ravel()}")
+    return fails
+
+
+def pins_dequant(dequant_f16_t, pack):
+    fails = []
+    for c in _gold("f16_dequant.json")["cases"]:
+        # one row, one group: the case's code sits at k = 5, all other codes are 0
+        q = np.zeros((1, 64), dtype=np.uint8)
+        q[0, 5] = c["q"]
+        s = np.array([[int(c["s"], 16)]], dtype=np.uint16).view(np.float16)
+        b = np.array([[int(c["b"], 16)]], dtype=np.uint16).view(np.float16)
+        wt = np.asarray(dequant_f16_t(pack(q), s, b))
+        if wt.shape != (64, 1):
+            fails.append(f"shape {wt.shape}")
+            continue
+        got = int(wt[5, 0])
+        if got != int(c["w"], 16):
+            fails.append(f"s={c['s']} q={c['q']} b={c['b']}: {got:#06x} != {c['w']}")
+        if int(wt[0, 0]) != int(c["b"], 16):
+            fails.append(f"q=0 -> {int(wt[0, 0]):#06x} != b {c['b']}")
+    return fails
+
+
+def pins_topk(topk):
+    cases = [
+        ([3.0, 1.0, 3.0, 2.0], 2, [0, 2]),
+        ([-0.0, 0.0, -1.0], 2, [0, 1]),
+        ([0.0, -0.0, 0.0, -0.0], 4, [0, 1, 2, 3]),
+        ([5.0] * 5, 3, [0, 1, 2]),
+        ([1.0, 2.0, 3.0, 4.0, 5.0], 5, [4, 3, 2, 1, 0]),
+        ([5.0, 4.0, 3.0, 2.0, 1.0], 3, [0, 1, 2]),
+        ([1.0, 7.0, 7.0, 2.0, 7.0, 3.0], 2, [1, 2]),
+        ([-3.0, -1.0, -2.0], 1, [1]),
+    ]
+    fails = []
+    for row, k, want in cases:
+        idx, val = topk(np.array([row], dtype=np.float32), k)
+        if np.asarray(idx)[0].tolist() != want:
+            fails.append(f"{row} k={k}: {np.asarray(idx)[0].tolist()} != {want}")
+        if np.asarray(val)[0].tolist() != [row[i] for i in want]:
+            fails.append(f"{row} k={k}: values")
+    return fails
+
+
+def test_pins_pass_on_oracle():
+    assert pins_pack(oracle.pack, oracle.unpack) == []
+    assert pins_gemv(oracle.gemv_ref, oracle.pack) == []
+    assert pins_dequant(oracle.dequant_f16_t, oracle.pack) == []
+    assert pins_topk(oracle.topk_ref) == []
+
+
+# ------------------------------------------------------------------------------- pack
+
+
+def test_pack_roundtrip_all_nibbles_all_positions():
+    # every code value in every position of the word
+    q = np.zeros((16 * 8, 8), dtype=np.uint8)
+    for v in range(16):
+        for i in range(8):
+            q[v * 8 + i, i] = v
+    w = oracle.pack(q)
+    for v in range(16):
+        for i in range(8):
+            assert int(w[v * 8 + i, 0]) == v << (4 * i)
+    assert np.array_equal(oracle.unpack(w), q)
+
+
+def test_pack_roundtrip_random():
+    q = synth.codes(37, 64 * 5, seed=1)
+    assert np.array_equal(oracle.unpack(oracle.pack(q)), q)
+    words = np.random.default_rng(2).integers(0, 2**32, size=(1000, 1000), dtype=np.uint32)
+    assert np.array_equal(oracle.pack(oracle.unpack(words)), words)
+
+
+def test_pack_numpy_matches_python_loop():
+    q = synth.codes(5, 128, seed=3)
+    assert oracle.pack(q).tolist() == oracle.pack_loop(q.tolist())
+    w = oracle.pack(q)
+    assert oracle.unpack(w).tolist() == oracle.unpack_loop(w.tolist())
+
+
+def test_pack_keeps_low_nibble_only():
+    q = np.array([[16, 17, 255, 0, 0, 0, 0, 31]], dtype=np.uint8)
+    assert int(oracle.pack(q)[0, 0]) == int(oracle.pack(q & 0xF)[0, 0]) == 0xF0000F10
+
+
+# ---------------------------------------------------------------------------- f16 + dequant
+
+
+def test_f16_encoder_matches_struct():
+    r = np.random.default_rng(4)
+    vals = np.concatenate([
+        r.standard_normal(20000) * 10.0 ** r.integers(-8, 4, 20000),
+        # exact midpoints between neighbouring f16 values, and points just off them
+        (np.arange(-2000, 2000) + 0.5) * 2.0 ** -10,
+        (np.arange(-2000, 2000) + 0.5) * 2.0 ** -24,
+        (np.arange(1, 4000) + 0.5) * 2.0 ** -24 + 2.0 ** -60,
+        [0.0, -0.0, 65504.0, -65504.0, 2.0 ** -24, 2.0 ** -25, 2.0 ** -26, 3 * 2.0 ** -26],
+    ])
+    assert np.array_equal(oracle.f16_bits(vals), oracle.f16_bits_struct(vals))
+
+
+def test_dequant_exact_matches_fraction_bruteforce():
+    q, s, b = synth.w4_weights(3, 128, seed=5)
+    w = oracle.dequant_exact(oracle.pack(q), s, b)
+    for n in range(3):
+        for k in range(128):
+            g = k // 64
+            exact = Fraction(float(s[n, g])) * int(q[n, k]) + Fraction(float(b[n, g]))
+            assert Fraction(w[n, k]) == exact
+
+
+def test_dequant_f16_t_is_transposed_rounded_exact():
+    q, s, b = synth.w4_weights(7, 192, seed=6)
+    qw = oracle.pack(q)
+    wt = oracle.dequant_f16_t(qw, s, b)
+    assert wt.shape == (192, 7) and wt.dtype == np.uint16
+    assert np.array_equal(wt, oracle.f16_bits_struct(oracle.dequant_exact(qw, s, b)).T)
+    # closed forms: s = 1, b = 0 -> w = q; b = -8 s -> w = s (q - 8)
+    ones = np.ones((7, 3), dtype=np.float16)
+    zeros = np.zeros((7, 3), dtype=np.float16)
+    assert np.array_equal(oracle.f16_value(oracle.dequant_f16_t(qw, ones, zeros)), q.T.astype(np.float64))
+    sym = oracle.dequant_exact(qw, s, (-8.0 * s.astype(np.float64)).astype(np.float16))
+    grp = np.arange(192) // 64
+    assert np.allclose(sym, s.astype(np.float64)[:, grp] * (q.astype(np.float64) - 8), rtol=0, atol=1e-3)
+
+
+# ------------------------------------------------------------------------------ GEMV
+
+
+def test_gemv_closed_forms():
+    m, n, k = 3, 9, 192
+    x = synth.activations(m, k, seed=7)
+    x64 = x.astype(np.float64)
+    ones = np.ones((n, k // 64), dtype=np.float16)
+    zeros = np.zeros((n, k // 64), dtype=np.float16)
+    for c in (0, 1, 7, 15):
+        q = np.full((n, k), c, dtype=np.uint8)
+        y, bound = oracle.gemv_ref(oracle.pack(q), ones, zeros, x)
+        assert np.array_equal(y, np.repeat((c * x64.sum(axis=1))[:, None], n, axis=1))
+    # q = 0: y = sum_g b_g X_g with X_g the group sums of x
+    _, s, b = synth.w4_weights(n, k, seed=8)
+    y, _ = oracle.gemv_ref(oracle.pack(np.zeros((n, k), np.uint8)), s, b, x)
+    xg = x64.reshape(m, k // 64, 64).sum(axis=2)
+    assert np.allclose(y, xg @ b.astype(np.float64).T, rtol=1e-13, atol=0)
+    # x = e_k: y[n] = w[n][k]
+    q, s, b = synth.w4_weights(n, k, seed=9)
+    qw = oracle.pack(q)
+    w = oracle.dequant_exact(qw, s, b)
+    for kk in (0, 63, 64, 100, 191):
+        e = np.zeros((1, k), dtype=np.float16)
+        e[0, kk] = 1.0
+        y, bound = oracle.gemv_ref(qw, s, b, e)
+        assert np.array_equal(y[0], w[:, kk]) and np.array_equal(bound[0], np.abs(w[:, kk]))
+    # x = 0: y = 0 and bound = 0
+    y, bound = oracle.gemv_ref(qw, s, b, np.zeros((2, k), np.float16))
+    assert not y.any() and not bound.any()
+
+
+def test_gemv_matches_fraction_bruteforce():
+    for k, n, m, seed in ((64, 5, 3, 10), (128, 4, 2, 11)):
+        q, s, b = synth.w4_weights(n, k, seed=seed)
+        x = synth.activations(m, k, seed=seed)
+        y, bound = oracle.gemv_ref(oracle.pack(q), s, b, x)
+        for mm in range(m):
+            for nn in range(n):
+                tot = Fraction(0)
+                mag = Fraction(0)
+                for kk in range(k):
+                    g = kk // 64
+                    w = Fraction(float(s[nn, g])) * int(q[nn, kk]) + Fraction(float(b[nn, g]))
+                    t = w * Fraction(float(x[mm, kk]))
+                    tot += t
+                    mag += abs(t)
+                assert abs(Fraction(y[mm, nn]) - tot) <= Fraction(1, 10**12) * mag
+                assert abs(Fraction(bound[mm, nn]) - mag) <= Fraction(1, 10**12) * mag
+
+
+def test_check_bound_rule():
+    y_ref = np.array([[1.0, -2.0, 0.0]])
+    bound = np.array([[10.0, 10.0, 0.0]])
+    assert oracle.check_bound(y_ref + np.array([[0.019, -0.0199, 0.0]]), y_ref, bound)[0]
+    assert not oracle.check_bound(y_ref + np.array([[0.021, 0, 0]]), y_ref, bound)[0]
+    assert not oracle.check_bound(y_ref + np.array([[0, 0, 1e-30]]), y_ref, bound)[0]
+    assert not oracle.check_bound(np.array([[np.nan, -2.0, 0.0]]), y_ref, bound)[0]
+
+
+def test_tolerance_admits_f32_accumulation():
+    # Any f32 summation of exact products errs by at most gamma_K * bound with
+    # gamma_K ~ K * 2**-24 (Higham); at K = 15360 that is 9.2e-4 < 2e-3.  A sequential
+    # f32 sum must therefore pass the rule.
+    k = 15360
+    q, s, b = synth.w4_weights(4, k, seed=12)
+    x = synth.activations(1, k, seed=12)
+    qw = oracle.pack(q)
+    y_ref, bound = oracle.gemv_ref(qw, s, b, x)
+    w32 = oracle.dequant_exact(qw, s, b).astype(np.float32)
+    acc = np.zeros(4, dtype=np.float32)
+    for kk in range(k):
+        acc += w32[:, kk] * np.float32(x[0, kk])
+    assert oracle.check_bound(acc[None, :], y_ref, bound)[0]
+
+
+# ------------------------------------------------------------------------------ GEMM
+
+
+def test_gemm_identity_and_onehot():
+    a = synth.activations(5, 64, seed=13)
+    eye = np.eye(64, dtype=np.float16)
+    c, bound = oracle.gemm_ref(a, eye)
+    assert np.array_equal(c, a.astype(np.float64))
+    bmat = synth.activations(64, 7, seed=14)
+    onehot = np.zeros((3, 64), dtype=np.float16)
+    onehot[0, 0] = onehot[1, 31] = onehot[2, 63] = 1.0
+    c, _ = oracle.gemm_ref(onehot, bmat)
+    assert np.array_equal(c, bmat.astype(np.float64)[[0, 31, 63]])
+
+
+def test_gemm_matches_fraction_bruteforce():
+    a = synth.activations(3, 16, seed=15)
+    bmat = synth.activations(16, 3, seed=16)  # square-ish so a transposed operand would still run
+    c, bound = oracle.gemm_ref(a, bmat)
+    for i in range(3):
+        for j in range(3):
+            terms = [Fraction(float(a[i, kk])) * Fraction(float(bmat[kk, j])) for kk in range(16)]
+            assert abs(Fraction(c[i, j]) - sum(terms)) <= Fraction(1, 10**12) * sum(abs(t) for t in terms)
+            assert Fraction(bound[i, j]) == sum(abs(t) for t in terms)
+
+
+# ------------------------------------------------------------------------------ top-k
+
+
+def test_topk_matches_python_sort():
+    r = np.random.default_rng(17)
+    for v, k in ((1, 1), (7, 7), (50, 10), (300, 64), (2, 1), (1000, 256)):
+        rows = r.integers(-4, 4, size=(3, v)).astype(np.float32) * 0.5  # many ties
+        rows[:, ::7] = -rows[:, ::7]
+        rows[rows == 0] = np.where(r.random((rows == 0).sum()) < 0.5, -0.0, 0.0)
+        idx, val = oracle.topk_ref(rows, k)
+        for i in range(3):
+            assert idx[i].tolist() == oracle.topk_ref_loop(rows[i].tolist(), k)
+            assert np.array_equal(val[i], rows[i, idx[i]])
+    # k = V is the full stable sort; k = 1 is the argmax
+    row = r.standard_normal((1, 999)).astype(np.float32)
+    assert oracle.topk_ref(row, 999)[0][0].tolist() == oracle.topk_ref_loop(row[0].tolist(), 999)
+    assert oracle.topk_ref(row, 1)[0][0, 0] == int(np.argmax(row[0]))
+
+
+def test_topk_checks():
+    v = np.array([[3.0, 2.995, 1.0, 0.0]], dtype=np.float64)
+    # gap 0.005 < 1e-2: ranks 0 and 1 may swap, rank 2 must match
+    assert oracle.check_topk_vs_exact(v, np.array([[1, 0, 2]]), 3)[0]
+    assert not oracle.check_topk_vs_exact(v, np.array([[1, 0, 3]]), 3)[0]
+    assert not oracle.check_topk_vs_exact(np.array([[3.0, 2.0, 1.0]]), np.array([[1, 0]]), 2)[0]
+    lg = np.array([[0.5, 2.0, 2.0, -1.0]], dtype=np.float32)
+    assert oracle.check_topk_selection(lg, [[1, 2]], [[2.0, 2.0]], 2)
+    assert not oracle.check_topk_selection(lg, [[2, 1]], [[2.0, 2.0]], 2)
+
+
+# -------------------------------------------------------------------- page figures
+
+
+def test_page_figures_fix_head_and_logit_dtypes():
+    g = _gold("page_figures.json")
+    assert (g["hidden"], g["vocab"]) == (synth.QWEN25_3B_HIDDEN, synth.QWEN25_3B_VOCAB)
+    head_bytes = g["hidden"] * g["vocab"] * 2
+    assert round(head_bytes / 1e6) == g["head_mb_per_token"]
+    # 4-byte logits are within 2% of the printed size; 2-byte ones are half of it
+    assert abs(g["vocab"] * 4 / 1e3 - g["logits_kb_per_token"]) / g["logits_kb_per_token"] < 0.02
+    assert abs(g["vocab"] * 2 / 1e3 - g["logits_kb_per_token"]) / g["logits_kb_per_token"] > 0.4
+
+
+# ------------------------------------------------------------------------------ mutants
+
+
+def _mut_unpack_high_first(qw):
+    q = w4ref.unpack(qw)
+    n, k = q.shape
+    return q.reshape(n, k // 8, 8)[:, :, ::-1].reshape(n, k).copy()
+
+
+def _mut_pack_high_first(q):
+    n, k = q.shape
+    return w4ref.pack(np.asarray(q).reshape(n, k // 8, 8)[:, :, ::-1].reshape(n, k))
+
+
+def _dequant_with(qw, s, b, group=64, shift=0, use_bias=True, sym=False):
+    q = w4ref.unpack(qw).astype(np.float64)
+    n, k = q.shape
+    grp = np.minimum((np.arange(k) + shift) // group, s.shape[1] - 1)
+    s64 = s.astype(np.float64)[:, grp]
+    if sym:
+        return s64 * (q - 8)
+    return s64 * q + (b.astype(np.float64)[:, grp] if use_bias else 0.0)
+
+
+def _gemv_from(dq):
+    def gemv(qw, s, b, x):
+        w = dq(qw, s, b)
+        x64 = x.astype(np.float64)
+        return x64 @ w.T, np.abs(x64) @ np.abs(w).T
+    return gemv
+
+
+def _dequant_t_from(dq):
+    return lambda qw, s, b: w4ref.f16_bits(dq(qw, s, b)).T.copy()
+
+
+def _dequant_t_double_round(qw, s, b):
+    return w4ref.f16_bits(w4ref.dequant_exact(qw, s, b).astype(np.float32)).T.copy()
+
+
+def _dequant_t_ftz(qw, s, b):
+    w = w4ref.dequant_exact(qw, s, b)
+    w = np.where(np.abs(w) < 2.0 ** -14, 0.0, w)
+    return w4ref.f16_bits(w).T.copy()
+
+
+def _gemv_drop_last_k(qw, s, b, x):
+    w = w4ref.dequant_exact(qw, s, b)[:, :-1]
+    x64 = x.astype(np.float64)[:, :-1]
+    return x64 @ w.T, np.abs(x64) @ np.abs(w).T
+
+
+def _topk_last_index_ties(v, k):
+    v = np.asarray(v)
+    rev = v[:, ::-1]
+    order = np.argsort(-rev, axis=1, kind="stable")[:, :k]
+    idx = v.shape[1] - 1 - order
+    return idx, np.take_along_axis(v, idx, axis=1)
+
+
+def _topk_raw_bits(v, k):
+    # orders by the f32 bit pattern read as a signed integer (wrong for negatives)
+    v = np.asarray(v, dtype=np.float32)
+    order = np.argsort(-v.view(np.int32).astype(np.int64), axis=1, kind="stable")[:, :k]
+    return order, np.take_along_axis(v, order, axis=1)
+
+
+def _topk_ascending(v, k):
+    order = np.argsort(np.asarray(v), axis=1, kind="stable")[:, :k]
+    return order, np.take_along_axis(np.asarray(v), order, axis=1)
+
+
+MUTANTS = {
+    "unpack high nibble first": lambda: pins_pack(w4ref.pack, _mut_unpack_high_first),
+    "pack high nibble first": lambda: pins_pack(_mut_pack_high_first, w4ref.unpack)
+    + pins_gemv(w4ref.gemv_ref, _mut_pack_high_first),
+    "group size 128": lambda: pins_gemv(_gemv_from(lambda qw, s, b: _dequant_with(qw, s, b, group=128)), w4ref.pack),
+    "missing bias": lambda: pins_gemv(_gemv_from(lambda qw, s, b: _dequant_with(qw, s, b, use_bias=False)), w4ref.pack),
+    "s*(q-8) without b": lambda: pins_gemv(_gemv_from(lambda qw, s, b: _dequant_with(qw, s, b, sym=True)), w4ref.pack),
+    "group index off by one": lambda: pins_gemv(_gemv_from(lambda qw, s, b: _dequant_with(qw, s, b, shift=1)), w4ref.pack),
+    "dropped last k term": lambda: pins_gemv(_gemv_drop_last_k, w4ref.pack),
+    "f32 then f16 rounding": lambda: pins_dequant(_dequant_t_double_round, w4ref.pack),
+    "subnormals flushed": lambda: pins_dequant(_dequant_t_ftz, w4ref.pack),
+    "dequant missing bias": lambda: pins_dequant(_dequant_t_from(lambda qw, s, b: _dequant_with(qw, s, b, use_bias=False)), w4ref.pack),
+    "argmax ties to last index": lambda: pins_topk(_topk_last_index_ties),
+    "raw-bit comparison": lambda: pins_topk(_topk_raw_bits),
+    "ascending order": lambda: pins_topk(_topk_ascending),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutants_fail(name):
+    assert MUTANTS[name](), f"planted mistake '{name}' passed every pin"
+
+
+def test_gemm_transposed_operand_fails_bruteforce():
+    a = synth.activations(4, 4, seed=18)
+    bmat = synth.activations(4, 4, seed=19)
+    c_bad = a.astype(np.float64) @ bmat.astype(np.float64).T
+    exact = [[sum(Fraction(float(a[i, kk])) * Fraction(float(bmat[kk, j])) for kk in range(4)) for j in range(4)]
+             for i in range(4)]
+    assert any(Fraction(c_bad[i, j]) != exact[i][j] for i in range(4) for j in range(4))
+    c_ok, _ = oracle.gemm_ref(a, bmat)
+    assert all(abs(Fraction(c_ok[i, j]) - exact[i][j]) < Fraction(1, 10**9) for i in range(4) for j in range(4))
