@@ -1,0 +1,419 @@
+#!/usr/bin/env python3
+"""Benchmark of the int4 group-64 affine linear-layer hot path on one MI355X.
+
+One step = one pass of the whole hot path on synthetic inputs shaped like the pages'
+workloads ("The inference engine -- Mojo 1.0 on Metal", "Crossing Mojo 1.0"):
+  decode  -- a Qwen2.5-3B-shaped decode token at M = 1: 36 layers x (q, k, v, o, gate, up,
+             down) int4 GEMVs, then the f16 LM head 2048 -> 151936 and on-device top-40;
+  prefill -- a 1570-token prefill of the three MLP matrices (gate, up: 2048 -> 11008;
+             down: 11008 -> 2048): each weight dequantized once into its transposed f16
+             scratch, then an f16 GEMM with f32 accumulation.
+Each phase is captured once as a HIP graph and replayed; HIP events on the replay stream
+time the phases inside every timed step.
+
+Printed (one JSON line): value = int4 GEMV GB/s of the decode phase (algorithmic bytes:
+N*K/2 codes + N*K/16 scales/biases + 2*M*K x + 4*M*N y per GEMV) and, beside it, the
+prefill's dequant+GEMM TFLOP/s (2*M*N*K per GEMM over the phase's wall time), each as a
+fraction of MI355X's 8 TB/s HBM and 2.5 PFLOP/s dense f16.  `roofline` is the dominant
+GEMV kernel's own rate from per-launch HIP events; `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload.  Outputs of the timed steps are re-checked against the
+oracle on sampled rows before anything is printed.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+METRIC = "W4 GEMV GB/s (% of HBM peak); prefill dequant+GEMM TFLOP/s (% MFMA peak)"
+TOPK = 40
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--eager", action="store_true", help="launch every kernel from Python instead of replaying graphs")
+    p.add_argument("--unfused", action="store_true", help="run q,k,v and gate,up as separate GEMVs (7 per layer)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-check", action="store_true", help="skip the parity re-check of the timed outputs")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def gemv_bytes(m, n, k):
+    return n * k // 2 + n * k // 16 + 2 * m * k + 4 * m * n
+
+
+class Workload:
+    """Device buffers of the decode step and the prefill, plus the host copies the oracle
+    needs for the parity re-check (only of sampled layers)."""
+
+    def __init__(self, torch, np, w4, synth, unfused=False):
+        self.torch, self.np, self.w4, self.synth = torch, np, w4, synth
+        dev = "cuda"
+        t0 = time.time()
+        self.layers = []  # per layer: list of (names, qw, s, b, x, y, (M, N, K))
+        self.gemv_bytes = 0
+        # q, k, v read one activation and gate, up another (as in the model); by default each
+        # group is stored row-concatenated so it runs as one GEMV (identical outputs).
+        groups = ([["q"], ["k"], ["v"], ["o"], ["gate"], ["up"], ["down"]] if unfused
+                  else [["q", "k", "v"], ["o"], ["gate", "up"], ["down"]])
+        shapes = {name: (j, n, k) for j, (name, n, k) in enumerate(synth.QWEN25_3B_LAYER)}
+        src_of = {"q": "attn", "k": "attn", "v": "attn", "o": "o", "gate": "mlp", "up": "mlp", "down": "down"}
+        for l in range(synth.QWEN25_3B_LAYERS):
+            xs = {}
+            mats = []
+            for grp in groups:
+                qs, ss, bs = [], [], []
+                for name in grp:
+                    j, n, k = shapes[name]
+                    q, s, b = synth.w4_weights(n, k, seed=0, workload=synth.W_DECODE, layer=l * 16 + j)
+                    qs.append(q); ss.append(s); bs.append(b)
+                q, s, b = np.concatenate(qs), np.concatenate(ss), np.concatenate(bs)
+                n, k = q.shape
+                qw = w4.w4_pack(torch.from_numpy(q).to(dev))
+                src = src_of[grp[0]]
+                if src not in xs:
+                    slot = ["attn", "o", "mlp", "down"].index(src)
+                    xs[src] = torch.from_numpy(synth.activations(1, k, seed=0, workload=synth.W_DECODE,
+                                                                 layer=l * 16 + 8 + slot)).to(dev)
+                y = torch.empty((1, n), dtype=torch.float32, device=dev)
+                mats.append(("+".join(grp), qw, torch.from_numpy(s).to(dev), torch.from_numpy(b).to(dev), xs[src], y,
+                             (1, n, k)))
+                self.gemv_bytes += gemv_bytes(1, n, k)
+            self.layers.append(mats)
+        log(f"decode weights packed on the GPU in {time.time() - t0:.1f}s ({self.gemv_bytes / 1e9:.3f} GB per step)")
+
+        t0 = time.time()
+        self.V, self.H = synth.QWEN25_3B_VOCAB, synth.QWEN25_3B_HIDDEN
+        self.head_host = synth.head_f16(self.H, self.V, seed=0, workload=synth.W_DECODE, layer=999)
+        self.head = torch.from_numpy(self.head_host).to(dev)
+        self.x_head_host = synth.activations(1, self.H, seed=0, workload=synth.W_DECODE, layer=998)
+        self.x_head = torch.from_numpy(self.x_head_host).to(dev)
+        self.logits = torch.empty((1, self.V), dtype=torch.float32, device=dev)
+        self.idx = torch.empty((1, TOPK), dtype=torch.int32, device=dev)
+        self.val = torch.empty((1, TOPK), dtype=torch.float32, device=dev)
+        self.topk_ws = torch.empty(max(16, w4.topk_workspace_bytes(1, self.V, TOPK)), dtype=torch.uint8, device=dev)
+        self.head_bytes = 2 * self.H * self.V + 2 * self.H + 4 * self.V + 4 * self.V  # head + x + logits w/r
+        log(f"f16 head [{self.H}][{self.V}] ready in {time.time() - t0:.1f}s")
+
+        t0 = time.time()
+        self.M = synth.PREFILL_TOKENS
+        self.prefill = []  # (name, qw, s, b, wt, A, C, (M, N, K), host q/s/b)
+        a_in = {}
+        for j, (name, n, k) in enumerate(synth.PREFILL_MATS):
+            q, s, b = synth.w4_weights(n, k, seed=0, workload=synth.W_PREFILL, layer=j)
+            qw = w4.w4_pack(torch.from_numpy(q).to(dev))
+            if k not in a_in:
+                a_in[k] = synth.activations(self.M, k, seed=0, workload=synth.W_PREFILL, layer=100 + k)
+            wt = torch.empty((k, n), dtype=torch.float16, device=dev)
+            c = torch.empty((self.M, n), dtype=torch.float32, device=dev)
+            self.prefill.append((name, qw, torch.from_numpy(s).to(dev), torch.from_numpy(b).to(dev), wt,
+                                 torch.from_numpy(a_in[k]).to(dev), c, (self.M, n, k), (q, s, b, a_in[k])))
+        self.prefill_flops = sum(2 * m * n * k for *_, (m, n, k), _ in self.prefill)
+        torch.cuda.synchronize()
+        log(f"prefill weights ready in {time.time() - t0:.1f}s ({self.prefill_flops / 1e9:.2f} GFLOP per step)")
+
+    # -- the three phases of a step (no allocation: every output is preallocated)
+    def run_gemvs(self):
+        gemv = self.w4.w4_gemv
+        for mats in self.layers:
+            for _, qw, s, b, x, y, _ in mats:
+                gemv(qw, s, b, x, out=y)
+
+    def run_head(self):
+        self.w4.gemm_f16(self.x_head, self.head, out=self.logits)
+        self.w4.logits_argmax_topk(self.logits, TOPK, idx=self.idx, val=self.val, workspace=self.topk_ws)
+
+    def run_prefill(self):
+        for _, qw, s, b, wt, a, c, _, _ in self.prefill:
+            self.w4.w4_dequant_f16_t(qw, s, b, out=wt)
+            self.w4.gemm_f16(a, wt, out=c)
+
+
+def capture(torch, fn):
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()  # eager warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def kernel_timings(torch, wl, reps=3):
+    """Per-launch HIP-event durations of every decode GEMV shape and of the prefill GEMMs and
+    dequants (eager launches on the current stream, each bracketed by its own events)."""
+    stream = torch.cuda.current_stream()
+    rec = {}
+
+    def timed(key, nbytes, flops, fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        rec.setdefault(key, []).append((e0, e1, nbytes, flops))
+
+    for _ in range(reps):
+        for mats in wl.layers:
+            for name, qw, s, b, x, y, (m, n, k) in mats:
+                timed(("w4_gemv", m, n, k), gemv_bytes(m, n, k), 0,
+                      lambda qw=qw, s=s, b=b, x=x, y=y: wl.w4.w4_gemv(qw, s, b, x, out=y))
+        for name, qw, s, b, wt, a, c, (m, n, k), _ in wl.prefill:
+            timed(("w4_dequant_f16_t", 0, n, k), n * k // 2 + n * k // 16 + 2 * n * k, 0,
+                  lambda qw=qw, s=s, b=b, wt=wt: wl.w4.w4_dequant_f16_t(qw, s, b, out=wt))
+            timed(("gemm_f16", m, n, k), 2 * (m * k + k * n) + 4 * m * n, 2 * m * n * k,
+                  lambda a=a, wt=wt, c=c: wl.w4.gemm_f16(a, wt, out=c))
+        timed(("gemm_f16", 1, wl.V, wl.H), 2 * wl.H * wl.V + 2 * wl.H + 4 * wl.V, 2 * wl.H * wl.V,
+              lambda: wl.w4.gemm_f16(wl.x_head, wl.head, out=wl.logits))
+    torch.cuda.synchronize()
+    out = {}
+    for key, lst in rec.items():
+        us = [e0.elapsed_time(e1) * 1e3 for e0, e1, _, _ in lst]
+        nb, fl = lst[0][2], lst[0][3]
+        avg = sum(us) / len(us)
+        out[key] = {"launches": len(us), "avg_us": avg, "bytes": nb, "flops": fl,
+                    "gbps": nb / avg / 1e3, "tflops": fl / avg / 1e6 if fl else 0.0}
+    return out
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "int4_weight_only_group_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel_src, key):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the current
+    kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+        ent = t["kernels"][key]
+        if ent.get("source_sha") != source_hash(kernel_src):
+            return None
+        return ent["hbm_bytes_per_launch"]
+    except Exception:
+        return None
+
+
+def parity_check(torch, np, wl, oracle, synth):
+    """Re-check the outputs of the last timed step against the oracle on sampled rows."""
+    rng = np.random.default_rng(123)
+    res = {}
+    worst = 0.0
+    # decode GEMVs of the last layer, 64 sampled output rows per GEMV
+    l = synth.QWEN25_3B_LAYERS - 1
+    shapes = {name: (j, n, k) for j, (name, n, k) in enumerate(synth.QWEN25_3B_LAYER)}
+    for names, _, _, _, x, y, (_, n, k) in wl.layers[l]:
+        parts = [synth.w4_weights(shapes[nm][1], k, seed=0, workload=synth.W_DECODE, layer=l * 16 + shapes[nm][0])
+                 for nm in names.split("+")]
+        q, s, b = (np.concatenate([p[i] for p in parts]) for i in range(3))
+        rows = np.sort(rng.choice(n, min(n, 64), replace=False))
+        y_ref, bound = oracle.gemv_ref(oracle.pack(q[rows]), s[rows], b[rows], x.cpu().numpy())
+        ok, wr = oracle.check_bound(y.cpu().numpy()[:, rows], y_ref, bound)
+        worst = max(worst, wr)
+        if not ok:
+            res["gemv_fail"] = names
+    res["gemv_worst_err_over_bound"] = worst
+    # f16 head on every column; top-40 against the fp64 logits (near-tie rule)
+    lg = wl.logits.cpu().numpy()
+    c_ref, bound = oracle.gemm_ref(wl.x_head_host, wl.head_host)
+    ok_h, wr_h = oracle.check_bound(lg, c_ref, bound)
+    res["head_worst_err_over_bound"] = wr_h
+    idx = wl.idx.cpu().numpy()
+    ok_t, loose = oracle.check_topk_vs_exact(c_ref, idx, TOPK)
+    ok_t &= bool(np.array_equal(wl.val.cpu().numpy().view(np.uint32), lg[0, idx[0]][None].view(np.uint32)))
+    res["topk_ok"] = ok_t
+    res["topk_ranks_in_near_tie"] = loose
+    del c_ref, bound
+    # prefill: dequant scratch bit-exact on sampled columns; GEMM on sampled rows incl. the M tail
+    worst_p = 0.0
+    ok_p = True
+    for name, qw, s, b, wt, a, c, (m, n, k), (qh, sh, bh, ah) in wl.prefill:
+        wt_ref = oracle.dequant_f16_t(oracle.pack(qh), sh, bh)
+        cols = np.sort(rng.choice(n, 64, replace=False))
+        ok_p &= bool(np.array_equal(wt.cpu().numpy().view(np.uint16)[:, cols], wt_ref[:, cols]))
+        rows = np.unique(np.concatenate([rng.choice(m - 34, 30, replace=False), np.arange(m - 34, m)]))
+        c_ref, bound = oracle.gemm_ref(ah[rows], wt_ref.view(np.float16))
+        okc, wr = oracle.check_bound(c.cpu().numpy()[rows], c_ref, bound)
+        ok_p &= okc
+        worst_p = max(worst_p, wr)
+    res["prefill_worst_err_over_bound"] = worst_p
+    res["ok"] = bool("gemv_fail" not in res and ok_h and ok_t and ok_p)
+    return res
+
+
+def cpu_baseline(np, oracle, synth):
+    """The oracle's GEMV (unpack + exact dequant + fp64 product) over decoder layer 0's seven
+    matrices at M = 1, on this host's cores."""
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    mats = []
+    for j, (name, n, k) in enumerate(synth.QWEN25_3B_LAYER):
+        q, s, b = synth.w4_weights(n, k, seed=0, workload=synth.W_DECODE, layer=j)
+        x = synth.activations(1, k, seed=0, workload=synth.W_DECODE, layer=8 + j)
+        mats.append((oracle.pack(q), s, b, x, gemv_bytes(1, n, k)))
+    t0 = time.perf_counter()
+    nbytes = 0
+    for qw, s, b, x, nb in mats:
+        oracle.gemv_ref(qw, s, b, x)
+        nbytes += nb
+    dt = time.perf_counter() - t0
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"oracle.gemv_ref over decoder layer 0's 7 int4 matrices at M=1 "
+                      f"({nbytes / 1e6:.1f} MB of algorithmic bytes, {dt:.1f} s; NumPy fp64, BLAS threads={threads})",
+            "seconds": dt}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import int4_weight_only_group_amd as w4
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    log(f"device {torch.cuda.get_device_name(0)}; library {w4.LIB_PATH}")
+    wl = Workload(torch, np, w4, synth, unfused=args.unfused)
+
+    phases = [wl.run_gemvs, wl.run_head, wl.run_prefill]
+    if args.eager:
+        runners = phases
+    else:
+        t0 = time.time()
+        graphs = [capture(torch, f) for f in phases]
+        runners = [g.replay for g in graphs]
+        log(f"captured 3 HIP graphs in {time.time() - t0:.1f}s")
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        for r in runners:
+            r()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        for j, r in enumerate(runners):
+            r()
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ph = [sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)) / 1e3 for j in range(3)]
+    log(f"timed {args.steps} steps in {wall * 1e3:.1f} ms: gemv {ph[0] / args.steps * 1e6:.1f} us, "
+        f"head+top-k {ph[1] / args.steps * 1e6:.1f} us, prefill {ph[2] / args.steps * 1e6:.1f} us per step")
+
+    check = None
+    if not args.no_check:
+        import oracle
+        t0 = time.time()
+        check = parity_check(torch, np, wl, oracle, synth)
+        log(f"parity re-check {'ok' if check['ok'] else 'FAILED'} in {time.time() - t0:.1f}s: {check}")
+
+    kt = kernel_timings(torch, wl)
+    # dominant decode kernel: the GEMV shape with the largest total time per step
+    per_step = {}
+    for mats in wl.layers[:1]:
+        for _, _, _, _, _, _, (m, n, k) in mats:
+            key = ("w4_gemv", m, n, k)
+            per_step[key] = per_step.get(key, 0.0) + kt[key]["avg_us"] * synth.QWEN25_3B_LAYERS
+    dom = max(per_step, key=per_step.get)
+    d = kt[dom]
+    roofline = {"bound": "hbm", "kernel": f"w4_gemv (M,N,K)=({dom[1]},{dom[2]},{dom[3]})",
+                "achieved": d["gbps"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": d["gbps"] / HBM_PEAK_GBS,
+                "traffic": traffic_for("gemv.hip", f"w4_gemv_{dom[1]}_{dom[2]}_{dom[3]}"),
+                "bytes_per_launch": d["bytes"], "avg_launch_us": d["avg_us"], "launches_timed": d["launches"]}
+    gk = [v for k_, v in kt.items() if k_[0] == "gemm_f16" and k_[1] == synth.PREFILL_TOKENS]
+    g_us = sum(v["avg_us"] for v in gk)
+    g_fl = sum(v["flops"] for v in gk)
+    roofline_prefill = {"bound": "mfma", "kernel": "gemm_f16 prefill GEMMs (1570x11008x2048 x2, 1570x2048x11008)",
+                        "achieved": g_fl / g_us / 1e6, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": g_fl / g_us / 1e6 / MFMA_F16_PEAK_TFLOPS,
+                        "traffic": traffic_for("gemm.hip", "gemm_f16_prefill"), "avg_launch_us": g_us / len(gk)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(np, oracle, synth)
+        log(f"cpu baseline {cpu['value']:.4f} GB/s in {cpu['seconds']:.1f}s")
+
+    gemv_gbps = wl.gemv_bytes * args.steps / ph[0] / 1e9
+    prefill_tflops = wl.prefill_flops * args.steps / ph[2] / 1e12
+    decode_bytes = wl.gemv_bytes + wl.head_bytes
+    out = {
+        "metric": METRIC,
+        "value": round(gemv_gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Qwen2.5-3B-shaped int4 decode step at M=1 (36 layers x q,k,v,o,gate,up,down W4 GEMVs, "
+                        "f16 head 2048->151936, top-40) + 1570-token prefill of gate/up/down (dequant once + f16 GEMM)",
+            "group": 64, "launch": "eager" if args.eager else "hipgraph",
+            "gemv_launches_per_step": sum(len(m) for m in wl.layers),
+            "qkv_gateup": "separate" if args.unfused else "row-concatenated",
+            "gemv_bytes_per_step": wl.gemv_bytes, "prefill_flops_per_step": wl.prefill_flops,
+        },
+        "frac_hbm": round(gemv_gbps / HBM_PEAK_GBS, 4),
+        "prefill_tflops": round(prefill_tflops, 2),
+        "prefill_frac_mfma": round(prefill_tflops / MFMA_F16_PEAK_TFLOPS, 4),
+        "phase_us_per_step": {"gemv": ph[0] / args.steps * 1e6, "head_topk": ph[1] / args.steps * 1e6,
+                              "prefill": ph[2] / args.steps * 1e6},
+        "decode_step_gbps": decode_bytes * args.steps / (ph[0] + ph[1]) / 1e9,
+        "roofline": roofline,
+        "roofline_prefill": roofline_prefill,
+        "kernels": {"/".join(map(str, k)): {kk: round(vv, 3) if isinstance(vv, float) else vv for kk, vv in v.items()}
+                    for k, v in kt.items()},
+        "cpu_baseline": cpu,
+        "parity": check,
+    }
+    if check is not None and not check["ok"]:
+        out["value"] = None
+        out["error"] = "parity re-check failed"
+    print(json.dumps(out), flush=True)
+    if check is not None and not check["ok"]:
+        sys.exit(1)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,136 @@
+/*
+ * w4.h -- C ABI of the MI355X (gfx950) group-wise affine int4 weight-only linear layer.
+ *
+ * The operations are those of a local LLM engine's int4 linear layer as described on
+ * "The inference engine -- Mojo 1.0 on Metal" (millfolio), section "Crossing Mojo 1.0":
+ * a multi-row decode GEMV that streams the packed weights, a prefill that dequantizes
+ * every weight once into a transposed half-precision scratch and then runs an f16 GEMM,
+ * and on-device argmax/top-k over the logits.  The weight format is MLX's affine 4-bit
+ * format (same page, "Appendix: the remaining gap, itemized") with group size 64
+ * ("Engineering investigation: can this MLX port become another 10x faster?",
+ * section "Selective quantization").
+ *
+ * Weight format (fixed):
+ *   codes    q[n][k] in 0..15, n < N output features, k < K input features, K % 64 == 0;
+ *   packed   qw[n][j], uint32, row-major [N][K/8]; code q[n][8j+i] in bits 4i..4i+3
+ *            (low nibble first, little-endian words);
+ *   scales   s[n][g], biases b[n][g], f16 bit patterns, row-major [N][K/64], g = k / 64;
+ *   weight   w[n][k] = s[n][g] * q[n][k] + b[n][g].
+ *
+ * Conventions for every function:
+ *   - f16 values travel as uint16_t bit patterns; f32 as float.
+ *   - Every pointer is a DEVICE pointer owned by the caller.  The library never allocates,
+ *     frees or retains device memory and keeps no per-call state; inputs are read-only;
+ *     outputs are fully overwritten (no accumulation) and must not alias inputs.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the default stream) and the call
+ *     returns without waiting for it.
+ *   - Every argument check runs on the host before anything is launched; on a non-zero
+ *     return nothing was launched and no output was touched.  Faults inside a kernel
+ *     surface as a HIP error at the caller's next synchronisation.
+ *   - Functions with a workspace use a two-phase protocol: with ws == NULL the required
+ *     byte count is written to *ws_bytes and W4_OK is returned without launching;
+ *     otherwise *ws_bytes is the capacity of ws (16-byte aligned) and too little returns
+ *     W4_ERR_WORKSPACE.  A required size of 0 means ws may be NULL-or-anything once queried.
+ *   - Alignment: the base pointers named below must be 16-byte aligned and the leading
+ *     dimensions of f16 operands multiples of 8 elements, else W4_ERR_ALIGN.
+ *   - The functions are reentrant; calls on different streams may run concurrently.
+ *   - No C++ exception crosses the ABI (an internal failure returns W4_ERR_INTERNAL).
+ *   - Only gfx950 devices are accepted (W4_ERR_DEVICE otherwise, or with no device).
+ */
+#ifndef W4_H
+#define W4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* w4_stream_t; /* == hipStream_t */
+
+enum {
+  W4_OK = 0,
+  W4_ERR_NULL = -1,      /* a required pointer is NULL */
+  W4_ERR_SHAPE = -2,     /* a size is out of the supported range */
+  W4_ERR_ALIGN = -3,     /* a pointer or leading dimension is misaligned */
+  W4_ERR_WORKSPACE = -4, /* the workspace is too small */
+  W4_ERR_DEVICE = -5,    /* no usable gfx950 device is current */
+  W4_ERR_LAUNCH = -6,    /* the HIP runtime rejected a launch */
+  W4_ERR_INTERNAL = -7   /* unexpected internal failure */
+};
+
+/* Static string describing a status code (never NULL). */
+const char* w4_strerror(int status);
+
+/*
+ * w4_pack -- pack 4-bit codes into the weight format ("quantized to int4 at load":
+ * "The inference engine -- Mojo 1.0 on Metal", "Where it fits").
+ *   q   uint8 [N][K], row-major, values 0..15 (only the low 4 bits of each byte are kept);
+ *   qw  uint32 [N][K/8] output.
+ * Requires N >= 1, K >= 64, K % 64 == 0; q and qw 16-byte aligned.  Bit-exact.
+ */
+int w4_pack(const uint8_t* q, uint32_t* qw, int64_t N, int64_t K, w4_stream_t stream);
+
+/*
+ * w4_gemv -- decode GEMV over the packed weights ("Crossing Mojo 1.0": the multi-row
+ * GEMV that keeps several weight streams in flight; "What's inside the engine today"):
+ *   y[m][n] = sum_k (s[n][k/64] * q[n][k] + b[n][k/64]) * x[m][k]      (f32 accumulation)
+ *   qw [N][K/8], scales/biases [N][K/64] (f16 bits), x f16 [M][K] with row stride ldx,
+ *   y  f32 [M][N] with row stride ldy.
+ * Requires 1 <= M <= 16, N >= 1, K >= 64, K % 64 == 0, ldx >= K, ldy >= N, ldx % 8 == 0;
+ * qw, scales, biases, x 16-byte aligned; y 4-byte aligned.  The result is deterministic;
+ * per output it is within 2e-3 * sum_k |w[n][k] x[m][k]| of the exact sum.
+ * Workspace: currently none (required size 0); ws/ws_bytes may be NULL.
+ */
+int w4_gemv(const uint32_t* qw, const uint16_t* scales, const uint16_t* biases,
+            const uint16_t* x, int64_t ldx, float* y, int64_t ldy,
+            int64_t M, int64_t N, int64_t K, void* ws, size_t* ws_bytes, w4_stream_t stream);
+
+/*
+ * w4_dequant_f16_t -- the prefill's "transposed half-precision scratch" ("Crossing Mojo
+ * 1.0": each weight dequantized once per prefill):
+ *   wt[k][n] = RN16(s[n][k/64] * q[n][k] + b[n][k/64])
+ * with one round-to-nearest-even step from the exact value (subnormals kept).
+ *   wt f16 [K][N] with row stride ldwt (N contiguous).
+ * Requires N >= 1, K >= 64, K % 64 == 0, ldwt >= N; qw, scales, biases 16-byte aligned,
+ * wt 2-byte aligned (16-byte aligned with ldwt % 8 == 0 for full-speed stores).  Bit-exact.
+ */
+int w4_dequant_f16_t(const uint32_t* qw, const uint16_t* scales, const uint16_t* biases,
+                     uint16_t* wt, int64_t ldwt, int64_t N, int64_t K, w4_stream_t stream);
+
+/*
+ * gemm_f16 -- C = A * B with f16 inputs and f32 accumulation and output: the prefill GEMM
+ * on the f16 scratch ("Crossing Mojo 1.0") and the f16 LM head ("What's inside the engine
+ * today": the head streamed as a [hidden x vocab] matrix per token).
+ *   A f16 [M][K] (row stride lda), B f16 [K][N] (row stride ldb, N contiguous),
+ *   C f32 [M][N] (row stride ldc).
+ * Requires M, N, K >= 1, lda >= K, ldb >= N, ldc >= N; A, B 2-byte aligned, C 4-byte
+ * aligned.  Large M uses matrix cores (needs K % 8 == 0, N % 8 == 0, lda and ldb multiples
+ * of 8, A and B 16-byte aligned); M <= 8 with N % 8 == 0 and aligned B streams B once;
+ * any other shape or alignment (e.g. one column of a head, B = H + id, ldb = V) takes a
+ * plain path.  Per output within 2e-3 * sum_k |A[m][k] B[k][n]| of the exact sum.
+ * Workspace: currently none (required size 0).
+ */
+int gemm_f16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C, int64_t ldc,
+             int64_t M, int64_t N, int64_t K, void* ws, size_t* ws_bytes, w4_stream_t stream);
+
+/*
+ * logits_argmax_topk -- on-device token selection ("Crossing Mojo 1.0": argmax/top-k on
+ * the GPU instead of downloading the logits; "What's inside the engine today": bit-exact
+ * against the host reference; "engine-mlx", "Tech details": in-graph greedy argmax).
+ *   logits f32 [M][V] (row stride ldl); idx int32 [M][k] and val f32 [M][k] outputs.
+ * Per row: the k largest logits ordered by value descending, ties to the lower index,
+ * -0.0 equal to +0.0; idx[m][0] is the argmax; val[m][r] == logits[m][idx[m][r]] bit for bit.
+ * Requires 1 <= M, 1 <= k <= min(V, 256), V < 2^31, ldl >= V, ceil(V / 8192) * k <= 8192;
+ * logits 4-byte aligned, idx/val 4-byte aligned.  Logits must be finite (unchecked).
+ * Workspace: M * ceil(V / chunk) * k * 8 bytes (query it; 0 when V <= 4096).
+ */
+int logits_argmax_topk(const float* logits, int64_t ldl, int64_t M, int64_t V, int64_t k,
+                       int32_t* idx, float* val, void* ws, size_t* ws_bytes, w4_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4_H */

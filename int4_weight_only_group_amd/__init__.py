@@ -1,0 +1,189 @@
+"""Group-wise affine int4 weight-only linear layer for MI355X (gfx950).
+
+Thin Python binding over the C ABI in include/w4.h (libw4.so).  Every function here only
+checks and marshals torch tensors (dtype, device, strides) and calls the library on the
+current HIP stream; all computation happens in the HIP kernels.  There is no CPU fallback.
+
+Weight format: packed codes ``qw`` int32 [N][K/8] (uint32 bit patterns, eight 4-bit codes
+per word, low nibble first), ``scales`` and ``biases`` float16 [N][K/64]; the weight is
+w[n][k] = scales[n][k//64] * q[n][k] + biases[n][k//64].
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._lib import lib, LIB_PATH  # noqa: F401
+
+__all__ = [
+    "W4Error", "w4_pack", "w4_gemv", "w4_dequant_f16_t", "gemm_f16", "logits_argmax_topk",
+    "topk_workspace_bytes", "status_string",
+]
+
+W4_OK = 0
+
+
+class W4Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+
+
+def status_string(status: int) -> str:
+    return lib().w4_strerror(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != W4_OK:
+        raise W4Error(fn, status)
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+
+
+def _rowmajor(t: torch.Tensor, name: str) -> int:
+    """Leading dimension of a 2-D tensor whose rows are contiguous."""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with contiguous rows (stride(1) == 1)")
+    return t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
+
+
+def _contig(t: torch.Tensor, name: str) -> None:
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def w4_pack(q: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """uint8 codes [N][K] -> packed int32 words [N][K/8] (eight codes per word)."""
+    _dev(q, "q", torch.uint8)
+    _contig(q, "q")
+    n, k = q.shape
+    if out is None:
+        out = torch.empty((n, k // 8), dtype=torch.int32, device=q.device)
+    _dev(out, "out", torch.int32)
+    _contig(out, "out")
+    if tuple(out.shape) != (n, k // 8):
+        raise ValueError("out must be [N][K/8]")
+    _check("w4_pack", lib().w4_pack(q.data_ptr(), out.data_ptr(), n, k, _stream()))
+    return out
+
+
+def _w4_args(qw, scales, biases):
+    _dev(qw, "qw", torch.int32)
+    _dev(scales, "scales", torch.float16)
+    _dev(biases, "biases", torch.float16)
+    for t, nm in ((qw, "qw"), (scales, "scales"), (biases, "biases")):
+        _contig(t, nm)
+    n, kw = qw.shape
+    k = kw * 8
+    if tuple(scales.shape) != (n, k // 64) or tuple(biases.shape) != (n, k // 64):
+        raise ValueError("scales and biases must be [N][K/64]")
+    return n, k
+
+
+def w4_gemv(qw: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, x: torch.Tensor,
+            out: torch.Tensor | None = None) -> torch.Tensor:
+    """y[m][n] = sum_k w[n][k] x[m][k] for x float16 [M][K] (M <= 16) -> float32 [M][N]."""
+    n, k = _w4_args(qw, scales, biases)
+    _dev(x, "x", torch.float16)
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError("x must be [M][K]")
+    ldx = _rowmajor(x, "x")
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32)
+    if tuple(out.shape) != (m, n):
+        raise ValueError("out must be [M][N]")
+    ldy = _rowmajor(out, "out")
+    _check("w4_gemv", lib().w4_gemv(qw.data_ptr(), scales.data_ptr(), biases.data_ptr(),
+                                    x.data_ptr(), ldx, out.data_ptr(), ldy, m, n, k, None, None,
+                                    _stream()))
+    return out
+
+
+def w4_dequant_f16_t(qw: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor,
+                     out: torch.Tensor | None = None) -> torch.Tensor:
+    """Transposed f16 scratch: float16 [K][N], out[k][n] = RN16(s*q + b)."""
+    n, k = _w4_args(qw, scales, biases)
+    if out is None:
+        out = torch.empty((k, n), dtype=torch.float16, device=qw.device)
+    _dev(out, "out", torch.float16)
+    if tuple(out.shape) != (k, n):
+        raise ValueError("out must be [K][N]")
+    ldwt = _rowmajor(out, "out")
+    _check("w4_dequant_f16_t", lib().w4_dequant_f16_t(qw.data_ptr(), scales.data_ptr(),
+                                                      biases.data_ptr(), out.data_ptr(), ldwt, n,
+                                                      k, _stream()))
+    return out
+
+
+def gemm_f16(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """C = A @ B: float16 A [M][K], float16 B [K][N] (rows contiguous) -> float32 [M][N]."""
+    _dev(a, "a", torch.float16)
+    _dev(b, "b", torch.float16)
+    lda, ldb = _rowmajor(a, "a"), _rowmajor(b, "b")
+    m, k = a.shape
+    k2, n = b.shape
+    if k != k2:
+        raise ValueError("inner dimensions differ")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=a.device)
+    _dev(out, "out", torch.float32)
+    if tuple(out.shape) != (m, n):
+        raise ValueError("out must be [M][N]")
+    ldc = _rowmajor(out, "out")
+    _check("gemm_f16", lib().gemm_f16(a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc,
+                                      m, n, k, None, None, _stream()))
+    return out
+
+
+def topk_workspace_bytes(m: int, v: int, k: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("logits_argmax_topk", lib().logits_argmax_topk(
+        ctypes.c_void_p(16), v, m, v, k, ctypes.c_void_p(16), ctypes.c_void_p(16), None,
+        ctypes.byref(n), None))
+    return int(n.value)
+
+
+def logits_argmax_topk(logits: torch.Tensor, k: int, idx: torch.Tensor | None = None,
+                       val: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Per row the k largest logits (value desc, ties to lower index): (int32 idx, float32 val)."""
+    _dev(logits, "logits", torch.float32)
+    ldl = _rowmajor(logits, "logits")
+    m, v = logits.shape
+    if idx is None:
+        idx = torch.empty((m, k), dtype=torch.int32, device=logits.device)
+    if val is None:
+        val = torch.empty((m, k), dtype=torch.float32, device=logits.device)
+    _dev(idx, "idx", torch.int32)
+    _dev(val, "val", torch.float32)
+    _contig(idx, "idx")
+    _contig(val, "val")
+    if tuple(idx.shape) != (m, k) or tuple(val.shape) != (m, k):
+        raise ValueError("idx and val must be [M][k]")
+    need = ctypes.c_size_t(0)
+    _check("logits_argmax_topk", lib().logits_argmax_topk(
+        logits.data_ptr(), ldl, m, v, k, idx.data_ptr(), val.data_ptr(), None,
+        ctypes.byref(need), None))
+    if need.value and (workspace is None or workspace.numel() * workspace.element_size() < need.value):
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=logits.device)
+    ws_ptr = workspace.data_ptr() if need.value else None
+    cap = ctypes.c_size_t(workspace.numel() * workspace.element_size() if need.value else 0)
+    _check("logits_argmax_topk", lib().logits_argmax_topk(
+        logits.data_ptr(), ldl, m, v, k, idx.data_ptr(), val.data_ptr(), ws_ptr,
+        ctypes.byref(cap) if need.value else None, _stream()))
+    return idx, val

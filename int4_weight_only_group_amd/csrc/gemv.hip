@@ -1,0 +1,249 @@
+// w4_gemv: decode GEMV over group-wise affine int4 weights (M = 1..16 activation rows).
+//
+// What it computes ("The inference engine -- Mojo 1.0 on Metal", "Crossing Mojo 1.0" and
+// "What's inside the engine today": the multi-row decode GEMV whose weight stream is the
+// limit):  y[m][n] = sum_k (s[n][g] q[n][k] + b[n][g]) x[m][k],  g = k / 64.
+//
+// Design for CDNA4 (wave64, HBM-bound):
+//  * A "team" of P lanes (P = 64, or 32 for short rows) owns R output rows.  Lane l of a
+//    team streams 16-byte chunks (32 codes = half a group) c = l, l+P, l+2P, ... of each
+//    of its R rows, so every load instruction of a wave reads P*16 contiguous bytes of one
+//    row and R independent weight streams are in flight per lane.
+//  * x is staged once per workgroup in LDS (per K-tile when M*K is large), with each
+//    8-element block re-ordered into the f16 pairs (x0,x4) (x1,x5) (x2,x6) (x3,x7) that
+//    match the order in which codes come out of a word.
+//  * Codes become f16 without conversion instructions: OR-ing a nibble into the mantissa
+//    of 1024.0 (0x6400) gives exactly 1024 + q; a nibble sitting at bits 4..7 OR-ed into
+//    64.0 (0x5400) gives exactly 64 + q.  So one word w (codes q0..q7) yields
+//      (w & 0x000F000F) | 0x64006400 = (1024+q0, 1024+q4)
+//      (w & 0x00F000F0) | 0x54005400 = (  64+q1,   64+q5)
+//    and the same on w >> 8 for (q2,q6), (q3,q7).  A packed f16 subtract removes the
+//    offset exactly, a packed f16 FMA forms w = s q + b with one rounding (the same value
+//    the prefill scratch holds), and v_dot2_f32_f16 accumulates w*x in f32 (the f16
+//    products are exact in f32).  Every term's error is thus relative to |w x|, which keeps
+//    each output within 2e-3 * sum_k |w x| (and exactly 0 when every w x is 0), at 17 VALU
+//    operations per 8 weights, shared by all M activation rows except the 4 dot products.
+//  * Each team reduces its lanes with cross-lane shuffles; one lane stores y.
+#include "w4_internal.h"
+
+namespace w4 {
+
+namespace {
+
+constexpr int kWG = 256;
+constexpr int kLdsBudget = 64 * 1024;
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(hf16x2, a), __builtin_bit_cast(hf16x2, b), c,
+                                false);
+}
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
+__device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// The 8 weights of word w as f16 pairs matching the x pair order (see file comment).
+__device__ __forceinline__ uint4 word_weights(uint32_t w, h2 s2, h2 b2) {
+  const uint32_t w8 = w >> 8;
+  const h2 o1024 = {(f16)1024.0f, (f16)1024.0f}, o64 = {(f16)64.0f, (f16)64.0f};
+  const h2 q0 = as_h2((w & 0x000F000Fu) | 0x64006400u) - o1024;   // exact
+  const h2 q1 = as_h2((w & 0x00F000F0u) | 0x54005400u) - o64;
+  const h2 q2 = as_h2((w8 & 0x000F000Fu) | 0x64006400u) - o1024;
+  const h2 q3 = as_h2((w8 & 0x00F000F0u) | 0x54005400u) - o64;
+  uint4 r;
+  r.x = as_u32(__builtin_elementwise_fma(q0, s2, b2));             // one rounding
+  r.y = as_u32(__builtin_elementwise_fma(q1, s2, b2));
+  r.z = as_u32(__builtin_elementwise_fma(q2, s2, b2));
+  r.w = as_u32(__builtin_elementwise_fma(q3, s2, b2));
+  return r;
+}
+
+__device__ __forceinline__ float pair_dot(uint4 w, uint4 x, float acc) {
+  acc = dot2(w.x, x.x, acc);
+  acc = dot2(w.y, x.y, acc);
+  acc = dot2(w.z, x.z, acc);
+  acc = dot2(w.w, x.w, acc);
+  return acc;
+}
+
+// (x0x1, x2x3, x4x5, x6x7) -> (x0x4, x1x5, x2x6, x3x7)
+__device__ __forceinline__ uint4 pair_up(uint4 d) {
+  uint4 p;
+  p.x = (d.x & 0xFFFFu) | (d.z << 16);
+  p.y = (d.x >> 16) | (d.z & 0xFFFF0000u);
+  p.z = (d.y & 0xFFFFu) | (d.w << 16);
+  p.w = (d.y >> 16) | (d.w & 0xFFFF0000u);
+  return p;
+}
+
+template <int MT, int R, int P>
+__global__ __launch_bounds__(kWG) void gemv_kernel(const uint32_t* __restrict__ qw,
+                                                   const uint16_t* __restrict__ sc,
+                                                   const uint16_t* __restrict__ bi,
+                                                   const uint16_t* __restrict__ x, int64_t ldx,
+                                                   float* __restrict__ y, int64_t ldy, int M,
+                                                   int N, int K, int KT) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int TEAMS = kWG / P;
+  const int CT = KT / 32;  // chunks per K-tile
+  uint4* xs = reinterpret_cast<uint4*>(smem);  // [MT][CT][4]
+
+  const int tid = threadIdx.x;
+  const int lane = tid % P;
+  const int team = tid / P;
+  const int row0 = (blockIdx.x * TEAMS + team) * R;
+  const int64_t KW = K / 8;  // words per row
+  const int G = K / kGroup;  // groups per row
+
+  const uint4* rowp[R];
+  const uint16_t* sp[R];
+  const uint16_t* bp[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int n = min(row0 + r, N - 1);  // clamp: tail rows reload the last row, never stored
+    rowp[r] = reinterpret_cast<const uint4*>(qw + (int64_t)n * KW);
+    sp[r] = sc + (int64_t)n * G;
+    bp[r] = bi + (int64_t)n * G;
+  }
+
+  float acc[R][MT];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[r][m] = 0.f;
+
+  for (int k0 = 0; k0 < K; k0 += KT) {
+    const int ct = min(CT, (K - k0) / 32);
+    if (k0 > 0) __syncthreads();
+    // ---- stage x[:, k0 : k0+KT) as re-ordered pairs, one 8-element block per item
+    for (int i = tid; i < MT * CT * 4; i += kWG) {
+      const int m = i / (CT * 4), cb = i - m * (CT * 4);
+      uint4 p = make_uint4(0, 0, 0, 0);
+      if (m < M && cb < ct * 4)
+        p = pair_up(*reinterpret_cast<const uint4*>(x + (int64_t)m * ldx + k0 + cb * 8));
+      xs[m * CT * 4 + cb] = p;
+    }
+    __syncthreads();
+
+    // ---- stream this tile's chunks of the team's R rows
+    const int c0 = k0 / 32;
+#pragma unroll 2
+    for (int cl = lane; cl < ct; cl += P) {
+      const int c = c0 + cl;
+      uint4 w[R];
+      uint16_t sbits[R], bbits[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) w[r] = load_nt(rowp[r] + c);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        sbits[r] = sp[r][c >> 1];
+        bbits[r] = bp[r][c >> 1];
+      }
+      uint4 wv[R][4];  // dequantized f16 pairs of the chunk, per row and word
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const f16 sv = __builtin_bit_cast(f16, sbits[r]), bv = __builtin_bit_cast(f16, bbits[r]);
+        const h2 s2 = {sv, sv}, b2 = {bv, bv};
+        wv[r][0] = word_weights(w[r].x, s2, b2);
+        wv[r][1] = word_weights(w[r].y, s2, b2);
+        wv[r][2] = word_weights(w[r].z, s2, b2);
+        wv[r][3] = word_weights(w[r].w, s2, b2);
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const uint4* xm = xs + (m * CT + cl) * 4;
+        const uint4 x0 = xm[0], x1 = xm[1], x2 = xm[2], x3 = xm[3];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float a = acc[r][m];
+          a = pair_dot(wv[r][0], x0, a);
+          a = pair_dot(wv[r][1], x1, a);
+          a = pair_dot(wv[r][2], x2, a);
+          a = pair_dot(wv[r][3], x3, a);
+          acc[r][m] = a;
+        }
+      }
+    }
+  }
+
+  // ---- team reduction and store
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      float v = acc[r][m];
+#pragma unroll
+      for (int off = P / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, P);
+      acc[r][m] = v;
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int n = row0 + r;
+      if (n < N) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          if (m < M) y[(int64_t)m * ldy + n] = acc[r][m];
+      }
+    }
+  }
+}
+
+template <int MT, int R, int P>
+void launch_t(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
+              int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
+  // K-tile: as much of x as fits the LDS budget (64 bytes per 32-element chunk and row).
+  const int per_chunk = MT * 64;
+  int ct = kLdsBudget / per_chunk;
+  const int C = K / 32;
+  if (ct > C) ct = C;
+  const int KT = ct * 32;
+  const size_t lds = (size_t)MT * ct * 64;
+  constexpr int rows_per_wg = (kWG / P) * R;
+  const unsigned grid = (unsigned)((N + rows_per_wg - 1) / rows_per_wg);
+  hipLaunchKernelGGL((gemv_kernel<MT, R, P>), dim3(grid), dim3(kWG), lds, st, qw, s, b, x, ldx,
+                     y, ldy, M, N, K, KT);
+}
+
+template <int MT, int P>
+void launch_r(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
+              int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
+  // Rows per team: enough workgroups to fill 256 CUs twice before giving a lane more rows.
+  constexpr int teams = kWG / P;
+  const int64_t want = 512;
+  if (MT <= 4 && (int64_t)N / (teams * 4) >= want)
+    launch_t<MT, 4, P>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+  else if ((int64_t)N / (teams * 2) >= want)
+    launch_t<MT, 2, P>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+  else
+    launch_t<MT, 1, P>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+}
+
+template <int MT>
+void launch_p(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
+              int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
+  if (K / 32 <= 32)
+    launch_r<MT, 32>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+  else
+    launch_r<MT, 64>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+}
+
+}  // namespace
+
+void launch_gemv(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
+                 int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
+  if (M <= 1)
+    launch_p<1>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+  else if (M <= 2)
+    launch_p<2>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+  else if (M <= 4)
+    launch_p<4>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+  else if (M <= 8)
+    launch_p<8>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+  else
+    launch_p<16>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+}
+
+}  // namespace w4

@@ -1,0 +1,49 @@
+// Internal declarations shared by the kernel files and the C-ABI layer.
+// Launchers assume their arguments were validated by abi.hip; they only enqueue work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w4 {
+
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __fp16 hf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGroup = 64;  // elements of K per (scale, bias)
+
+// 16-byte streaming load that is not expected to be re-read (non-temporal hint).
+__device__ __forceinline__ uint4 load_nt(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// ---------------------------------------------------------------- launchers
+void launch_pack(const uint8_t* q, uint32_t* qw, int64_t N, int64_t K, hipStream_t st);
+
+void launch_gemv(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
+                 int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st);
+
+void launch_dequant_t(const uint32_t* qw, const uint16_t* s, const uint16_t* b, uint16_t* wt,
+                      int64_t ldwt, int N, int K, hipStream_t st);
+
+// Which gemm path a shape takes (exposed for tests through the ABI's behaviour only).
+enum GemmPath { kGemmMfma = 0, kGemmSmallM = 1, kGemmPlain = 2 };
+GemmPath gemm_path(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M,
+                   int64_t N, int64_t K);
+void launch_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C,
+                 int64_t ldc, int M, int N, int K, hipStream_t st);
+
+// Top-k: chunk size (in logits) used for rows longer than one block, and workspace bytes.
+int topk_chunk(int64_t V, int k);        // 0 when the shape is unsupported
+size_t topk_ws_bytes(int64_t M, int64_t V, int k);
+void launch_topk(const float* logits, int64_t ldl, int M, int V, int k, int32_t* idx, float* val,
+                 void* ws, hipStream_t st);
+
+}  // namespace w4

@@ -1,0 +1,133 @@
+"""The C-ABI library loads, exports what include/w4.h declares, and rejects bad arguments
+on the host before touching a device (CPU only: no kernel is launched here)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4.h")
+
+W4_OK, W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_ALIGN, W4_ERR_WORKSPACE, W4_ERR_DEVICE = 0, -1, -2, -3, -4, -5
+
+P = 4096  # a fake, 16-byte aligned "device" address: never dereferenced by these calls
+
+
+def _lib():
+    from int4_weight_only_group_amd._lib import lib
+    return lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+def test_header_declares_the_five_entry_points():
+    names = _declared()
+    for n in ("w4_pack", "w4_gemv", "w4_dequant_f16_t", "gemm_f16", "logits_argmax_topk", "w4_strerror"):
+        assert n in names, names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for n in _declared():
+        assert hasattr(lib, n), n
+    out = os.popen(f"nm -D --defined-only {lib._name}").read()
+    for n in _declared():
+        assert re.search(rf"\bT {n}$", out, flags=re.M), n
+
+
+def test_strerror():
+    lib = _lib()
+    for s in range(-8, 1):
+        assert lib.w4_strerror(s)
+    assert lib.w4_strerror(0) == b"ok"
+
+
+def test_pack_argument_errors():
+    lib = _lib()
+    assert lib.w4_pack(None, P, 4, 64, None) == W4_ERR_NULL
+    assert lib.w4_pack(P, None, 4, 64, None) == W4_ERR_NULL
+    assert lib.w4_pack(P, P, 0, 64, None) == W4_ERR_SHAPE
+    assert lib.w4_pack(P, P, 4, 96, None) == W4_ERR_SHAPE
+    assert lib.w4_pack(P, P, 4, 0, None) == W4_ERR_SHAPE
+    assert lib.w4_pack(P + 8, P, 4, 64, None) == W4_ERR_ALIGN
+
+
+def test_gemv_argument_errors():
+    lib = _lib()
+    g = lambda **kw: lib.w4_gemv(kw.get("qw", P), P, P, kw.get("x", P), kw.get("ldx", 128), P,
+                                 kw.get("ldy", 8), kw.get("M", 1), kw.get("N", 8), kw.get("K", 128),
+                                 None, None, None)
+    assert g(qw=None) == W4_ERR_NULL
+    assert g(M=0) == W4_ERR_SHAPE
+    assert g(M=17) == W4_ERR_SHAPE
+    assert g(K=100, ldx=104) == W4_ERR_SHAPE
+    assert g(ldx=64) == W4_ERR_SHAPE
+    assert g(ldy=4) == W4_ERR_SHAPE
+    assert g(x=P + 2) == W4_ERR_ALIGN
+    assert g(ldx=132) == W4_ERR_ALIGN
+    n = ctypes.c_size_t(123)
+    assert lib.w4_gemv(P, P, P, P, 128, P, 8, 1, 8, 128, None, ctypes.byref(n), None) == W4_OK
+    assert n.value == 0
+
+
+def test_dequant_and_gemm_argument_errors():
+    lib = _lib()
+    assert lib.w4_dequant_f16_t(P, P, P, None, 8, 8, 64, None) == W4_ERR_NULL
+    assert lib.w4_dequant_f16_t(P, P, P, P, 4, 8, 64, None) == W4_ERR_SHAPE
+    assert lib.w4_dequant_f16_t(P, P, P, P + 1, 8, 8, 64, None) == W4_ERR_ALIGN
+    assert lib.gemm_f16(None, 8, P, 8, P, 8, 2, 8, 8, None, None, None) == W4_ERR_NULL
+    assert lib.gemm_f16(P, 4, P, 8, P, 8, 2, 8, 8, None, None, None) == W4_ERR_SHAPE
+    assert lib.gemm_f16(P, 8, P, 8, P, 8, 0, 8, 8, None, None, None) == W4_ERR_SHAPE
+    assert lib.gemm_f16(P + 1, 8, P, 8, P, 8, 2, 8, 8, None, None, None) == W4_ERR_ALIGN
+    assert lib.gemm_f16(P, 8, P, 8, P + 2, 8, 2, 8, 8, None, None, None) == W4_ERR_ALIGN
+
+
+def test_topk_argument_errors_and_workspace_query():
+    lib = _lib()
+    t = lambda **kw: lib.logits_argmax_topk(kw.get("lg", P), kw.get("ldl", kw.get("V", 100)), kw.get("M", 1),
+                                            kw.get("V", 100), kw.get("k", 5), P, P, kw.get("ws", None),
+                                            kw.get("wsb", None), None)
+    assert t(lg=None) == W4_ERR_NULL
+    assert t(k=0) == W4_ERR_SHAPE
+    assert t(k=257, V=1000) == W4_ERR_SHAPE
+    assert t(k=6, V=5) == W4_ERR_SHAPE
+    assert t(ldl=50) == W4_ERR_SHAPE
+    assert t(lg=P + 2) == W4_ERR_ALIGN
+    n = ctypes.c_size_t(0)
+    assert t(V=151936, k=40, M=1, wsb=ctypes.byref(n)) == W4_OK
+    assert n.value == 38 * 40 * 8  # 38 chunks of 4096 logits, 40 keys of 8 bytes each
+    small = ctypes.c_size_t(n.value - 8)
+    assert t(V=151936, k=40, ws=P, wsb=ctypes.byref(small)) == W4_ERR_WORKSPACE
+    assert t(V=151936, k=40, ws=None, wsb=None) == W4_ERR_WORKSPACE
+    n2 = ctypes.c_size_t(7)
+    assert t(V=2, k=1, M=16, wsb=ctypes.byref(n2)) == W4_OK and n2.value == 0
+
+
+@pytest.mark.skipif(_has_gpu(), reason="checks the no-device error path")
+def test_valid_call_without_device_reports_device_error():
+    lib = _lib()
+    assert lib.w4_pack(P, P, 4, 64, None) == W4_ERR_DEVICE
+    assert lib.gemm_f16(P, 8, P, 8, P, 8, 2, 8, 8, None, None, None) == W4_ERR_DEVICE
+
+
+def test_binding_names_match_abi():
+    import int4_weight_only_group_amd as w4
+    for n in ("w4_pack", "w4_gemv", "w4_dequant_f16_t", "gemm_f16", "logits_argmax_topk"):
+        assert callable(getattr(w4, n))
+    assert w4.topk_workspace_bytes(8, 262144, 64) == 8 * 64 * 64 * 8

@@ -1,0 +1,379 @@
+"""GPU parity: every HIP entry point, called through the C ABI, against the CPU oracle.
+
+Integer and byte work (pack, dequant bits, top-k indices) must be bit-exact; f32 products
+must satisfy |y - y_ref| <= 2e-3 * sum_k |w_k x_k| per output.  Shapes span several tiles
+and ragged tails; the workload shapes run at full size (sampled rows where the fp64
+reference would be slow).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+RTOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def w4():
+    import int4_weight_only_group_amd as m
+    return m
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def to_np(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def upload_layer(w4, q, s, b):
+    qw = w4.w4_pack(dev(q))
+    return qw, dev(s), dev(b)
+
+
+# ----------------------------------------------------------------------------- pack
+
+
+@pytest.mark.parametrize("n,k", [(1, 64), (3, 128), (37, 960), (4864, 896), (257, 2048)])
+def test_pack_bit_exact(w4, n, k):
+    q = synth.codes(n, k, seed=n + k)
+    got = to_np(w4.w4_pack(dev(q))).view(np.uint32)
+    assert np.array_equal(got, oracle.pack(q))
+
+
+def test_pack_keeps_low_nibble(w4):
+    q = np.random.default_rng(3).integers(0, 256, size=(9, 128), dtype=np.uint8)
+    got = to_np(w4.w4_pack(dev(q))).view(np.uint32)
+    assert np.array_equal(got, oracle.pack(q))
+    assert np.array_equal(oracle.unpack(got), q & 0xF)
+
+
+# ----------------------------------------------------------------------------- GEMV
+
+
+def gemv_case(w4, m, n, k, seed, x_override=None, ldx_pad=0, ldy_pad=0):
+    q, s, b = synth.w4_weights(n, k, seed=seed)
+    x = synth.activations(m, k, seed=seed) if x_override is None else x_override
+    qw, sd, bd = upload_layer(w4, q, s, b)
+    xd_full = dev(np.pad(x, ((0, 0), (0, ldx_pad))))
+    xd = xd_full[:, :k]
+    yd_full = torch.full((m, n + ldy_pad), 7.0, dtype=torch.float32, device="cuda")
+    yd = yd_full[:, :n]
+    w4.w4_gemv(qw, sd, bd, xd, out=yd)
+    y = to_np(yd_full)
+    if ldy_pad:
+        assert np.all(y[:, n:] == 7.0), "write outside y"
+    y_ref, bound = oracle.gemv_ref(oracle.pack(q), s, b, x)
+    ok, worst = oracle.check_bound(y[:, :n], y_ref, bound, RTOL)
+    assert ok, f"(M,N,K)=({m},{n},{k}) worst err/bound {worst:.3g}"
+    return worst
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 5, 8, 11, 16])
+@pytest.mark.parametrize("n,k", [(1, 64), (3, 128), (257, 960), (70, 2048), (33, 2112), (5, 11008)])
+def test_gemv_small_shapes(w4, m, n, k):
+    gemv_case(w4, m, n, k, seed=1000 * m + n + k)
+
+
+def test_gemv_strided_x_and_y(w4):
+    gemv_case(w4, 3, 129, 384, seed=5, ldx_pad=24, ldy_pad=5)
+    gemv_case(w4, 1, 64, 1024, seed=6, ldx_pad=8, ldy_pad=1)
+
+
+def test_gemv_zero_rows_are_exactly_zero(w4):
+    x = synth.activations(4, 256, seed=7)
+    x[1] = 0
+    x[3] = 0
+    q, s, b = synth.w4_weights(50, 256, seed=7)
+    qw, sd, bd = upload_layer(w4, q, s, b)
+    y = to_np(w4.w4_gemv(qw, sd, bd, dev(x)))
+    assert not y[1].any() and not y[3].any()
+
+
+def test_gemv_closed_form_constant_codes(w4):
+    # q = c, s = 1, b = 0  ->  y = c * sum(x)
+    k, n = 896, 40
+    x = synth.activations(2, k, seed=8)
+    for c in (0, 5, 15):
+        q = np.full((n, k), c, np.uint8)
+        s = np.ones((n, k // 64), np.float16)
+        b = np.zeros((n, k // 64), np.float16)
+        qw, sd, bd = upload_layer(w4, q, s, b)
+        y = to_np(w4.w4_gemv(qw, sd, bd, dev(x)))
+        want = c * x.astype(np.float64).sum(axis=1)
+        bound = c * np.abs(x.astype(np.float64)).sum(axis=1)
+        assert np.all(np.abs(y - want[:, None]) <= RTOL * bound[:, None])
+
+
+def test_gemv_cancelling_weights_are_exactly_zero(w4):
+    # q = 8 with b = -8 s: every weight is exactly 0, so y must be exactly 0 (bound 0)
+    k, n = 2048, 96
+    x = synth.activations(5, k, seed=17)
+    _, s, _ = synth.w4_weights(n, k, seed=17)
+    b = (-8.0 * s.astype(np.float64)).astype(np.float16)
+    q = np.full((n, k), 8, np.uint8)
+    qw, sd, bd = upload_layer(w4, q, s, b)
+    y = to_np(w4.w4_gemv(qw, sd, bd, dev(x)))
+    assert not y.any()
+    # and a mix: half the groups cancel, half do not
+    q[:, : k // 2] = synth.codes(n, k // 2, seed=18)
+    qw, sd, bd = upload_layer(w4, q, s, b)
+    y = to_np(w4.w4_gemv(qw, sd, bd, dev(x)))
+    y_ref, bound = oracle.gemv_ref(oracle.pack(q), s, b, x)
+    assert oracle.check_bound(y, y_ref, bound, RTOL)[0]
+
+
+def test_gemv_single_config_full(w4):
+    # single W4A16 GEMV (M, N, K) = (1, 4864, 896), seed 0
+    q, s, b = synth.w4_weights(4864, 896, seed=0, workload=synth.W_SINGLE)
+    x = synth.activations(1, 896, seed=0, workload=synth.W_SINGLE)
+    qw, sd, bd = upload_layer(w4, q, s, b)
+    y = to_np(w4.w4_gemv(qw, sd, bd, dev(x)))
+    y_ref, bound = oracle.gemv_ref(oracle.pack(q), s, b, x)
+    ok, worst = oracle.check_bound(y, y_ref, bound, RTOL)
+    assert ok, worst
+
+
+WORKLOAD_SHAPES = sorted({(n, k) for _, n, k in synth.QWEN25_3B_LAYER}
+                         | {(n, k) for _, n, k in synth.QWEN3_1P7B_CLASSIFY}
+                         | {(n, k) for _, n, k in synth.GEMMA12B_LAYER})
+
+
+@pytest.mark.parametrize("n,k", WORKLOAD_SHAPES)
+@pytest.mark.parametrize("m", [1, 8, 16])
+def test_gemv_workload_shapes_full(w4, m, n, k):
+    gemv_case(w4, m, n, k, seed=n * 7 + k + m)
+
+
+def test_gemv_deterministic(w4):
+    q, s, b = synth.w4_weights(2048, 2048, seed=9)
+    x = synth.activations(3, 2048, seed=9)
+    qw, sd, bd = upload_layer(w4, q, s, b)
+    xd = dev(x)
+    y1 = to_np(w4.w4_gemv(qw, sd, bd, xd))
+    y2 = to_np(w4.w4_gemv(qw, sd, bd, xd))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+# ------------------------------------------------------------------------- dequant
+
+
+@pytest.mark.parametrize("n,k", [(1, 64), (7, 192), (65, 128), (257, 960), (100, 2112), (2048, 11008), (11008, 2048)])
+def test_dequant_bit_exact(w4, n, k):
+    q, s, b = synth.w4_weights(n, k, seed=n + 3 * k)
+    qw, sd, bd = upload_layer(w4, q, s, b)
+    got = to_np(w4.w4_dequant_f16_t(qw, sd, bd)).view(np.uint16)
+    assert np.array_equal(got, oracle.dequant_f16_t(oracle.pack(q), s, b))
+
+
+def test_dequant_strided_output(w4):
+    n, k = 40, 256
+    q, s, b = synth.w4_weights(n, k, seed=11)
+    qw, sd, bd = upload_layer(w4, q, s, b)
+    full = torch.full((k, n + 8), -1.0, dtype=torch.float16, device="cuda")
+    w4.w4_dequant_f16_t(qw, sd, bd, out=full[:, :n])
+    got = to_np(full).view(np.uint16)
+    assert np.array_equal(got[:, :n], oracle.dequant_f16_t(oracle.pack(q), s, b))
+    assert np.all(got[:, n:] == np.float16(-1.0).view(np.uint16))
+
+
+def test_dequant_rounding_pins(w4):
+    # the hand-derived rounding cases (tests/golden/f16_dequant.json) through the GPU
+    import json, os
+    cases = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "f16_dequant.json")))["cases"]
+    n = len(cases)
+    q = np.zeros((n, 64), np.uint8)
+    s = np.zeros((n, 1), np.uint16)
+    b = np.zeros((n, 1), np.uint16)
+    for i, c in enumerate(cases):
+        q[i, 5] = c["q"]
+        s[i, 0] = int(c["s"], 16)
+        b[i, 0] = int(c["b"], 16)
+    qw, sd, bd = upload_layer(w4, q, s.view(np.float16), b.view(np.float16))
+    got = to_np(w4.w4_dequant_f16_t(qw, sd, bd)).view(np.uint16)
+    for i, c in enumerate(cases):
+        assert got[5, i] == int(c["w"], 16), c
+        assert got[0, i] == int(c["b"], 16), c
+
+
+def test_dequant_random_scales_full_f16_range(w4):
+    # scales and biases drawn over the whole finite f16 range with subnormals
+    r = np.random.default_rng(12)
+    n, k = 300, 128
+    q = synth.codes(n, k, seed=12)
+    s = r.integers(0, 0x7BFF, size=(n, 2)).astype(np.uint16)
+    b = r.integers(0, 0xFBFF, size=(n, 2)).astype(np.uint16)
+    b[(b & 0x7C00) == 0x7C00] = 0
+    s[:50] = r.integers(0, 0x0400, size=(50, 2))  # subnormal scales
+    b[:50] = r.integers(0, 0x0400, size=(50, 2)) | 0x8000
+    w = oracle.dequant_exact(oracle.pack(q), s.view(np.float16), b.view(np.float16))
+    keep = np.all(np.abs(w) < 65504, axis=1)
+    q, s, b = q[keep], s[keep], b[keep]
+    qw, sd, bd = upload_layer(w4, q, s.view(np.float16), b.view(np.float16))
+    got = to_np(w4.w4_dequant_f16_t(qw, sd, bd)).view(np.uint16)
+    assert np.array_equal(got, oracle.dequant_f16_t(oracle.pack(q), s.view(np.float16), b.view(np.float16)))
+
+
+# ---------------------------------------------------------------------------- GEMM
+
+
+def gemm_case(w4, m, n, k, seed, lda_pad=0, ldb_pad=0, ldc_pad=0, a=None, bmat=None):
+    a = synth.activations(m, k, seed=seed) if a is None else a
+    bmat = synth.activations(k, n, seed=seed + 1) if bmat is None else bmat
+    ad = dev(np.pad(a, ((0, 0), (0, lda_pad))))[:, :k]
+    bd = dev(np.pad(bmat, ((0, 0), (0, ldb_pad))))[:, :n]
+    cfull = torch.full((m, n + ldc_pad), 3.0, dtype=torch.float32, device="cuda")
+    w4.gemm_f16(ad, bd, out=cfull[:, :n])
+    c = to_np(cfull)
+    if ldc_pad:
+        assert np.all(c[:, n:] == 3.0)
+    c_ref, bound = oracle.gemm_ref(a, bmat)
+    ok, worst = oracle.check_bound(c[:, :n], c_ref, bound, RTOL)
+    assert ok, f"(M,N,K)=({m},{n},{k}) worst {worst:.3g}"
+    return c[:, :n]
+
+
+@pytest.mark.parametrize("m,n,k", [
+    (9, 8, 8), (33, 264, 72), (130, 520, 200), (257, 1000, 2056), (128, 256, 32), (1570, 264, 64),
+    (300, 2048, 1000), (17, 8, 4096),
+])
+def test_gemm_mfma_path(w4, m, n, k):
+    gemm_case(w4, m, n, k, seed=m + n + k)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 8, 8), (3, 1032, 2048), (8, 4096, 256), (5, 520, 3840), (1, 4752, 2048)])
+def test_gemm_small_m_path(w4, m, n, k):
+    gemm_case(w4, m, n, k, seed=m + n + k)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 1), (16, 1, 2048), (3, 5, 7), (20, 3, 100), (2, 13, 64)])
+def test_gemm_plain_path(w4, m, n, k):
+    gemm_case(w4, m, n, k, seed=m + n + k)
+
+
+def test_gemm_strided_operands(w4):
+    gemm_case(w4, 40, 128, 96, seed=1, lda_pad=8, ldb_pad=16, ldc_pad=3)
+    gemm_case(w4, 2, 256, 64, seed=2, lda_pad=8, ldb_pad=8, ldc_pad=1)
+
+
+def test_gemm_identity_is_exact(w4):
+    a = synth.activations(70, 64, seed=3)
+    c = gemm_case(w4, 70, 64, 64, seed=3, a=a, bmat=np.eye(64, dtype=np.float16))
+    assert np.array_equal(c, a.astype(np.float32))
+
+
+def test_gemm_head_column_slice(w4):
+    # two columns of an f16 head read through B = H + id with ldb = V (plain path)
+    k, v = 2048, 4099
+    h = synth.head_f16(k, v, seed=4)
+    x = synth.activations(16, k, seed=4)
+    hd, xd = dev(h), dev(x)
+    ids = (17, 4098)
+    out = torch.empty((16, 2), dtype=torch.float32, device="cuda")
+    for j, i in enumerate(ids):
+        w4.gemm_f16(xd, hd[:, i:i + 1], out=out[:, j:j + 1])
+    c = to_np(out)
+    c_ref, bound = oracle.gemm_ref(x, h[:, list(ids)])
+    assert oracle.check_bound(c, c_ref, bound, RTOL)[0]
+
+
+def test_gemm_prefill_sampled_rows(w4):
+    # (M, N, K) = (1570, 11008, 2048): 128 sampled rows incl. the M tail 1536..1569
+    m, n, k = 1570, 11008, 2048
+    a = synth.activations(m, k, seed=5)
+    bmat = synth.activations(k, n, seed=6)
+    c = to_np(w4.gemm_f16(dev(a), dev(bmat)))
+    rows = np.unique(np.concatenate([np.random.default_rng(5).choice(1536, 94, replace=False),
+                                     np.arange(1536, 1570)]))
+    c_ref, bound = oracle.gemm_ref(a[rows], bmat)
+    ok, worst = oracle.check_bound(c[rows], c_ref, bound, RTOL)
+    assert ok, worst
+
+
+def test_gemm_deterministic(w4):
+    a = dev(synth.activations(300, 512, seed=7))
+    b = dev(synth.activations(512, 1024, seed=8))
+    c1 = to_np(w4.gemm_f16(a, b))
+    c2 = to_np(w4.gemm_f16(a, b))
+    assert np.array_equal(c1.view(np.uint32), c2.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------- top-k
+
+
+def topk_case(w4, logits, k):
+    ld = dev(logits)
+    idx, val = w4.logits_argmax_topk(ld, k)
+    idx, val = to_np(idx), to_np(val)
+    ok = oracle.check_topk_selection(logits, idx, val, k)
+    assert ok, (logits.shape, k)
+
+
+@pytest.mark.parametrize("m,v,k", [
+    (1, 1, 1), (1, 2, 1), (16, 2, 1), (3, 5, 5), (2, 100, 40), (1, 4096, 64), (2, 4097, 64),
+    (1, 151936, 40), (8, 262144, 64), (1, 262144, 256), (4, 9000, 256), (1, 40000, 1),
+])
+def test_topk_random(w4, m, v, k):
+    logits = (np.random.default_rng(m * v + k).standard_normal((m, v)) * 0.9).astype(np.float32)
+    topk_case(w4, logits, k)
+
+
+def test_topk_ties_and_signed_zero(w4):
+    r = np.random.default_rng(13)
+    v = 10000
+    rows = [
+        np.zeros(v, np.float32),                                   # all equal
+        np.where(r.random(v) < 0.5, np.float32(-0.0), np.float32(0.0)),  # +-0 mixed
+        np.round(r.standard_normal(v) * 2).astype(np.float32),     # many duplicates
+        np.repeat(np.arange(v // 100, dtype=np.float32), 100)[::-1].copy(),  # runs straddling k
+        -np.abs(r.standard_normal(v)).astype(np.float32),           # all negative
+    ]
+    logits = np.stack(rows)
+    for k in (1, 7, 64, 100, 101, 256):
+        topk_case(w4, logits, k)
+
+
+def test_topk_strided_rows(w4):
+    logits = np.random.default_rng(14).standard_normal((3, 6000)).astype(np.float32)
+    full = dev(np.pad(logits, ((0, 0), (0, 13))))
+    idx, val = w4.logits_argmax_topk(full[:, :6000], 33)
+    assert oracle.check_topk_selection(logits, to_np(idx), to_np(val), 33)
+
+
+def test_topk_deterministic(w4):
+    logits = dev(np.round(np.random.default_rng(15).standard_normal((2, 151936)) * 4).astype(np.float32))
+    a = [to_np(t) for t in w4.logits_argmax_topk(logits, 40)]
+    b = [to_np(t) for t in w4.logits_argmax_topk(logits, 40)]
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
+# ------------------------------------------------------------- a small decode step
+
+
+def test_decode_step_small_end_to_end(w4):
+    # W4 GEMV -> f16 head -> top-k, checked against fp64 logits with the near-tie rule
+    k_hidden, v, n = 512, 5000, 512
+    q, s, b = synth.w4_weights(n, k_hidden, seed=16)
+    x = synth.activations(1, k_hidden, seed=16)
+    h = synth.head_f16(n, v, seed=16)
+    qw, sd, bd = upload_layer(w4, q, s, b)
+    y = w4.w4_gemv(qw, sd, bd, dev(x))
+    y16 = y.to(torch.float16)  # the head consumes f16 activations
+    logits = w4.gemm_f16(y16, dev(h))
+    idx, val = w4.logits_argmax_topk(logits, 40)
+    idx, val, lg = to_np(idx), to_np(val), to_np(logits)
+    assert np.array_equal(val.view(np.uint32), lg[0, idx[0]][None].view(np.uint32))
+    # the oracle's own chain on the host inputs: fp64 GEMV, f16 rounding, fp64 head
+    y_ref, _ = oracle.gemv_ref(oracle.pack(q), s, b, x)
+    exact, _ = oracle.gemm_ref(y_ref.astype(np.float16), h)
+    ok, loose = oracle.check_topk_vs_exact(exact, idx, 40)
+    assert ok, loose
