@@ -172,7 +172,16 @@ def kernel_timings(torch, wl, reps=3):
         e1.record(stream)
         rec.setdefault(key, []).append((e0, e1, nbytes, flops))
 
+    # Give the CPU a head start (a device-side sleep) so every launch and its events are
+    # queued before the GPU reaches them: the events then bracket back-to-back kernels.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    torch.cuda._sleep(1_000_000)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    cycles_per_ms = 1_000_000 / max(e0.elapsed_time(e1), 1e-3)
     for _ in range(reps):
+        torch.cuda._sleep(int(cycles_per_ms * 30))
         for mats in wl.layers:
             for name, qw, s, b, x, y, (m, n, k) in mats:
                 timed(("w4_gemv", m, n, k), gemv_bytes(m, n, k), 0,
@@ -184,7 +193,7 @@ def kernel_timings(torch, wl, reps=3):
                   lambda a=a, wt=wt, c=c: wl.w4.gemm_f16(a, wt, out=c))
         timed(("gemm_f16", 1, wl.V, wl.H), 2 * wl.H * wl.V + 2 * wl.H + 4 * wl.V, 2 * wl.H * wl.V,
               lambda: wl.w4.gemm_f16(wl.x_head, wl.head, out=wl.logits))
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
     out = {}
     for key, lst in rec.items():
         us = [e0.elapsed_time(e1) * 1e3 for e0, e1, _, _ in lst]
@@ -266,26 +275,28 @@ def parity_check(torch, np, wl, oracle, synth):
 
 
 def cpu_baseline(np, oracle, synth):
-    """The oracle's GEMV (unpack + exact dequant + fp64 product) over decoder layer 0's seven
-    matrices at M = 1, on this host's cores."""
+    """The oracle's GEMV (unpack + exact dequant + fp64 product) over the seven matrices of as
+    many decoder layers as take about 10 s, at M = 1, on this host's cores."""
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    mats = []
-    for j, (name, n, k) in enumerate(synth.QWEN25_3B_LAYER):
-        q, s, b = synth.w4_weights(n, k, seed=0, workload=synth.W_DECODE, layer=j)
-        x = synth.activations(1, k, seed=0, workload=synth.W_DECODE, layer=8 + j)
-        mats.append((oracle.pack(q), s, b, x, gemv_bytes(1, n, k)))
-    t0 = time.perf_counter()
     nbytes = 0
-    for qw, s, b, x, nb in mats:
-        oracle.gemv_ref(qw, s, b, x)
-        nbytes += nb
-    dt = time.perf_counter() - t0
+    dt = 0.0
+    layers = 0
+    while dt < 10.0 and layers < synth.QWEN25_3B_LAYERS:  # about 10 s of host work
+        for j, (name, n, k) in enumerate(synth.QWEN25_3B_LAYER):
+            q, s, b = synth.w4_weights(n, k, seed=0, workload=synth.W_DECODE, layer=layers * 16 + j)
+            x = synth.activations(1, k, seed=0, workload=synth.W_DECODE, layer=layers * 16 + 8 + j)
+            qw = oracle.pack(q)
+            t0 = time.perf_counter()
+            oracle.gemv_ref(qw, s, b, x)
+            dt += time.perf_counter() - t0
+            nbytes += gemv_bytes(1, n, k)
+        layers += 1
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"oracle.gemv_ref over decoder layer 0's 7 int4 matrices at M=1 "
+            "sample": f"oracle.gemv_ref over the 7 int4 matrices of {layers} decoder layer(s) at M=1 "
                       f"({nbytes / 1e6:.1f} MB of algorithmic bytes, {dt:.1f} s; NumPy fp64, BLAS threads={threads})",
             "seconds": dt}
 

@@ -109,8 +109,9 @@ int w4_dequant_f16_t(const uint32_t* qw, const uint16_t* scales, const uint16_t*
  * aligned.  Large M uses matrix cores (needs K % 8 == 0, N % 8 == 0, lda and ldb multiples
  * of 8, A and B 16-byte aligned); M <= 8 with N % 8 == 0 and aligned B streams B once;
  * any other shape or alignment (e.g. one column of a head, B = H + id, ldb = V) takes a
- * plain path.  Per output within 2e-3 * sum_k |A[m][k] B[k][n]| of the exact sum.
- * Workspace: currently none (required size 0).
+ * plain path.  Per output within 2e-3 * sum_k |A[m][k] B[k][n]| of the exact sum; the result
+ * is deterministic.  Workspace: shapes whose output tiles would leave most of the 256 CUs
+ * idle split K and need ksplit * M * N * 4 bytes for the partial tiles (query it); 0 otherwise.
  */
 int gemm_f16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C, int64_t ldc,
              int64_t M, int64_t N, int64_t K, void* ws, size_t* ws_bytes, w4_stream_t stream);

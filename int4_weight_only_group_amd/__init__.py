@@ -19,7 +19,7 @@ from ._lib import lib, LIB_PATH  # noqa: F401
 
 __all__ = [
     "W4Error", "w4_pack", "w4_gemv", "w4_dequant_f16_t", "gemm_f16", "logits_argmax_topk",
-    "topk_workspace_bytes", "status_string",
+    "topk_workspace_bytes", "gemm_workspace_bytes", "status_string",
 ]
 
 W4_OK = 0
@@ -130,8 +130,13 @@ def w4_dequant_f16_t(qw: torch.Tensor, scales: torch.Tensor, biases: torch.Tenso
     return out
 
 
-def gemm_f16(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
-    """C = A @ B: float16 A [M][K], float16 B [K][N] (rows contiguous) -> float32 [M][N]."""
+def gemm_f16(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None,
+             workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """C = A @ B: float16 A [M][K], float16 B [K][N] (rows contiguous) -> float32 [M][N].
+
+    Shapes that split K need a workspace (see gemm_workspace_bytes); one is allocated when
+    none (or too small a one) is given.
+    """
     _dev(a, "a", torch.float16)
     _dev(b, "b", torch.float16)
     lda, ldb = _rowmajor(a, "a"), _rowmajor(b, "b")
@@ -145,9 +150,27 @@ def gemm_f16(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None) 
     if tuple(out.shape) != (m, n):
         raise ValueError("out must be [M][N]")
     ldc = _rowmajor(out, "out")
+    need = ctypes.c_size_t(0)
     _check("gemm_f16", lib().gemm_f16(a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc,
-                                      m, n, k, None, None, _stream()))
+                                      m, n, k, None, ctypes.byref(need), None))
+    ws_ptr, cap = None, None
+    if need.value:
+        if workspace is None or workspace.numel() * workspace.element_size() < need.value:
+            workspace = torch.empty(need.value, dtype=torch.uint8, device=a.device)
+        ws_ptr = workspace.data_ptr()
+        cap = ctypes.byref(ctypes.c_size_t(workspace.numel() * workspace.element_size()))
+    _check("gemm_f16", lib().gemm_f16(a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc,
+                                      m, n, k, ws_ptr, cap, _stream()))
     return out
+
+
+def gemm_workspace_bytes(a: torch.Tensor, b: torch.Tensor) -> int:
+    """Workspace bytes gemm_f16 needs for these operands (0 for most shapes)."""
+    need = ctypes.c_size_t(0)
+    _check("gemm_f16", lib().gemm_f16(a.data_ptr(), _rowmajor(a, "a"), b.data_ptr(), _rowmajor(b, "b"),
+                                      ctypes.c_void_p(16), b.shape[1], a.shape[0], b.shape[1], a.shape[1],
+                                      None, ctypes.byref(need), None))
+    return int(need.value)
 
 
 def topk_workspace_bytes(m: int, v: int, k: int) -> int:

@@ -136,12 +136,12 @@ int gemm_f16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, flo
     if (!al2(A) || !al2(B) || !al4(C)) return W4_ERR_ALIGN;
     if (w4::gemm_path(A, lda, B, ldb, M, N, K) == w4::kGemmPlain && (M + 15) / 16 > 65535)
       return W4_ERR_SHAPE;
-    const int w = workspace(ws, ws_bytes, 0);
+    const int w = workspace(ws, ws_bytes, w4::gemm_ws_bytes(A, lda, B, ldb, M, N, K));
     if (w < 0) return w;
     if (w == 1) return W4_OK;
     if (int e = check_device()) return e;
     (void)hipGetLastError();
-    w4::launch_gemm(A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, (hipStream_t)stream);
+    w4::launch_gemm(A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, ws, (hipStream_t)stream);
     return launched();
   } catch (...) {
     return W4_ERR_INTERNAL;

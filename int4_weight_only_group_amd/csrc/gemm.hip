@@ -18,6 +18,8 @@
 //    A values of a k are wave-uniform scalar loads.
 //  * plain (any other shape or alignment, e.g. one strided column of a head): a workgroup
 //    per (column, 16 rows), threads split K.
+#include <mutex>
+
 #include "w4_internal.h"
 
 namespace w4 {
@@ -29,108 +31,196 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 __device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_cast(f16, h); }
 
 // ------------------------------------------------------------------------ MFMA path
-constexpr int BM = 128, BN = 256, BK = 32;
-constexpr int LDS_K = BK + 8;  // f16 per LDS row (padding keeps 16-byte alignment)
+// 256 x 256 block tile, BK = 64, four waves each owning a 128 x 128 tile: 4 x 4
+// v_mfma_f32_32x32x16_f16 accumulators (256 f32 per lane, in AGPRs), one wave per SIMD.
+// LDS holds two stages of A [256][64] and B^T [256][64] (K contiguous, padded rows), so
+// each K-tile costs one barrier and the next tile's global loads are in flight while the
+// matrix cores work on the current one.  B arrives [K][N] (N contiguous); each thread loads
+// an 8 (k) x 8 (n) block with eight 16-byte loads and transposes it in registers with
+// v_perm_b32 before a 16-byte LDS store per column.  Tails: A rows and B column blocks are
+// clamped on load and never stored, the K tail is zero-filled, so the MFMA loop has no
+// guards.  Tiles are ordered so that each XCD works on a contiguous range of them (its own
+// L2 then holds the A and B panels they share).  Shapes with too few tiles for 256 CUs split
+// K; the slices' partial tiles go to the workspace and a second kernel adds them in a fixed
+// order (deterministic).
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int LDK = BK + 8;                      // f16 per LDS row (144 B)
+// B^T rows get 16 extra bytes every 8 rows: the transposed stores put consecutive lanes 8
+// rows apart, which with 144-byte rows would land them all in the same LDS banks.
+__device__ __forceinline__ int brow(int n) { return n * LDK + (n >> 3) * 8; }
+constexpr int STAGE = BM * LDK + BN * LDK + (BN / 8) * 8;  // f16 per stage
+constexpr size_t kGemmLds = 2 * STAGE * sizeof(uint16_t);
 
-__device__ __forceinline__ uint32_t half_of(uint4 v, int j) {
-  const uint32_t d = (j >> 1) == 0 ? v.x : (j >> 1) == 1 ? v.y : (j >> 1) == 2 ? v.z : v.w;
-  return (j & 1) ? (d >> 16) : (d & 0xFFFFu);
+__device__ __forceinline__ uint32_t dword_of(const uint4& v, int d) {
+  return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
 }
 
-__global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint16_t* __restrict__ A,
-                                                        int64_t lda,
-                                                        const uint16_t* __restrict__ B,
-                                                        int64_t ldb, float* __restrict__ C,
-                                                        int64_t ldc, int M, int N, int K,
-                                                        int tilesN) {
-  __shared__ __align__(16) uint16_t As[BM * LDS_K];
-  __shared__ __align__(16) uint16_t Bs[BN * LDS_K];
+struct GemmArgs {
+  const uint16_t* A;
+  const uint16_t* B;
+  float* C;
+  float* ws;
+  int64_t lda, ldb, ldc;
+  int M, N, K;
+  int tilesM, tilesN, ksplit, kslice;
+};
 
-  const int tm = blockIdx.x / tilesN, tn = blockIdx.x % tilesN;
+__device__ __forceinline__ void tile_of(const GemmArgs& g, int bid, int& tm, int& tn, int& split) {
+  // XCD-aware order: the hardware deals workgroups round-robin to 8 XCDs; give each XCD a
+  // contiguous range of the linear order below.
+  const int total = gridDim.x;
+  const int q = total / 8, rem = total % 8, xcd = bid % 8, idx = bid / 8;
+  const int lin = xcd * q + min(xcd, rem) + idx;
+  const int nt = g.tilesM * g.tilesN;
+  split = lin / nt;
+  const int t = lin - split * nt;
+  // groups of 4 tile-rows, column-major inside a group: consecutive tiles share B panels
+  constexpr int GM = 4;
+  const int group = t / (GM * g.tilesN);
+  const int first_m = group * GM;
+  const int gsize = min(g.tilesM - first_m, GM);
+  const int in = t - group * GM * g.tilesN;
+  tm = first_m + in % gsize;
+  tn = in / gsize;
+}
+
+__global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs g) {
+  extern __shared__ __align__(16) uint16_t lds[];
+  int tm, tn, split;
+  tile_of(g, blockIdx.x, tm, tn, split);
   const int m0 = tm * BM, n0 = tn * BN;
+  const int kbeg = split * g.kslice;
+  const int kend = min(g.K, kbeg + g.kslice);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // global -> register mapping
-  const int a_row0 = tid >> 2, a_kc = (tid & 3) * 8;  // + 64 rows for the second chunk
-  const int b_nb = tid & 31, b_kb = tid >> 5;         // 8-column block, 4-row block
-  const uint16_t* a_src[2];
+  // global -> register mapping: A rows a_r + 32 i, 8-element chunk a_kc; B 8x8 block
+  const int a_r = tid >> 3, a_kc = (tid & 7) * 8;
+  const int b_nb = tid & 31, b_kb = tid >> 5;
+  const uint16_t* a_src[8];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int gm = min(m0 + a_row0 + i * 64, M - 1);
-    a_src[i] = A + (int64_t)gm * lda + a_kc;
-  }
-  const int gn = min(n0 + b_nb * 8, N - 8);
-  const uint16_t* b_src = B + gn + (int64_t)(b_kb * 4) * ldb;
+  for (int i = 0; i < 8; ++i)
+    a_src[i] = g.A + (int64_t)min(m0 + a_r + 32 * i, g.M - 1) * g.lda + a_kc;
+  const uint16_t* b_src = g.B + min(n0 + b_nb * 8, g.N - 8) + (int64_t)(b_kb * 8) * g.ldb;
 
-  uint4 ra[2], rb[4];
+  uint4 ra[8], rb[8];
   auto load = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      ra[i] = (k0 + a_kc < K) ? *reinterpret_cast<const uint4*>(a_src[i] + k0) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 8; ++i)
+      ra[i] = (k0 + a_kc < kend) ? *reinterpret_cast<const uint4*>(a_src[i] + k0) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      rb[i] = (k0 + b_kb * 4 + i < K)
-                  ? *reinterpret_cast<const uint4*>(b_src + (int64_t)(k0 + i) * ldb)
+    for (int i = 0; i < 8; ++i)
+      rb[i] = (k0 + b_kb * 8 + i < kend)
+                  ? *reinterpret_cast<const uint4*>(b_src + (int64_t)(k0 + i) * g.ldb)
                   : make_uint4(0, 0, 0, 0);
   };
-  auto store = [&]() {
+  auto store = [&](int stage) {
+    uint16_t* As = lds + stage * STAGE;
+    uint16_t* Bs = As + BM * LDK;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<uint4*>(&As[(a_row0 + i * 64) * LDS_K + a_kc]) = ra[i];
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<uint4*>(&As[(a_r + 32 * i) * LDK + a_kc]) = ra[i];
+    // 8x8 transpose of 16-bit values: column j of the block becomes 8 contiguous k
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      uint2 v;
-      v.x = half_of(rb[0], j) | (half_of(rb[1], j) << 16);
-      v.y = half_of(rb[2], j) | (half_of(rb[3], j) << 16);
-      *reinterpret_cast<uint2*>(&Bs[(b_nb * 8 + j) * LDS_K + b_kb * 4]) = v;
+      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+      const int d = j >> 1;
+      uint4 o;
+      o.x = __builtin_amdgcn_perm(dword_of(rb[1], d), dword_of(rb[0], d), sel);
+      o.y = __builtin_amdgcn_perm(dword_of(rb[3], d), dword_of(rb[2], d), sel);
+      o.z = __builtin_amdgcn_perm(dword_of(rb[5], d), dword_of(rb[4], d), sel);
+      o.w = __builtin_amdgcn_perm(dword_of(rb[7], d), dword_of(rb[6], d), sel);
+      *reinterpret_cast<uint4*>(&Bs[brow(b_nb * 8 + j) + b_kb * 8]) = o;
     }
   };
 
-  f32x16 acc[2][4];
+  f32x16 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  load(0);
-  for (int k0 = 0; k0 < K; k0 += BK) {
-    __syncthreads();
-    store();
-    __syncthreads();
-    if (k0 + BK < K) load(k0 + BK);
+  const int nk = (kend - kbeg + BK - 1) / BK;
+  load(kbeg);
+  store(0);
+  __syncthreads();
+  for (int t = 0; t < nk; ++t) {
+    if (t + 1 < nk) load(kbeg + (t + 1) * BK);
+    const uint16_t* As = lds + (t & 1) * STAGE;
+    const uint16_t* Bs = As + BM * LDK;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       const int kof = ks * 16 + (lane >> 5) * 8;
-      f16x8 a[2], b[4];
+      f16x8 a[4], b[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const f16x8*>(&As[(wm * 64 + i * 32 + (lane & 31)) * LDS_K + kof]);
+      for (int i = 0; i < 4; ++i)
+        a[i] = *reinterpret_cast<const f16x8*>(&As[(wm * 128 + i * 32 + (lane & 31)) * LDK + kof]);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const f16x8*>(&Bs[(wn * 128 + j * 32 + (lane & 31)) * LDS_K + kof]);
+        b[j] = *reinterpret_cast<const f16x8*>(&Bs[brow(wn * 128 + j * 32 + (lane & 31)) + kof]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
+    if (t + 1 < nk) store((t + 1) & 1);
+    __syncthreads();
   }
 
   // D layout of a 32x32 tile: lane l, value r -> row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+  float* out = g.ksplit == 1 ? g.C : g.ws + (int64_t)split * g.M * g.N;
+  const int64_t ldo = g.ksplit == 1 ? g.ldc : g.N;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int col = n0 + wn * 128 + j * 32 + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (row < M && col < N) C[(int64_t)row * ldc + col] = acc[i][j][r];
+        const int row = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (row < g.M && col < g.N) out[(int64_t)row * ldo + col] = acc[i][j][r];
       }
     }
+}
+
+// C[m][n] = sum over s (in order) of ws[s][m][n]
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws,
+                                                            float* __restrict__ C, int64_t ldc,
+                                                            int M, int N, int S) {
+  const int64_t MN = (int64_t)M * N;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < MN; e += (int64_t)gridDim.x * 256) {
+    float v = ws[e];
+    for (int s = 1; s < S; ++s) v += ws[s * MN + e];
+    const int64_t m = e / N, n = e - m * N;
+    C[m * ldc + n] = v;
+  }
+}
+
+struct GemmPlan {
+  int tilesM, tilesN, ksplit, kslice;
+};
+
+GemmPlan plan_mfma(int64_t M, int64_t N, int64_t K) {
+  GemmPlan p;
+  p.tilesM = (int)((M + BM - 1) / BM);
+  p.tilesN = (int)((N + BN - 1) / BN);
+  const int tiles = p.tilesM * p.tilesN;
+  const int kt = (int)((K + BK - 1) / BK);
+  int s = 1;
+  // split K while fewer than half the CUs would have a tile, keeping >= 8 K-tiles per slice
+  while (tiles * s * 2 <= 256 && kt / (s * 2) >= 8) s *= 2;
+  p.ksplit = s;
+  p.kslice = ((kt + s - 1) / s) * BK;
+  p.ksplit = (int)((K + p.kslice - 1) / p.kslice);
+  return p;
+}
+
+__device__ __forceinline__ uint32_t half_of(uint4 v, int j) {
+  const uint32_t d = dword_of(v, j >> 1);
+  return (j & 1) ? (d >> 16) : (d & 0xFFFFu);
 }
 
 // -------------------------------------------------------------------- small-M path
@@ -237,6 +327,13 @@ __global__ __launch_bounds__(256) void gemm_plain_kernel(const uint16_t* __restr
 
 }  // namespace
 
+size_t gemm_ws_bytes(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M,
+                     int64_t N, int64_t K) {
+  if (gemm_path(A, lda, B, ldb, M, N, K) != kGemmMfma) return 0;
+  const GemmPlan p = plan_mfma(M, N, K);
+  return p.ksplit > 1 ? (size_t)p.ksplit * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
 GemmPath gemm_path(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M,
                    int64_t N, int64_t K) {
   const bool vec = K % 8 == 0 && N % 8 == 0 && lda % 8 == 0 && ldb % 8 == 0 && aligned16(A) &&
@@ -246,12 +343,26 @@ GemmPath gemm_path(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ld
 }
 
 void launch_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C,
-                 int64_t ldc, int M, int N, int K, hipStream_t st) {
+                 int64_t ldc, int M, int N, int K, void* ws, hipStream_t st) {
   switch (gemm_path(A, lda, B, ldb, M, N, K)) {
     case kGemmMfma: {
-      const int tilesM = (M + BM - 1) / BM, tilesN = (N + BN - 1) / BN;
-      hipLaunchKernelGGL(gemm_mfma_kernel, dim3((unsigned)(tilesM * tilesN)), dim3(256), 0, st, A,
-                         lda, B, ldb, C, ldc, M, N, K, tilesN);
+      static std::once_flag lds_attr;
+      std::call_once(lds_attr, [] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_mfma_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
+      });
+      const GemmPlan p = plan_mfma(M, N, K);
+      GemmArgs g{A, B, C, reinterpret_cast<float*>(ws), lda, ldb, ldc, M, N, K,
+                 p.tilesM, p.tilesN, p.ksplit, p.kslice};
+      hipLaunchKernelGGL(gemm_mfma_kernel, dim3((unsigned)(p.tilesM * p.tilesN * p.ksplit)),
+                         dim3(256), kGemmLds, st, g);
+      if (p.ksplit > 1) {
+        const int64_t MN = (int64_t)M * N;
+        int64_t blocks = (MN + 255) / 256;
+        if (blocks > 4096) blocks = 4096;
+        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                           reinterpret_cast<const float*>(ws), C, ldc, M, N, p.ksplit);
+      }
       break;
     }
     case kGemmSmallM: {

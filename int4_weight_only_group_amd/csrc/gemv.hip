@@ -191,6 +191,162 @@ __global__ __launch_bounds__(kWG) void gemv_kernel(const uint32_t* __restrict__ 
   }
 }
 
+// ------------------------------------------------------------------ M = 1 kernel
+// Decode at M = 1 needs no LDS: lane l of a team of L lanes always handles the chunks
+// c = l + j*L (j < NIT) of whatever row it streams, so its slice of x is loaded once into
+// registers (re-ordered into pairs).  Each team walks row blocks of R rows with a grid
+// stride, two blocks at a time in ping-pong registers: the next block's loads are in flight
+// while the current one is dequantized and reduced.  The first loads are issued before x is
+// read.  EXACT means L * NIT == K / 32 (no chunk past the end of a row).
+
+// (w & mask) | magic in one VALU op; GFX9 VOP3 takes no literal, so both constants come in
+// as VGPRs.
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "v"(mask), "v"(magic));
+  return r;
+}
+
+struct Consts {
+  uint32_t m_lo, m_hi, mag_lo, mag_hi;  // 0x000F000F, 0x00F000F0, 0x64006400, 0x54005400
+};
+
+// One word's 8 weights (f16 pairs ordered like the x pairs), accumulated into acc.
+__device__ __forceinline__ float word_fma(uint32_t w, h2 s2, h2 b2, const uint4& xp, float acc,
+                                          const Consts& k) {
+  const uint32_t w8 = w >> 8;
+  const h2 o1024 = {(f16)1024.0f, (f16)1024.0f}, o64 = {(f16)64.0f, (f16)64.0f};
+  const h2 q0 = as_h2(and_or(w, k.m_lo, k.mag_lo)) - o1024;   // exact
+  const h2 q1 = as_h2(and_or(w, k.m_hi, k.mag_hi)) - o64;
+  const h2 q2 = as_h2(and_or(w8, k.m_lo, k.mag_lo)) - o1024;
+  const h2 q3 = as_h2(and_or(w8, k.m_hi, k.mag_hi)) - o64;
+  acc = dot2(as_u32(__builtin_elementwise_fma(q0, s2, b2)), xp.x, acc);  // one rounding each
+  acc = dot2(as_u32(__builtin_elementwise_fma(q1, s2, b2)), xp.y, acc);
+  acc = dot2(as_u32(__builtin_elementwise_fma(q2, s2, b2)), xp.z, acc);
+  acc = dot2(as_u32(__builtin_elementwise_fma(q3, s2, b2)), xp.w, acc);
+  return acc;
+}
+
+template <int R, int NIT>
+struct Block {
+  uint4 w[R][NIT];
+  uint32_t s[R][NIT], b[R][NIT];  // f16 bits in the low half (32-bit keeps them in VGPRs)
+};
+
+template <int L, int NIT, int R, bool EXACT>
+__global__ __launch_bounds__(kWG) void gemv1_kernel(const uint32_t* __restrict__ qw,
+                                                    const uint16_t* __restrict__ sc,
+                                                    const uint16_t* __restrict__ bi,
+                                                    const uint16_t* __restrict__ x,
+                                                    float* __restrict__ y, int N, int K,
+                                                    int nblocks) {
+  constexpr int TEAMS = kWG / L;
+  const int lane = threadIdx.x % L;
+  const int team = blockIdx.x * TEAMS + threadIdx.x / L;
+  const int T = gridDim.x * TEAMS;
+  const int C = K / 32;       // 16-byte chunks per row
+  const int G = K / kGroup;   // groups per row
+  const uint4* q4 = reinterpret_cast<const uint4*>(qw) + lane;
+  const uint16_t* sl = sc + (lane >> 1);
+  const uint16_t* bl = bi + (lane >> 1);
+
+  auto valid = [&](int j) { return EXACT || lane + j * L < C; };
+  auto load = [&](int blk, Block<R, NIT>& B) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int n = min(blk * R + r, N - 1);  // tail rows reload the last row, never stored
+      const uint4* p = q4 + (int64_t)n * C;
+      const uint16_t* ps = sl + (int64_t)n * G;
+      const uint16_t* pb = bl + (int64_t)n * G;
+#pragma unroll
+      for (int j = 0; j < NIT; ++j) {
+        if (valid(j)) {
+          B.w[r][j] = load_nt(p + j * L);
+          B.s[r][j] = ps[j * (L / 2)];
+          B.b[r][j] = pb[j * (L / 2)];
+        } else {
+          B.w[r][j] = make_uint4(0, 0, 0, 0);
+          B.s[r][j] = 0;
+          B.b[r][j] = 0;
+        }
+      }
+    }
+  };
+
+  Block<R, NIT> A, B;
+  int blk = team;
+  if (blk < nblocks) load(blk, A);
+
+  Consts k;
+  k.m_lo = __builtin_amdgcn_readfirstlane(0x000F000Fu);
+  k.m_hi = __builtin_amdgcn_readfirstlane(0x00F000F0u);
+  k.mag_lo = __builtin_amdgcn_readfirstlane(0x64006400u);
+  k.mag_hi = __builtin_amdgcn_readfirstlane(0x54005400u);
+
+  // this lane's slice of x, as pairs; zero past the end of the row
+  uint4 xv[NIT][4];
+#pragma unroll
+  for (int j = 0; j < NIT; ++j) {
+    const uint4* xp = reinterpret_cast<const uint4*>(x + (lane + j * L) * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xv[j][i] = valid(j) ? pair_up(xp[i]) : make_uint4(0, 0, 0, 0);
+  }
+
+  auto compute = [&](int blk, const Block<R, NIT>& B) {
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      // four independent accumulation chains (one per word of a chunk) for ILP
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+      for (int j = 0; j < NIT; ++j) {
+        const f16 sv = __builtin_bit_cast(f16, (uint16_t)B.s[r][j]);
+        const f16 bv = __builtin_bit_cast(f16, (uint16_t)B.b[r][j]);
+        const h2 s2 = {sv, sv}, b2 = {bv, bv};
+        a0 = word_fma(B.w[r][j].x, s2, b2, xv[j][0], a0, k);
+        a1 = word_fma(B.w[r][j].y, s2, b2, xv[j][1], a1, k);
+        a2 = word_fma(B.w[r][j].z, s2, b2, xv[j][2], a2, k);
+        a3 = word_fma(B.w[r][j].w, s2, b2, xv[j][3], a3, k);
+      }
+      float a = (a0 + a1) + (a2 + a3);
+#pragma unroll
+      for (int off = L / 2; off >= 1; off >>= 1) a += __shfl_xor(a, off, L);
+      acc[r] = a;
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (blk * R + r < N) y[blk * R + r] = acc[r];
+    }
+  };
+
+  while (blk < nblocks) {
+    const int b1 = blk + T;
+    if (b1 < nblocks) load(b1, B);
+    compute(blk, A);
+    if (b1 >= nblocks) break;
+    const int b2 = b1 + T;
+    if (b2 < nblocks) load(b2, A);
+    compute(b1, B);
+    blk = b2;
+  }
+}
+
+template <int L, int NIT, int R>
+void launch_m1(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
+               float* y, int N, int K, int max_wgs, hipStream_t st) {
+  constexpr int teams = kWG / L;
+  const int nblocks = (N + R - 1) / R;
+  int grid = (nblocks + teams - 1) / teams;
+  if (max_wgs > 0 && grid > max_wgs) grid = max_wgs;
+  if (L * NIT == K / 32)
+    hipLaunchKernelGGL((gemv1_kernel<L, NIT, R, true>), dim3(grid), dim3(kWG), 0, st, qw, s, b, x,
+                       y, N, K, nblocks);
+  else
+    hipLaunchKernelGGL((gemv1_kernel<L, NIT, R, false>), dim3(grid), dim3(kWG), 0, st, qw, s, b,
+                       x, y, N, K, nblocks);
+}
+
 template <int MT, int R, int P>
 void launch_t(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
               int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
@@ -230,10 +386,35 @@ void launch_p(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const ui
     launch_r<MT, 64>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
 }
 
+// M = 1 policy: lanes per row, chunk iterations and rows per block by K; the grid is
+// capped so every team walks several row blocks (see launch_m1).
+bool launch_gemv_m1(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
+                    float* y, int N, int K, hipStream_t st) {
+  const int C = K / 32;
+  const int cap = 0;
+  if (C <= 32) {
+    launch_m1<8, 4, 2>(qw, s, b, x, y, N, K, cap, st);
+  } else if (C <= 64) {
+    launch_m1<16, 4, 2>(qw, s, b, x, y, N, K, cap, st);
+  } else if (C <= 128) {
+    launch_m1<32, 4, 2>(qw, s, b, x, y, N, K, cap, st);
+  } else if (C <= 256) {
+    launch_m1<64, 4, 1>(qw, s, b, x, y, N, K, cap, st);
+  } else if (C <= 384) {
+    launch_m1<64, 6, 1>(qw, s, b, x, y, N, K, cap, st);
+  } else if (C <= 512) {
+    launch_m1<64, 8, 1>(qw, s, b, x, y, N, K, cap, st);
+  } else {
+    return false;
+  }
+  return true;
+}
+
 }  // namespace
 
 void launch_gemv(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
                  int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
+  if (M <= 1 && launch_gemv_m1(qw, s, b, x, y, N, K, st)) return;
   if (M <= 1)
     launch_p<1>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
   else if (M <= 2)

@@ -7,12 +7,19 @@
 //
 // Order: value descending, ties to the lower index, -0.0 equal to +0.0.  Each candidate is
 // a 64-bit key  (orderable(value) << 32) | ~index  whose unsigned order is exactly that
-// order, so selection is a plain descending sort of keys (deterministic, exact).
+// order (keys are unique), so selection is exact and deterministic.
 //
-// Two passes for long rows: pass 1 splits a row into chunks of `chunk` logits and keeps
-// each chunk's k best keys (bitonic sort in LDS); pass 2 sorts a row's chunk winners and
-// writes the k best.  Short rows (V <= 4096) take pass 2 straight from the logits.  The
-// output values are re-read from the logits at the chosen index, so -0.0 stays -0.0.
+// Block selection (block_topk): each of the 256 threads holds E keys in registers.  The
+// block sorts only the 256 per-thread maxima; T, the k-th largest of them, is a key that at
+// least k keys reach, so the block's k largest keys are all >= T.  Keys >= T are compacted
+// into LDS (their order there does not matter) and sorted; the first k are the answer.  On
+// random logits only a few k keys pass the threshold; in the worst case (all equal) all of
+// them do and the sort covers the whole block, with the same result.
+//
+// Long rows run in two passes: pass 1 selects each chunk's k best keys into the workspace,
+// pass 2 selects the row's k best among them.  Rows of at most 4096 logits take pass 2
+// straight from the logits.  Values are re-read from the logits at the chosen index, so
+// -0.0 stays -0.0.
 #include "w4_internal.h"
 
 namespace w4 {
@@ -20,7 +27,7 @@ namespace w4 {
 namespace {
 
 constexpr int kWG = 256;
-constexpr int kMaxSort = 8192;  // keys per LDS sort (64 KB)
+constexpr int kMaxCand = 8192;  // keys per row after pass 1
 
 __device__ __forceinline__ uint64_t make_key(float v, uint32_t i) {
   uint32_t u = __float_as_uint(v);
@@ -31,12 +38,12 @@ __device__ __forceinline__ uint64_t make_key(float v, uint32_t i) {
 
 __device__ __forceinline__ uint32_t key_index(uint64_t key) { return ~(uint32_t)key; }
 
-// Descending bitonic sort of n (power of two) keys in LDS by the whole workgroup.
+// Descending bitonic sort of n (a power of two, >= 2) keys in LDS by the whole workgroup.
 __device__ void sort_desc(uint64_t* s, int n) {
   for (int size = 2; size <= n; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       for (int i = threadIdx.x; i < (n >> 1); i += kWG) {
-        const int lo = 2 * stride * (i / stride) + (i % stride);
+        const int lo = ((i & ~(stride - 1)) << 1) | (i & (stride - 1));
         const int hi = lo + stride;
         const bool desc = (lo & size) == 0;
         const uint64_t a = s[lo], b = s[hi];
@@ -56,45 +63,80 @@ __host__ __device__ inline int pow2_ceil(int v) {
   return p;
 }
 
-// Pass 1: keys of logits[m][c*chunk : (c+1)*chunk) -> k best into cand[m][c][0:k].
+// The k (<= 256) largest of the block's keys (E per thread), sorted, into s[0..k).
+// s must hold max(256, 256 * E) keys; *cnt is an LDS counter.
+template <int E>
+__device__ void block_topk(const uint64_t (&key)[E], int k, uint64_t* s, int* cnt) {
+  const int tid = threadIdx.x;
+  uint64_t mx = key[0];
+#pragma unroll
+  for (int e = 1; e < E; ++e) mx = key[e] > mx ? key[e] : mx;
+  s[tid] = mx;
+  if (tid == 0) *cnt = 0;
+  __syncthreads();
+  sort_desc(s, kWG);
+  const uint64_t T = s[k - 1];
+  int mine = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) mine += key[e] >= T;
+  __syncthreads();  // every thread has read T before s is overwritten
+  int pos = atomicAdd(cnt, mine);
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (key[e] >= T) s[pos++] = key[e];
+  __syncthreads();
+  const int total = *cnt;
+  const int n = pow2_ceil(total < 2 ? 2 : total);
+  for (int i = total + tid; i < n; i += kWG) s[i] = 0ull;  // pads sort last
+  __syncthreads();
+  sort_desc(s, n);
+}
+
+// Pass 1: the k best keys of logits[m][c*chunk, (c+1)*chunk) into cand[m][c][0:k).
+template <int E>
 __global__ __launch_bounds__(kWG) void topk_chunk_kernel(const float* __restrict__ logits,
-                                                         int64_t ldl, int V, int k, int chunk,
+                                                         int64_t ldl, int V, int k,
                                                          uint64_t* __restrict__ cand) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint64_t* s = reinterpret_cast<uint64_t*>(smem);
+  __shared__ int cnt;
   const int c = blockIdx.x, m = blockIdx.y;
   const int nchunks = gridDim.x;
   const float* row = logits + (int64_t)m * ldl;
-  const int base = c * chunk;
-  for (int i = threadIdx.x; i < chunk; i += kWG) {
-    const int v = base + i;
-    s[i] = (v < V) ? make_key(row[v], (uint32_t)v) : 0ull;  // 0 sorts below every finite key
+  const int base = c * (E * kWG);
+  uint64_t key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int v = base + e * kWG + threadIdx.x;  // coalesced: one row segment per e
+    key[e] = v < V ? make_key(row[v], (uint32_t)v) : 0ull;  // 0 sorts below every key
   }
-  __syncthreads();
-  sort_desc(s, chunk);
+  block_topk<E>(key, k, s, &cnt);
   uint64_t* out = cand + ((int64_t)m * nchunks + c) * k;
   for (int i = threadIdx.x; i < k; i += kWG) out[i] = s[i];
 }
 
-// Pass 2: sort n candidate keys per row (from cand, or straight from the logits when
-// cand == nullptr) and write the k best indices and their logits.
+// Pass 2: the k best of a row's ncand keys (from cand, or the logits themselves when
+// cand == nullptr) -> indices and logits.
+template <int E>
 __global__ __launch_bounds__(kWG) void topk_final_kernel(const float* __restrict__ logits,
                                                          int64_t ldl, int V, int k,
                                                          const uint64_t* __restrict__ cand,
-                                                         int ncand, int npow2,
-                                                         int32_t* __restrict__ idx,
+                                                         int ncand, int32_t* __restrict__ idx,
                                                          float* __restrict__ val) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint64_t* s = reinterpret_cast<uint64_t*>(smem);
+  __shared__ int cnt;
   const int m = blockIdx.x;
   const float* row = logits + (int64_t)m * ldl;
-  for (int i = threadIdx.x; i < npow2; i += kWG) {
-    uint64_t key = 0ull;
-    if (i < ncand) key = cand ? cand[(int64_t)m * ncand + i] : make_key(row[i], (uint32_t)i);
-    s[i] = key;
+  uint64_t key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = e * kWG + threadIdx.x;
+    uint64_t kk = 0ull;
+    if (i < ncand) kk = cand ? cand[(int64_t)m * ncand + i] : make_key(row[i], (uint32_t)i);
+    key[e] = kk;
   }
-  __syncthreads();
-  sort_desc(s, npow2);
+  block_topk<E>(key, k, s, &cnt);
   for (int i = threadIdx.x; i < k; i += kWG) {
     uint32_t j = key_index(s[i]);
     if (j >= (uint32_t)V) j = (uint32_t)V - 1;  // unreachable for k <= V; keeps reads in bounds
@@ -103,14 +145,36 @@ __global__ __launch_bounds__(kWG) void topk_final_kernel(const float* __restrict
   }
 }
 
+template <int E>
+void launch_final(const float* logits, int64_t ldl, int M, int V, int k, const uint64_t* cand,
+                  int ncand, int32_t* idx, float* val, hipStream_t st) {
+  hipLaunchKernelGGL((topk_final_kernel<E>), dim3(M), dim3(kWG), (size_t)E * kWG * 8, st, logits,
+                     ldl, V, k, cand, ncand, idx, val);
+}
+
+void final_pass(const float* logits, int64_t ldl, int M, int V, int k, const uint64_t* cand,
+                int ncand, int32_t* idx, float* val, hipStream_t st) {
+  if (ncand <= kWG)
+    launch_final<1>(logits, ldl, M, V, k, cand, ncand, idx, val, st);
+  else if (ncand <= 4 * kWG)
+    launch_final<4>(logits, ldl, M, V, k, cand, ncand, idx, val, st);
+  else if (ncand <= 8 * kWG)
+    launch_final<8>(logits, ldl, M, V, k, cand, ncand, idx, val, st);
+  else if (ncand <= 16 * kWG)
+    launch_final<16>(logits, ldl, M, V, k, cand, ncand, idx, val, st);
+  else
+    launch_final<32>(logits, ldl, M, V, k, cand, ncand, idx, val, st);
+}
+
 }  // namespace
 
+// Chunk (logits per pass-1 block) for a row of V logits: 4096, or 8192 when 4096-chunks
+// would leave more than kMaxCand candidates; 0 when even that is too many.
 int topk_chunk(int64_t V, int k) {
   if (V <= 4096) return (int)pow2_ceil((int)V);  // single pass
-  int chunk = 4096;
-  while (((V + chunk - 1) / chunk) * k > kMaxSort && chunk < kMaxSort) chunk <<= 1;
-  if (((V + chunk - 1) / chunk) * k > kMaxSort) return 0;
-  return chunk;
+  for (int chunk = 4096; chunk <= 8192; chunk <<= 1)
+    if (((V + chunk - 1) / chunk) * k <= kMaxCand) return chunk;
+  return 0;
 }
 
 size_t topk_ws_bytes(int64_t M, int64_t V, int k) {
@@ -123,20 +187,19 @@ size_t topk_ws_bytes(int64_t M, int64_t V, int k) {
 void launch_topk(const float* logits, int64_t ldl, int M, int V, int k, int32_t* idx, float* val,
                  void* ws, hipStream_t st) {
   if (V <= 4096) {
-    const int np = pow2_ceil(V < 2 ? 2 : V);
-    hipLaunchKernelGGL(topk_final_kernel, dim3(M), dim3(kWG), (size_t)np * 8, st, logits, ldl, V,
-                       k, (const uint64_t*)nullptr, V, np, idx, val);
+    final_pass(logits, ldl, M, V, k, nullptr, V, idx, val, st);
     return;
   }
   const int chunk = topk_chunk(V, k);
   const int nchunks = (V + chunk - 1) / chunk;
   uint64_t* cand = reinterpret_cast<uint64_t*>(ws);
-  hipLaunchKernelGGL(topk_chunk_kernel, dim3(nchunks, M), dim3(kWG), (size_t)chunk * 8, st,
-                     logits, ldl, V, k, chunk, cand);
-  const int ncand = nchunks * k;
-  const int np = pow2_ceil(ncand < 2 ? 2 : ncand);
-  hipLaunchKernelGGL(topk_final_kernel, dim3(M), dim3(kWG), (size_t)np * 8, st, logits, ldl, V, k,
-                     (const uint64_t*)cand, ncand, np, idx, val);
+  if (chunk == 4096)
+    hipLaunchKernelGGL((topk_chunk_kernel<16>), dim3(nchunks, M), dim3(kWG), (size_t)chunk * 8, st,
+                       logits, ldl, V, k, cand);
+  else
+    hipLaunchKernelGGL((topk_chunk_kernel<32>), dim3(nchunks, M), dim3(kWG), (size_t)chunk * 8, st,
+                       logits, ldl, V, k, cand);
+  final_pass(logits, ldl, M, V, k, cand, nchunks * k, idx, val, st);
 }
 
 }  // namespace w4

@@ -37,8 +37,10 @@ void launch_dequant_t(const uint32_t* qw, const uint16_t* s, const uint16_t* b, 
 enum GemmPath { kGemmMfma = 0, kGemmSmallM = 1, kGemmPlain = 2 };
 GemmPath gemm_path(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M,
                    int64_t N, int64_t K);
+size_t gemm_ws_bytes(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M,
+                     int64_t N, int64_t K);
 void launch_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C,
-                 int64_t ldc, int M, int N, int K, hipStream_t st);
+                 int64_t ldc, int M, int N, int K, void* ws, hipStream_t st);
 
 // Top-k: chunk size (in logits) used for rows longer than one block, and workspace bytes.
 int topk_chunk(int64_t V, int k);        // 0 when the shape is unsupported
