@@ -125,6 +125,8 @@ class Workload:
             self.prefill.append((name, qw, torch.from_numpy(s).to(dev), torch.from_numpy(b).to(dev), wt,
                                  torch.from_numpy(a_in[k]).to(dev), c, (self.M, n, k), (q, s, b, a_in[k])))
         self.prefill_flops = sum(2 * m * n * k for *_, (m, n, k), _ in self.prefill)
+        ws = max(w4.gemm_workspace_bytes(a, wt) for _, _, _, _, wt, a, _, _, _ in self.prefill)
+        self.gemm_ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
         log(f"prefill weights ready in {time.time() - t0:.1f}s ({self.prefill_flops / 1e9:.2f} GFLOP per step)")
 
@@ -142,7 +144,7 @@ class Workload:
     def run_prefill(self):
         for _, qw, s, b, wt, a, c, _, _ in self.prefill:
             self.w4.w4_dequant_f16_t(qw, s, b, out=wt)
-            self.w4.gemm_f16(a, wt, out=c)
+            self.w4.gemm_f16(a, wt, out=c, workspace=self.gemm_ws)
 
 
 def capture(torch, fn):
@@ -159,48 +161,46 @@ def capture(torch, fn):
     return g
 
 
-def kernel_timings(torch, wl, reps=3):
-    """Per-launch HIP-event durations of every decode GEMV shape and of the prefill GEMMs and
-    dequants (eager launches on the current stream, each bracketed by its own events)."""
-    stream = torch.cuda.current_stream()
-    rec = {}
+def kernel_timings(torch, wl, reps=5):
+    """Per-launch device time of each kernel shape of the step.  The launches of one shape
+    (e.g. the 36 layers' gate|up GEMVs, each on its own weights) are captured in a HIP graph
+    of their own and replayed between two events; time / launches is the average launch
+    duration including the in-graph dispatch gap (a conservative figure)."""
+    groups = {}
 
-    def timed(key, nbytes, flops, fn):
+    def add(key, nbytes, flops, fn):
+        g = groups.setdefault(key, {"bytes": nbytes, "flops": flops, "fns": []})
+        g["fns"].append(fn)
+
+    for mats in wl.layers:
+        for name, qw, s, b, x, y, (m, n, k) in mats:
+            add(("w4_gemv", m, n, k), gemv_bytes(m, n, k), 0,
+                lambda qw=qw, s=s, b=b, x=x, y=y: wl.w4.w4_gemv(qw, s, b, x, out=y))
+    for name, qw, s, b, wt, a, c, (m, n, k), _ in wl.prefill:
+        add(("w4_dequant_f16_t", 0, n, k), n * k // 2 + n * k // 16 + 2 * n * k, 0,
+            lambda qw=qw, s=s, b=b, wt=wt: wl.w4.w4_dequant_f16_t(qw, s, b, out=wt))
+        add(("gemm_f16", m, n, k), 2 * (m * k + k * n) + 4 * m * n, 2 * m * n * k,
+            lambda a=a, wt=wt, c=c: wl.w4.gemm_f16(a, wt, out=c, workspace=wl.gemm_ws))
+    add(("gemm_f16", 1, wl.V, wl.H), 2 * wl.H * wl.V + 2 * wl.H + 4 * wl.V, 2 * wl.H * wl.V,
+        lambda: wl.w4.gemm_f16(wl.x_head, wl.head, out=wl.logits))
+    add(("logits_argmax_topk", 1, wl.V, TOPK), 4 * wl.V, 0,
+        lambda: wl.w4.logits_argmax_topk(wl.logits, TOPK, idx=wl.idx, val=wl.val, workspace=wl.topk_ws))
+
+    stream = torch.cuda.current_stream()
+    out = {}
+    for key, g in groups.items():
+        fns = g["fns"]
+        graph = capture(torch, lambda fns=fns: [f() for f in fns])
+        graph.replay()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        fn()
+        for _ in range(reps):
+            graph.replay()
         e1.record(stream)
-        rec.setdefault(key, []).append((e0, e1, nbytes, flops))
-
-    # Give the CPU a head start (a device-side sleep) so every launch and its events are
-    # queued before the GPU reaches them: the events then bracket back-to-back kernels.
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    torch.cuda._sleep(1_000_000)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    cycles_per_ms = 1_000_000 / max(e0.elapsed_time(e1), 1e-3)
-    for _ in range(reps):
-        torch.cuda._sleep(int(cycles_per_ms * 30))
-        for mats in wl.layers:
-            for name, qw, s, b, x, y, (m, n, k) in mats:
-                timed(("w4_gemv", m, n, k), gemv_bytes(m, n, k), 0,
-                      lambda qw=qw, s=s, b=b, x=x, y=y: wl.w4.w4_gemv(qw, s, b, x, out=y))
-        for name, qw, s, b, wt, a, c, (m, n, k), _ in wl.prefill:
-            timed(("w4_dequant_f16_t", 0, n, k), n * k // 2 + n * k // 16 + 2 * n * k, 0,
-                  lambda qw=qw, s=s, b=b, wt=wt: wl.w4.w4_dequant_f16_t(qw, s, b, out=wt))
-            timed(("gemm_f16", m, n, k), 2 * (m * k + k * n) + 4 * m * n, 2 * m * n * k,
-                  lambda a=a, wt=wt, c=c: wl.w4.gemm_f16(a, wt, out=c))
-        timed(("gemm_f16", 1, wl.V, wl.H), 2 * wl.H * wl.V + 2 * wl.H + 4 * wl.V, 2 * wl.H * wl.V,
-              lambda: wl.w4.gemm_f16(wl.x_head, wl.head, out=wl.logits))
         torch.cuda.synchronize()
-    out = {}
-    for key, lst in rec.items():
-        us = [e0.elapsed_time(e1) * 1e3 for e0, e1, _, _ in lst]
-        nb, fl = lst[0][2], lst[0][3]
-        avg = sum(us) / len(us)
-        out[key] = {"launches": len(us), "avg_us": avg, "bytes": nb, "flops": fl,
-                    "gbps": nb / avg / 1e3, "tflops": fl / avg / 1e6 if fl else 0.0}
+        avg = e0.elapsed_time(e1) * 1e3 / (reps * len(fns))
+        out[key] = {"launches": reps * len(fns), "avg_us": avg, "bytes": g["bytes"], "flops": g["flops"],
+                    "gbps": g["bytes"] / avg / 1e3, "tflops": g["flops"] / avg / 1e6 if g["flops"] else 0.0}
     return out
 
 

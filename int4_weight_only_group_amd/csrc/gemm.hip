@@ -186,6 +186,164 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs g) {
     }
 }
 
+// ------------------------------------------------------------- MFMA path, LDS DMA
+// Same 256 x 256 tile and 4 x (128 x 128) wave split as above, but both operands travel
+// HBM -> LDS with gfx950's 16-byte LDS DMA (global_load_lds_dwordx4: lane l's 16 bytes land
+// at the instruction's LDS base + 16 l), so no registers hold tiles in flight.  Four LDS
+// stages of BK = 32 (32 KB each) keep three K-tiles in flight while the matrix cores work on
+// the fourth.  B stays [k][n] in LDS and its MFMA operand (8 consecutive k of one column per
+// lane) is read with two ds_read_b64_tr_b16: within each 16-lane group, result lane i gets
+// element i mod 4 of source lanes 4e + i / 4 (e = 0..3), so source lane L pointing at
+// B[k0 + L / 4][n0 + 4 (L mod 4)] hands lane i the column B[k0 .. k0 + 3][n0 + i].
+// The 16-byte chunks are XOR-swizzled in LDS (A: chunk ^ (row / 2 mod 4) within a 64-byte
+// row; B: chunk ^ (k mod 8) within a 512-byte row) so the operand reads do not pile onto the
+// same banks.  Waits are explicit (vmcnt for this wave's DMA, then a plain s_barrier): a
+// __syncthreads() would drain every K-tile in flight.  Requires K % 32 == 0 (split-K slices
+// are multiples of 32); other K take the register-staged kernel above.
+constexpr int DBK = 32;
+constexpr int DSTAGES = 4;
+constexpr int DSTAGE_BYTES = (BM + BN) * DBK * 2;      // 32 KB
+constexpr size_t kDmaLds = (size_t)DSTAGES * DSTAGE_BYTES;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// One 16-byte-per-lane LDS DMA (lds: wave-uniform LDS byte address of the 1 KB destination).
+// Issued as inline asm: through the builtin, the compiler would protect every later LDS read
+// with a wait for all DMA in flight, which serializes the K-tile pipeline; the kernel waits
+// explicitly instead (W4_SYNC).
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
+               "s"(lds)
+               : "memory", "m0");
+}
+
+// wait for this wave's DMA down to n outstanding instructions and for all of its LDS reads
+// (a stage may be refilled right after the barrier), then barrier
+#define W4_SYNC(n) asm volatile("s_waitcnt vmcnt(" #n ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
+
+__global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs g) {
+  extern __shared__ __align__(16) unsigned char dlds[];
+  int tm, tn, split;
+  tile_of(g, blockIdx.x, tm, tn, split);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kbeg = split * g.kslice;
+  const int kend = min(g.K, kbeg + g.kslice);
+  const int nk = (kend - kbeg) / DBK;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // DMA source addresses (this lane, K-tile 0): wave w issues A and B instructions 4w..4w+3
+  const uint16_t* a_src[4];
+  const uint16_t* b_src[4];
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) {
+    const int i = wave * 4 + ii;
+    const int row = 16 * i + (lane >> 2);
+    const int ca = (lane & 3) ^ ((row >> 1) & 3);
+    a_src[ii] = g.A + (int64_t)min(m0 + row, g.M - 1) * g.lda + kbeg + ca * 8;
+    const int krow = 2 * i + (lane >> 5);
+    const int cb = (lane & 31) ^ (krow & 7);
+    b_src[ii] = g.B + (int64_t)(kbeg + krow) * g.ldb + min(n0 + cb * 8, g.N - 8);
+  }
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t*)dlds;
+  auto issue = [&](int t) {
+    const uint32_t st = lds_base + (uint32_t)((t % DSTAGES) * DSTAGE_BYTES);
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+      dma16(a_src[ii] + t * DBK, st + (uint32_t)((wave * 4 + ii) * 1024));
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+      dma16(b_src[ii] + (int64_t)t * DBK * g.ldb,
+            st + (uint32_t)(BM * DBK * 2 + (wave * 4 + ii) * 1024));
+  };
+
+  // per-lane LDS read offsets (bytes within a stage)
+  int a_off[4][2];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int r = wm * 128 + mi * 32 + (lane & 31);
+      const int c = 2 * ks + (lane >> 5);
+      a_off[mi][ks] = r * 64 + ((c ^ ((r >> 1) & 3)) * 16);
+    }
+  int b_off[4][2][2];
+  {
+    const int grp = lane >> 4, L = lane & 15;
+#pragma unroll
+    for (int nj = 0; nj < 4; ++nj)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int krow = 16 * ks + 8 * (grp >> 1) + 4 * h + (L >> 2);
+          const int ncol = wn * 128 + nj * 32 + (grp & 1) * 16 + 4 * (L & 3);
+          const int c = ncol >> 3;
+          b_off[nj][ks][h] = BM * DBK * 2 + krow * 512 + ((c ^ (krow & 7)) * 16) + (L & 1) * 8;
+        }
+  }
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  for (int t = 0; t < 3 && t < nk; ++t) issue(t);
+  for (int t = 0; t < nk; ++t) {
+    // this wave's DMA for tile t is done once at most the later tiles' 8 instructions each
+    // are outstanding; the barrier then covers every wave's part of tile t and guarantees
+    // that every wave has finished computing tile t - 1 (whose stage is refilled next).
+    const int later = min(2, nk - 1 - t);
+    if (later == 2)
+      W4_SYNC(16);
+    else if (later == 1)
+      W4_SYNC(8);
+    else
+      W4_SYNC(0);
+    if (t + 3 < nk) issue(t + 3);
+    const unsigned char* st = dlds + (t % DSTAGES) * DSTAGE_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      f16x8 a[4], b[4];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) a[mi] = *reinterpret_cast<const f16x8*>(st + a_off[mi][ks]);
+#pragma unroll
+      for (int nj = 0; nj < 4; ++nj) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(st + b_off[nj][ks][0]));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(st + b_off[nj][ks][1]));
+        const short v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        b[nj] = __builtin_bit_cast(f16x8, v);
+      }
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < 4; ++nj)
+          acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mi], b[nj], acc[mi][nj], 0, 0, 0);
+    }
+  }
+
+  float* out = g.ksplit == 1 ? g.C : g.ws + (int64_t)split * g.M * g.N;
+  const int64_t ldo = g.ksplit == 1 ? g.ldc : g.N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn * 128 + j * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (row < g.M && col < g.N) out[(int64_t)row * ldo + col] = acc[i][j][r];
+      }
+    }
+}
+
 // C[m][n] = sum over s (in order) of ws[s][m][n]
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws,
                                                             float* __restrict__ C, int64_t ldc,
@@ -349,13 +507,18 @@ void launch_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
       static std::once_flag lds_attr;
       std::call_once(lds_attr, [] {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_mfma_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_dma_kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDmaLds);
       });
       const GemmPlan p = plan_mfma(M, N, K);
       GemmArgs g{A, B, C, reinterpret_cast<float*>(ws), lda, ldb, ldc, M, N, K,
                  p.tilesM, p.tilesN, p.ksplit, p.kslice};
-      hipLaunchKernelGGL(gemm_mfma_kernel, dim3((unsigned)(p.tilesM * p.tilesN * p.ksplit)),
-                         dim3(256), kGemmLds, st, g);
+      const dim3 grid((unsigned)(p.tilesM * p.tilesN * p.ksplit));
+      if (K % DBK == 0)
+        hipLaunchKernelGGL(gemm_dma_kernel, grid, dim3(256), kDmaLds, st, g);
+      else
+        hipLaunchKernelGGL(gemm_mfma_kernel, grid, dim3(256), kGemmLds, st, g);
       if (p.ksplit > 1) {
         const int64_t MN = (int64_t)M * N;
         int64_t blocks = (MN + 255) / 256;

@@ -233,13 +233,16 @@ struct Block {
   uint32_t s[R][NIT], b[R][NIT];  // f16 bits in the low half (32-bit keeps them in VGPRs)
 };
 
-template <int L, int NIT, int R, bool EXACT>
+// XL: x is staged once per workgroup in LDS (pairs, K * 2 bytes) and read per chunk instead
+// of being held in 16 * NIT registers per lane; fewer registers allow more waves.
+template <int L, int NIT, int R, bool EXACT, bool XL>
 __global__ __launch_bounds__(kWG) void gemv1_kernel(const uint32_t* __restrict__ qw,
                                                     const uint16_t* __restrict__ sc,
                                                     const uint16_t* __restrict__ bi,
                                                     const uint16_t* __restrict__ x,
                                                     float* __restrict__ y, int N, int K,
                                                     int nblocks) {
+  extern __shared__ __align__(16) unsigned char smem[];
   constexpr int TEAMS = kWG / L;
   const int lane = threadIdx.x % L;
   const int team = blockIdx.x * TEAMS + threadIdx.x / L;
@@ -250,8 +253,13 @@ __global__ __launch_bounds__(kWG) void gemv1_kernel(const uint32_t* __restrict__
   const uint16_t* sl = sc + (lane >> 1);
   const uint16_t* bl = bi + (lane >> 1);
 
+  // Every load is unconditional (block and chunk indices are clamped to valid addresses, a
+  // chunk past the end of the row is zeroed after the load): with no branch around a load,
+  // the compiler's wait counts stay exact and the next block's loads are never waited for
+  // while the current block is being computed.
   auto valid = [&](int j) { return EXACT || lane + j * L < C; };
   auto load = [&](int blk, Block<R, NIT>& B) {
+    blk = min(blk, nblocks - 1);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int n = min(blk * R + r, N - 1);  // tail rows reload the last row, never stored
@@ -260,12 +268,12 @@ __global__ __launch_bounds__(kWG) void gemv1_kernel(const uint32_t* __restrict__
       const uint16_t* pb = bl + (int64_t)n * G;
 #pragma unroll
       for (int j = 0; j < NIT; ++j) {
-        if (valid(j)) {
-          B.w[r][j] = load_nt(p + j * L);
-          B.s[r][j] = ps[j * (L / 2)];
-          B.b[r][j] = pb[j * (L / 2)];
-        } else {
-          B.w[r][j] = make_uint4(0, 0, 0, 0);
+        const int jc = valid(j) ? j * L : (C - 1 - lane);  // in-row chunk for this lane
+        B.w[r][j] = load_nt(p + jc);
+        B.s[r][j] = ps[jc >> 1];
+        B.b[r][j] = pb[jc >> 1];
+        if (!valid(j)) {
+          B.w[r][j] = make_uint4(0, 0, 0, 0);  // weight = fma(0, 0, 0) = 0
           B.s[r][j] = 0;
           B.b[r][j] = 0;
         }
@@ -275,7 +283,15 @@ __global__ __launch_bounds__(kWG) void gemv1_kernel(const uint32_t* __restrict__
 
   Block<R, NIT> A, B;
   int blk = team;
-  if (blk < nblocks) load(blk, A);
+  load(blk, A);
+  __builtin_amdgcn_sched_barrier(0);
+  uint4* xs = reinterpret_cast<uint4*>(smem);
+  if constexpr (XL) {
+    for (int i = threadIdx.x; i < C * 4; i += kWG)
+      xs[i] = pair_up(*reinterpret_cast<const uint4*>(x + i * 8));
+    __syncthreads();
+  }
+  if (team >= nblocks) return;
 
   Consts k;
   k.m_lo = __builtin_amdgcn_readfirstlane(0x000F000Fu);
@@ -284,31 +300,52 @@ __global__ __launch_bounds__(kWG) void gemv1_kernel(const uint32_t* __restrict__
   k.mag_hi = __builtin_amdgcn_readfirstlane(0x54005400u);
 
   // this lane's slice of x, as pairs; zero past the end of the row
-  uint4 xv[NIT][4];
+  uint4 xv[XL ? 1 : NIT][4];
 #pragma unroll
-  for (int j = 0; j < NIT; ++j) {
-    const uint4* xp = reinterpret_cast<const uint4*>(x + (lane + j * L) * 32);
+  for (int j = 0; j < (XL ? 0 : NIT); ++j) {
+    const int c = valid(j) ? lane + j * L : C - 1;
+    const uint4* xp = reinterpret_cast<const uint4*>(x + c * 32);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xv[j][i] = valid(j) ? pair_up(xp[i]) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      xv[j][i] = pair_up(xp[i]);
+      if (!valid(j)) xv[j][i] = make_uint4(0, 0, 0, 0);
+    }
   }
 
   auto compute = [&](int blk, const Block<R, NIT>& B) {
     float acc[R];
+    float a0[R], a1[R], a2[R], a3[R];  // four independent chains per row (ILP)
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      // four independent accumulation chains (one per word of a chunk) for ILP
-      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int r = 0; r < R; ++r) a0[r] = a1[r] = a2[r] = a3[r] = 0.f;
 #pragma unroll
-      for (int j = 0; j < NIT; ++j) {
+    for (int j = 0; j < NIT; ++j) {
+      uint4 x0, x1, x2, x3;
+      if constexpr (XL) {
+        const int c = valid(j) ? lane + j * L : C - 1;  // invalid chunks have zero weights
+        x0 = xs[c * 4 + 0];
+        x1 = xs[c * 4 + 1];
+        x2 = xs[c * 4 + 2];
+        x3 = xs[c * 4 + 3];
+      } else {
+        x0 = xv[j][0];
+        x1 = xv[j][1];
+        x2 = xv[j][2];
+        x3 = xv[j][3];
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
         const f16 sv = __builtin_bit_cast(f16, (uint16_t)B.s[r][j]);
         const f16 bv = __builtin_bit_cast(f16, (uint16_t)B.b[r][j]);
         const h2 s2 = {sv, sv}, b2 = {bv, bv};
-        a0 = word_fma(B.w[r][j].x, s2, b2, xv[j][0], a0, k);
-        a1 = word_fma(B.w[r][j].y, s2, b2, xv[j][1], a1, k);
-        a2 = word_fma(B.w[r][j].z, s2, b2, xv[j][2], a2, k);
-        a3 = word_fma(B.w[r][j].w, s2, b2, xv[j][3], a3, k);
+        a0[r] = word_fma(B.w[r][j].x, s2, b2, x0, a0[r], k);
+        a1[r] = word_fma(B.w[r][j].y, s2, b2, x1, a1[r], k);
+        a2[r] = word_fma(B.w[r][j].z, s2, b2, x2, a2[r], k);
+        a3[r] = word_fma(B.w[r][j].w, s2, b2, x3, a3[r], k);
       }
-      float a = (a0 + a1) + (a2 + a3);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float a = (a0[r] + a1[r]) + (a2[r] + a3[r]);
 #pragma unroll
       for (int off = L / 2; off >= 1; off >>= 1) a += __shfl_xor(a, off, L);
       acc[r] = a;
@@ -320,31 +357,48 @@ __global__ __launch_bounds__(kWG) void gemv1_kernel(const uint32_t* __restrict__
     }
   };
 
-  while (blk < nblocks) {
-    const int b1 = blk + T;
-    if (b1 < nblocks) load(b1, B);
-    compute(blk, A);
-    if (b1 >= nblocks) break;
-    const int b2 = b1 + T;
-    if (b2 < nblocks) load(b2, A);
-    compute(b1, B);
-    blk = b2;
+  // Every team walks `per` blocks (team, team + T, ...; the same count for all teams, the
+  // surplus past nblocks is computed on clamped loads and never stored).  The steady-state
+  // loop and the peeled tail contain only unconditional loads, so wait counts are exact on
+  // every path; sched_barrier keeps the scheduler from sinking a prefetch below the math of
+  // the block before it.
+  const int per = (nblocks + T - 1) / T;
+  int i = 0;
+  for (; i + 2 < per; i += 2) {
+    load(blk + (i + 1) * T, B);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(blk + i * T, A);
+    load(blk + (i + 2) * T, A);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(blk + (i + 1) * T, B);
+  }
+  if (per - i == 2) {
+    load(blk + (i + 1) * T, B);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(blk + i * T, A);
+    compute(blk + (i + 1) * T, B);
+  } else {
+    compute(blk + i * T, A);
   }
 }
 
-template <int L, int NIT, int R>
+// per: blocks each team walks; the grid is sized so that teams * per just covers the blocks
+// (no team is left with a surplus block to load and discard).
+template <int L, int NIT, int R, bool XL>
 void launch_m1(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
-               float* y, int N, int K, int max_wgs, hipStream_t st) {
+               float* y, int N, int K, int per, hipStream_t st) {
   constexpr int teams = kWG / L;
   const int nblocks = (N + R - 1) / R;
-  int grid = (nblocks + teams - 1) / teams;
-  if (max_wgs > 0 && grid > max_wgs) grid = max_wgs;
+  if (per < 1) per = 1;
+  const int T = (nblocks + per - 1) / per;
+  const int grid = (T + teams - 1) / teams;
+  const size_t lds = XL ? (size_t)K * 2 : 0;
   if (L * NIT == K / 32)
-    hipLaunchKernelGGL((gemv1_kernel<L, NIT, R, true>), dim3(grid), dim3(kWG), 0, st, qw, s, b, x,
-                       y, N, K, nblocks);
+    hipLaunchKernelGGL((gemv1_kernel<L, NIT, R, true, XL>), dim3(grid), dim3(kWG), lds, st, qw, s,
+                       b, x, y, N, K, nblocks);
   else
-    hipLaunchKernelGGL((gemv1_kernel<L, NIT, R, false>), dim3(grid), dim3(kWG), 0, st, qw, s, b,
-                       x, y, N, K, nblocks);
+    hipLaunchKernelGGL((gemv1_kernel<L, NIT, R, false, XL>), dim3(grid), dim3(kWG), lds, st, qw,
+                       s, b, x, y, N, K, nblocks);
 }
 
 template <int MT, int R, int P>
@@ -388,22 +442,29 @@ void launch_p(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const ui
 
 // M = 1 policy: lanes per row, chunk iterations and rows per block by K; the grid is
 // capped so every team walks several row blocks (see launch_m1).
+// Per-shape choice measured on MI355X (back-to-back launches on distinct weights): short
+// rows use one-shot teams holding x in registers; long rows (K >= 3840) read x from LDS and
+// big matrices give each team several row blocks.
 bool launch_gemv_m1(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
                     float* y, int N, int K, hipStream_t st) {
   const int C = K / 32;
-  const int cap = 0;
   if (C <= 32) {
-    launch_m1<8, 4, 2>(qw, s, b, x, y, N, K, cap, st);
+    launch_m1<32, 1, 1, true>(qw, s, b, x, y, N, K, 1, st);
   } else if (C <= 64) {
-    launch_m1<16, 4, 2>(qw, s, b, x, y, N, K, cap, st);
+    if (N >= 8192)
+      launch_m1<64, 1, 4, false>(qw, s, b, x, y, N, K, 1, st);
+    else if (N > 2048 || N <= 1024)
+      launch_m1<64, 1, 1, false>(qw, s, b, x, y, N, K, 1, st);
+    else
+      launch_m1<64, 1, 2, false>(qw, s, b, x, y, N, K, 1, st);
   } else if (C <= 128) {
-    launch_m1<32, 4, 2>(qw, s, b, x, y, N, K, cap, st);
+    launch_m1<64, 2, 1, true>(qw, s, b, x, y, N, K, N >= 16384 ? 6 : 1, st);
   } else if (C <= 256) {
-    launch_m1<64, 4, 1>(qw, s, b, x, y, N, K, cap, st);
+    launch_m1<64, 4, 1, true>(qw, s, b, x, y, N, K, 1, st);
   } else if (C <= 384) {
-    launch_m1<64, 6, 1>(qw, s, b, x, y, N, K, cap, st);
+    launch_m1<64, 6, 1, true>(qw, s, b, x, y, N, K, 1, st);
   } else if (C <= 512) {
-    launch_m1<64, 8, 1>(qw, s, b, x, y, N, K, cap, st);
+    launch_m1<64, 8, 1, true>(qw, s, b, x, y, N, K, 2, st);
   } else {
     return false;
   }

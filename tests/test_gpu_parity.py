@@ -244,7 +244,7 @@ def gemm_case(w4, m, n, k, seed, lda_pad=0, ldb_pad=0, ldc_pad=0, a=None, bmat=N
 
 @pytest.mark.parametrize("m,n,k", [
     (9, 8, 8), (33, 264, 72), (130, 520, 200), (257, 1000, 2056), (128, 256, 32), (1570, 264, 64),
-    (300, 2048, 1000), (17, 8, 4096),
+    (300, 2048, 1000), (17, 8, 4096), (300, 1000, 2048), (513, 520, 96), (40, 2056, 32),
 ])
 def test_gemm_mfma_path(w4, m, n, k):
     gemm_case(w4, m, n, k, seed=m + n + k)
