@@ -47,6 +47,13 @@ def parse_args():
     p.add_argument("--unfused", action="store_true", help="run q,k,v and gate,up as separate GEMVs (7 per layer)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-check", action="store_true", help="skip the parity re-check of the timed outputs")
+    p.add_argument("--counters", metavar="MANIFEST",
+                   help="counter-collection pass: launch each kernel shape of the step 3 times (eagerly, between "
+                        "marker kernels) plus a copy of known size, write the launch plan to MANIFEST and exit; "
+                        "run under rocprofv3 --pmc")
+    p.add_argument("--traffic-from", nargs=3, metavar=("MANIFEST", "FETCH_CSV", "WRITE_CSV"),
+                   help="(no GPU) turn the FETCH_SIZE and WRITE_SIZE counter CSVs of two --counters passes into "
+                        "profiles/traffic.json and print a table of them")
     return p.parse_args()
 
 
@@ -161,11 +168,10 @@ def capture(torch, fn):
     return g
 
 
-def kernel_timings(torch, wl, reps=5):
-    """Per-launch device time of each kernel shape of the step.  The launches of one shape
-    (e.g. the 36 layers' gate|up GEMVs, each on its own weights) are captured in a HIP graph
-    of their own and replayed between two events; time / launches is the average launch
-    duration including the in-graph dispatch gap (a conservative figure)."""
+def kernel_groups(wl):
+    """The step's launches grouped by kernel shape: key -> algorithmic bytes and flops of one
+    launch, and one closure per launch (e.g. the 36 layers' gate|up GEMVs, each on its own
+    weights)."""
     groups = {}
 
     def add(key, nbytes, flops, fn):
@@ -185,7 +191,15 @@ def kernel_timings(torch, wl, reps=5):
         lambda: wl.w4.gemm_f16(wl.x_head, wl.head, out=wl.logits))
     add(("logits_argmax_topk", 1, wl.V, TOPK), 4 * wl.V, 0,
         lambda: wl.w4.logits_argmax_topk(wl.logits, TOPK, idx=wl.idx, val=wl.val, workspace=wl.topk_ws))
+    return groups
 
+
+def kernel_timings(torch, wl, reps=5):
+    """Per-launch device time of each kernel shape of the step.  The launches of one shape
+    are captured in a HIP graph of their own and replayed between two events; time /
+    launches is the average launch duration including the in-graph dispatch gap (a
+    conservative figure)."""
+    groups = kernel_groups(wl)
     stream = torch.cuda.current_stream()
     out = {}
     for key, g in groups.items():
@@ -202,6 +216,110 @@ def kernel_timings(torch, wl, reps=5):
         out[key] = {"launches": reps * len(fns), "avg_us": avg, "bytes": g["bytes"], "flops": g["flops"],
                     "gbps": g["bytes"] / avg / 1e3, "tflops": g["flops"] / avg / 1e6 if g["flops"] else 0.0}
     return out
+
+
+SOURCE_OF = {"w4_gemv": "gemv.hip", "w4_dequant_f16_t": "dequant.hip", "gemm_f16": "gemm.hip",
+             "logits_argmax_topk": "topk.hip"}
+COUNTER_REPS = 3
+COPY_ELEMS = 128 << 20  # f16 elements of the calibration copy (256 MiB read, 256 MiB written)
+
+
+def counters_pass(torch, wl, manifest_path):
+    """Launch plan for the counter runs: a marker kernel (an int16 fill, a kernel nothing
+    else here launches), then a copy of known size COUNTER_REPS times, then for each kernel
+    shape COUNTER_REPS launches on different weights, each group followed by a marker.
+    The plan and the algorithmic bytes of each group go to manifest_path."""
+    marker = torch.empty(4097, dtype=torch.int16, device="cuda")
+    src = torch.ones(COPY_ELEMS, dtype=torch.float16, device="cuda")
+    dst = torch.empty_like(src)
+    plan = [{"key": "copy", "read_bytes": 2 * COPY_ELEMS, "write_bytes": 2 * COPY_ELEMS, "source": None}]
+    torch.cuda.synchronize()
+    marker.fill_(1)
+    for _ in range(COUNTER_REPS):
+        torch.neg(src, out=dst)
+    marker.fill_(1)
+    for key, g in kernel_groups(wl).items():
+        fns = g["fns"]
+        for r in range(COUNTER_REPS):
+            fns[r % len(fns)]()
+        marker.fill_(1)
+        plan.append({"key": "_".join(map(str, key)), "bytes": g["bytes"], "flops": g["flops"],
+                     "source": SOURCE_OF[key[0]], "source_sha": source_hash(SOURCE_OF[key[0]])})
+    torch.cuda.synchronize()
+    with open(manifest_path, "w") as f:
+        json.dump({"reps": COUNTER_REPS, "groups": plan}, f, indent=1)
+    log(f"counter pass: {len(plan)} groups of {COUNTER_REPS} launches; plan in {manifest_path}")
+
+
+def _counter_segments(csv_path, counter):
+    """Per marker-delimited segment (after the first marker): the summed counter of every
+    dispatch in it and the dispatched kernels' names."""
+    import csv
+    disp = {}
+    with open(csv_path, newline="") as f:
+        for r in csv.DictReader(f):
+            d = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "v": 0.0})
+            if r["Counter_Name"] == counter:
+                d["v"] += float(r["Counter_Value"])
+    segs, cur, started = [], None, False
+    for i in sorted(disp):
+        d = disp[i]
+        if "FillFunctor<short>" in d["name"]:
+            if started:
+                segs.append(cur)
+            started, cur = True, {"v": 0.0, "names": []}
+        elif started:
+            cur["v"] += d["v"]
+            cur["names"].append(d["name"].replace("(anonymous namespace)::", "").split("(")[0][:80])
+    return segs
+
+
+def traffic_from(manifest_path, fetch_csv, write_csv, out_path=None):
+    """profiles/traffic.json from two counter runs of the --counters pass.  FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch, read at the L2's memory side) are scaled by the factor that
+    makes the calibration copy read and write exactly its known bytes."""
+    with open(manifest_path) as f:
+        man = json.load(f)
+    reps = man["reps"]
+    fs, ws = _counter_segments(fetch_csv, "FETCH_SIZE"), _counter_segments(write_csv, "WRITE_SIZE")
+    groups = man["groups"]
+    if len(fs) != len(groups) or len(ws) != len(groups):
+        raise SystemExit(f"segments {len(fs)}/{len(ws)} do not match the plan's {len(groups)} groups")
+    copy = groups[0]
+    f_fac = copy["read_bytes"] / (fs[0]["v"] / reps * 1024)
+    w_fac = copy["write_bytes"] / (ws[0]["v"] / reps * 1024)
+    out = {"method": "rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, over bench.py --counters; KiB per "
+                     "dispatch summed over each call's dispatches, averaged over the calls, scaled by the copy factors",
+           "copy_calibration": {"bytes_read": copy["read_bytes"], "bytes_written": copy["write_bytes"],
+                                "fetch_kib_per_launch": fs[0]["v"] / reps, "write_kib_per_launch": ws[0]["v"] / reps,
+                                "fetch_factor": f_fac, "write_factor": w_fac},
+           "kernels": {}}
+    rows = []
+    for g, fseg, wseg in zip(groups[1:], fs[1:], ws[1:]):
+        rd = fseg["v"] / reps * 1024 * f_fac
+        wr = wseg["v"] / reps * 1024 * w_fac
+        out["kernels"][g["key"]] = {"source_sha": g["source_sha"], "dispatches": sorted(set(fseg["names"])),
+                                    "fetch_kib_raw": fseg["v"] / reps, "write_kib_raw": wseg["v"] / reps,
+                                    "hbm_read_bytes": rd, "hbm_write_bytes": wr, "hbm_bytes_per_launch": rd + wr,
+                                    "algorithmic_bytes": g["bytes"], "traffic_over_algorithmic": (rd + wr) / g["bytes"]}
+        rows.append((g["key"], g["bytes"], rd, wr, (rd + wr) / g["bytes"]))
+    # the three prefill GEMMs together, per launch
+    pre = [k for k in out["kernels"] if k.startswith("gemm_f16_1570_")]
+    if pre:
+        ks = [out["kernels"][k] for k in pre]
+        out["kernels"]["gemm_f16_prefill"] = {
+            "source_sha": ks[0]["source_sha"], "of": pre,
+            "hbm_bytes_per_launch": sum(k["hbm_bytes_per_launch"] for k in ks) / len(ks),
+            "algorithmic_bytes": sum(k["algorithmic_bytes"] for k in ks) / len(ks)}
+    path = out_path or os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(f"copy factors: fetch {f_fac:.3f}, write {w_fac:.3f}")
+    print("| kernel shape | algorithmic B | HBM read B | HBM write B | traffic / algorithmic |")
+    print("|---|---|---|---|---|")
+    for key, b, rd, wr, ratio in rows:
+        print(f"| {key} | {b} | {rd:.0f} | {wr:.0f} | {ratio:.3f} |")
+    print(f"wrote {path}")
 
 
 def source_hash(*names):
@@ -303,6 +421,9 @@ def cpu_baseline(np, oracle, synth):
 
 def main():
     args = parse_args()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -318,6 +439,9 @@ def main():
     torch.cuda.set_device(0)
     log(f"device {torch.cuda.get_device_name(0)}; library {w4.LIB_PATH}")
     wl = Workload(torch, np, w4, synth, unfused=args.unfused)
+    if args.counters:
+        counters_pass(torch, wl, args.counters)
+        return
 
     phases = [wl.run_gemvs, wl.run_head, wl.run_prefill]
     if args.eager:
