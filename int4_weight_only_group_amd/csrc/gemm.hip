@@ -222,6 +222,22 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
 // (a stage may be refilled right after the barrier), then barrier
 #define W4_SYNC(n) asm volatile("s_waitcnt vmcnt(" #n ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
+// LDS swizzles of the DMA kernel's stages, chosen so that every LDS read of a fragment is
+// free of bank conflicts whether the LDS serves 128 or 256 bytes per clock.
+//  A stage: row r holds 64 B = four 16-B chunks; logical chunk c sits at c ^ a_swz(r).  A
+//  b128 read covers rows r0..r0+15 (r0 % 16 == 0) at one logical chunk: a_swz is a bijection
+//  of (r >> 1) & 3 over any 8 consecutive rows of equal parity, and of (r >> 2) & 3 over the
+//  16 rows of equal r & 3, so both 8-lane and 16-lane phases hit distinct banks.
+//  B stage: k-row holds 512 B = 32 chunks; chunk c sits at c ^ b_swz(k).  A transposing b64
+//  read takes, per 16 lanes, 4 consecutive k-rows x 2 chunks and, per 32 lanes, 4 k-rows x
+//  4 chunks; b_swz(k) = 2 * h(k & 3) with h(x) = (x ^ 2x) & 7, whose bits 1..2 and 2..3 are
+//  both bijective in k & 3, spreads either phase over distinct banks.
+__device__ __forceinline__ int a_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int b_swz(int k) {
+  const int x = k & 3;
+  return ((x ^ (x << 1)) & 7) << 1;
+}
+
 __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs g) {
   extern __shared__ __align__(16) unsigned char dlds[];
   int tm, tn, split;
@@ -241,10 +257,10 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs g) {
   for (int ii = 0; ii < 4; ++ii) {
     const int i = wave * 4 + ii;
     const int row = 16 * i + (lane >> 2);
-    const int ca = (lane & 3) ^ ((row >> 1) & 3);
+    const int ca = (lane & 3) ^ a_swz(row);
     a_src[ii] = g.A + (int64_t)min(m0 + row, g.M - 1) * g.lda + kbeg + ca * 8;
     const int krow = 2 * i + (lane >> 5);
-    const int cb = (lane & 31) ^ (krow & 7);
+    const int cb = (lane & 31) ^ b_swz(krow);
     b_src[ii] = g.B + (int64_t)(kbeg + krow) * g.ldb + min(n0 + cb * 8, g.N - 8);
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t*)dlds;
@@ -267,7 +283,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs g) {
     for (int ks = 0; ks < 2; ++ks) {
       const int r = wm * 128 + mi * 32 + (lane & 31);
       const int c = 2 * ks + (lane >> 5);
-      a_off[mi][ks] = r * 64 + ((c ^ ((r >> 1) & 3)) * 16);
+      a_off[mi][ks] = r * 64 + ((c ^ a_swz(r)) * 16);
     }
   int b_off[4][2][2];
   {
@@ -281,7 +297,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs g) {
           const int krow = 16 * ks + 8 * (grp >> 1) + 4 * h + (L >> 2);
           const int ncol = wn * 128 + nj * 32 + (grp & 1) * 16 + 4 * (L & 3);
           const int c = ncol >> 3;
-          b_off[nj][ks][h] = BM * DBK * 2 + krow * 512 + ((c ^ (krow & 7)) * 16) + (L & 1) * 8;
+          b_off[nj][ks][h] = BM * DBK * 2 + krow * 512 + ((c ^ b_swz(krow)) * 16) + (L & 1) * 8;
         }
   }
 
@@ -293,41 +309,79 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  for (int t = 0; t < 3 && t < nk; ++t) issue(t);
-  for (int t = 0; t < nk; ++t) {
-    // this wave's DMA for tile t is done once at most the later tiles' 8 instructions each
-    // are outstanding; the barrier then covers every wave's part of tile t and guarantees
-    // that every wave has finished computing tile t - 1 (whose stage is refilled next).
-    const int later = min(2, nk - 1 - t);
+  // Operand fragments of one 16-wide k-step: A rows (b128 reads) and B columns (two
+  // transposing b64 reads each).  Two sets alternate so that the reads of the next k-step
+  // are in flight while the 16 MFMAs of the current one run.
+  struct Frag {
+    f16x8 a[4], b[4];
+  };
+  auto load = [&](const unsigned char* st, int ks, Frag& f) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) f.a[mi] = *reinterpret_cast<const f16x8*>(st + a_off[mi][ks]);
+#pragma unroll
+    for (int nj = 0; nj < 4; ++nj) {
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(st + b_off[nj][ks][0]));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(st + b_off[nj][ks][1]));
+      f.b[nj] = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int nj = 0; nj < 4; ++nj)
+        acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[mi], f.b[nj], acc[mi][nj], 0, 0, 0);
+  };
+  // the 12 LDS reads of the next fragments interleaved with the first 12 of 16 MFMAs
+  auto interleave = [&]() {
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  };
+
+  // Pipeline: the DMA runs up to 3 K-tiles ahead into a ring of 4 stages.  Iteration t
+  // reads k-step 1 of tile t while computing k-step 0, meets the other waves at a barrier
+  // (after it tile t + 1 has landed and no wave reads tile t's stage any more, so the DMA of
+  // tile t + 4 may overwrite it), then reads k-step 0 of tile t + 1 while computing k-step 1
+  // of tile t.
+  const int pre = min(DSTAGES, nk);
+  for (int t = 0; t < pre; ++t) issue(t);
+  switch (pre) {  // tile 0 landed; tiles 1 .. pre-1 (8 instructions each) may be in flight
+    case 4: W4_SYNC(24); break;
+    case 3: W4_SYNC(16); break;
+    case 2: W4_SYNC(8); break;
+    default: W4_SYNC(0); break;
+  }
+  Frag f0, f1;
+  load(dlds, 0, f0);
+  for (int t = 0; t + 1 < nk; ++t) {
+    load(dlds + (t % DSTAGES) * DSTAGE_BYTES, 1, f1);
+    mma(f0);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    const int later = min(2, nk - 2 - t);  // tiles after t + 1 already issued
     if (later == 2)
       W4_SYNC(16);
     else if (later == 1)
       W4_SYNC(8);
     else
       W4_SYNC(0);
-    if (t + 3 < nk) issue(t + 3);
-    const unsigned char* st = dlds + (t % DSTAGES) * DSTAGE_BYTES;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      f16x8 a[4], b[4];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) a[mi] = *reinterpret_cast<const f16x8*>(st + a_off[mi][ks]);
-#pragma unroll
-      for (int nj = 0; nj < 4; ++nj) {
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(st + b_off[nj][ks][0]));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(st + b_off[nj][ks][1]));
-        const short v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        b[nj] = __builtin_bit_cast(f16x8, v);
-      }
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < 4; ++nj)
-          acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mi], b[nj], acc[mi][nj], 0, 0, 0);
-    }
+    if (t + DSTAGES < nk) issue(t + DSTAGES);
+    load(dlds + ((t + 1) % DSTAGES) * DSTAGE_BYTES, 0, f0);
+    mma(f1);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
   }
+  load(dlds + ((nk - 1) % DSTAGES) * DSTAGE_BYTES, 1, f1);
+  mma(f0);
+  interleave();
+  __builtin_amdgcn_sched_barrier(0);
+  mma(f1);
 
   float* out = g.ksplit == 1 ? g.C : g.ws + (int64_t)split * g.M * g.N;
   const int64_t ldo = g.ksplit == 1 ? g.ldc : g.N;
