@@ -525,10 +525,8 @@ __global__ __launch_bounds__(256) void gemm_plain_kernel(const uint16_t* __restr
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < PL_ROWS; ++i) {
-    float v = acc[i];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    if (lane == 0) red[wave][i] = v;
+    const float v = group_sum<64>(acc[i]);
+    if (lane == 63) red[wave][i] = v;
   }
   __syncthreads();
   if (threadIdx.x < rows) {

@@ -172,13 +172,10 @@ __global__ __launch_bounds__(kWG) void gemv_kernel(const uint32_t* __restrict__ 
   for (int r = 0; r < R; ++r) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      float v = acc[r][m];
-#pragma unroll
-      for (int off = P / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, P);
-      acc[r][m] = v;
+      acc[r][m] = group_sum<P>(acc[r][m]);
     }
   }
-  if (lane == 0) {
+  if (lane == P - 1) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int n = row0 + r;
@@ -345,12 +342,9 @@ __global__ __launch_bounds__(kWG) void gemv1_kernel(const uint32_t* __restrict__
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      float a = (a0[r] + a1[r]) + (a2[r] + a3[r]);
-#pragma unroll
-      for (int off = L / 2; off >= 1; off >>= 1) a += __shfl_xor(a, off, L);
-      acc[r] = a;
+      acc[r] = group_sum<L>((a0[r] + a1[r]) + (a2[r] + a3[r]));
     }
-    if (lane == 0) {
+    if (lane == L - 1) {
 #pragma unroll
       for (int r = 0; r < R; ++r)
         if (blk * R + r < N) y[blk * R + r] = acc[r];

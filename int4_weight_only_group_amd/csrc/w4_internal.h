@@ -24,6 +24,28 @@ __device__ __forceinline__ uint4 load_nt(const void* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// Sum over aligned groups of W lanes (W = 16, 32 or 64) with DPP lane moves instead of LDS
+// permutes; the group's total lands in its last lane (lane W - 1 of the group).  Steps: swap
+// neighbours, swap pairs (quad sums), half-row mirror (8), row mirror (16: every lane of the
+// row), then broadcast row sums forward into rows 1, 3 (32) and rows 2, 3 (64).  The order of
+// the additions is fixed, so results are deterministic.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               CTRL, ROWS, 0xF, false));
+}
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(W == 16 || W == 32 || W == 64, "group of 16, 32 or 64 lanes");
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);  // row_half_mirror
+  v += dpp_f<0x140>(v);  // row_mirror
+  if constexpr (W >= 32) v += dpp_f<0x142, 0xA>(v);  // row_bcast15 into rows 1 and 3
+  if constexpr (W >= 64) v += dpp_f<0x143, 0xC>(v);  // row_bcast31 into rows 2 and 3
+  return v;
+}
+
 // ---------------------------------------------------------------- launchers
 void launch_pack(const uint8_t* q, uint32_t* qw, int64_t N, int64_t K, hipStream_t st);
 
