@@ -434,25 +434,28 @@ void launch_p(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const ui
     launch_r<MT, 64>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
 }
 
-// M = 1 policy: lanes per row, chunk iterations and rows per block by K; the grid is
-// capped so every team walks several row blocks (see launch_m1).
-// Per-shape choice measured on MI355X (back-to-back launches on distinct weights): short
-// rows use one-shot teams holding x in registers; long rows (K >= 3840) read x from LDS and
-// big matrices give each team several row blocks.
+// M = 1 policy (K / 32 = C chunks per row), measured on MI355X with back-to-back graph
+// launches on distinct weights: rows of 2048 take one 64-lane wave per row, two or four rows
+// per wave once N is large; rows of 6144 keep x in registers; longer rows read x from LDS
+// and very long ones loop two blocks per team.
 bool launch_gemv_m1(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
                     float* y, int N, int K, hipStream_t st) {
   const int C = K / 32;
   if (C <= 32) {
     launch_m1<32, 1, 1, true>(qw, s, b, x, y, N, K, 1, st);
   } else if (C <= 64) {
-    if (N >= 8192)
+    if (N >= 16384)
       launch_m1<64, 1, 4, false>(qw, s, b, x, y, N, K, 1, st);
+    else if (N >= 8192)
+      launch_m1<64, 1, 2, false>(qw, s, b, x, y, N, K, 2, st);
     else if (N > 2048 || N <= 1024)
       launch_m1<64, 1, 1, false>(qw, s, b, x, y, N, K, 1, st);
     else
       launch_m1<64, 1, 2, false>(qw, s, b, x, y, N, K, 1, st);
   } else if (C <= 128) {
-    launch_m1<64, 2, 1, true>(qw, s, b, x, y, N, K, N >= 16384 ? 6 : 1, st);
+    launch_m1<64, 2, 2, true>(qw, s, b, x, y, N, K, N >= 16384 ? 2 : 1, st);
+  } else if (C <= 192) {
+    launch_m1<64, 3, 2, false>(qw, s, b, x, y, N, K, 1, st);
   } else if (C <= 256) {
     launch_m1<64, 4, 1, true>(qw, s, b, x, y, N, K, 1, st);
   } else if (C <= 384) {

@@ -16,10 +16,21 @@
 // random logits only a few k keys pass the threshold; in the worst case (all equal) all of
 // them do and the sort covers the whole block, with the same result.
 //
+// Wave selection (wave_topk, k <= 64, no workgroup barrier): each lane holds E keys; the lane
+// whose maximum ranks k-1 among the 64 lane maxima gives the threshold T (at least k keys
+// reach it: the k lanes whose maxima do); keys >= T (at most k * E, usually about k) are
+// compacted with ballot/mbcnt, and each candidate's rank among them (the count of larger
+// candidates) is its output position.  Keys past the end of the data are padding keys that
+// are distinct and below every real key, so maxima and ranks never tie.  A workgroup of four
+// waves selects from 4 * 64 * E keys: each wave from its quarter, then one wave from the four
+// waves' 4k survivors.
+//
 // Long rows run in two passes: pass 1 selects each chunk's k best keys into the workspace,
 // pass 2 selects the row's k best among them.  Rows of at most 4096 logits take pass 2
 // straight from the logits.  Values are re-read from the logits at the chosen index, so
-// -0.0 stays -0.0.
+// -0.0 stays -0.0.  k > 64 takes the block selection above.
+#include <mutex>
+
 #include "w4_internal.h"
 
 namespace w4 {
@@ -145,6 +156,160 @@ __global__ __launch_bounds__(kWG) void topk_final_kernel(const float* __restrict
   }
 }
 
+// ------------------------------------------------------------------ wave selection (k <= 64)
+
+// Padding key for position p past the data: high word 0 (every real key's high word is at
+// least 0x00800000 for finite logits), low word unique per position.
+__device__ __forceinline__ uint64_t pad_key(uint32_t p) { return (uint64_t)p; }
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int src) {
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, src);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// The k largest of this wave's 64 * E distinct keys, sorted descending, into out[0..k).
+// wm: 64 keys of LDS, cand: 64 * E keys of LDS (both private to the wave).
+template <int E>
+__device__ void wave_topk(const uint64_t (&key)[E], int k, uint64_t* wm, uint64_t* cand,
+                          uint64_t* out) {
+  const int lane = threadIdx.x & 63;
+  uint64_t mx = key[0];
+#pragma unroll
+  for (int e = 1; e < E; ++e) mx = key[e] > mx ? key[e] : mx;
+  wm[lane] = mx;
+  wave_sync();
+  int rank = 0;
+  for (int j = 0; j < 64; ++j) rank += wm[j] > mx ? 1 : 0;
+  const uint64_t who = __ballot(rank == k - 1);  // exactly one lane: maxima are distinct
+  const uint64_t T = readlane64(mx, (int)__builtin_ctzll(who));
+  int c = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool take = key[e] >= T;
+    const uint64_t bits = __ballot(take);
+    const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(bits >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)bits, 0));
+    if (take) cand[c + before] = key[e];
+    c += __builtin_popcountll(bits);
+  }
+  wave_sync();
+  for (int i = lane; i < c; i += 64) {
+    const uint64_t ki = cand[i];
+    int r = 0;
+    for (int j = 0; j < c; ++j) r += cand[j] > ki ? 1 : 0;
+    if (r < k) out[r] = ki;
+  }
+  wave_sync();
+}
+
+// A workgroup of four waves: the k best of 4 * 64 * E keys (key[e] of lane l of wave w is
+// element w * 64 * E + e * 64 + l of the group's range) into out[0..k) (LDS, read after the
+// final barrier).
+template <int E>
+__device__ void group_topk(const uint64_t (&key)[E], int k, unsigned char* smem, uint64_t* out) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint64_t* wm = reinterpret_cast<uint64_t*>(smem) + w * 64;                // 4 x 64
+  uint64_t* surv = reinterpret_cast<uint64_t*>(smem) + 256;                 // 4 x 64
+  uint64_t* cand = reinterpret_cast<uint64_t*>(smem) + 512 + w * 64 * E;    // 4 x 64E
+  wave_topk<E>(key, k, wm, cand, surv + w * 64);
+  __syncthreads();
+  if (w == 0) {
+    uint64_t k2[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {  // survivors of wave e sit at e * 64 + (0 .. k-1)
+      k2[e] = lane < k ? surv[e * 64 + lane] : pad_key((uint32_t)(e * 64 + lane));
+    }
+    wave_topk<4>(k2, k, wm, cand, out);
+  }
+  __syncthreads();
+}
+
+template <int E>
+constexpr size_t group_lds() {
+  return (size_t)(512 + 4 * 64 * E + 64) * 8;
+}
+
+// Pass 1: the k best keys of logits[m][c*chunk, (c+1)*chunk) into cand[m][c][0:k),
+// chunk = 4 * 64 * E.
+template <int E>
+__global__ __launch_bounds__(kWG) void wtopk_chunk_kernel(const float* __restrict__ logits,
+                                                          int64_t ldl, int V, int k,
+                                                          uint64_t* __restrict__ cand) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int c = blockIdx.x, m = blockIdx.y;
+  const int nchunks = gridDim.x;
+  const float* row = logits + (int64_t)m * ldl;
+  const int base = c * (4 * 64 * E) + (threadIdx.x >> 6) * 64 * E + (threadIdx.x & 63);
+  uint64_t key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int v = base + e * 64;  // coalesced: one 256-byte row segment per e and wave
+    key[e] = v < V ? make_key(row[v], (uint32_t)v) : pad_key(~(uint32_t)v & 0x7fffffffu);
+  }
+  uint64_t* out = reinterpret_cast<uint64_t*>(smem) + 512 + 4 * 64 * E;
+  group_topk<E>(key, k, smem, out);
+  uint64_t* dst = cand + ((int64_t)m * nchunks + c) * k;
+  for (int i = threadIdx.x; i < k; i += kWG) dst[i] = out[i];
+}
+
+// Pass 2: the k best of a row's ncand keys (from cand, or the logits themselves when
+// cand == nullptr) -> indices and logits.
+template <int E>
+__global__ __launch_bounds__(kWG) void wtopk_final_kernel(const float* __restrict__ logits,
+                                                          int64_t ldl, int V, int k,
+                                                          const uint64_t* __restrict__ cand,
+                                                          int ncand, int32_t* __restrict__ idx,
+                                                          float* __restrict__ val) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int m = blockIdx.x;
+  const float* row = logits + (int64_t)m * ldl;
+  const int base = (threadIdx.x >> 6) * 64 * E + (threadIdx.x & 63);
+  uint64_t key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = base + e * 64;
+    uint64_t kk = pad_key(~(uint32_t)i & 0x7fffffffu);
+    if (i < ncand) kk = cand ? cand[(int64_t)m * ncand + i] : make_key(row[i], (uint32_t)i);
+    key[e] = kk;
+  }
+  uint64_t* out = reinterpret_cast<uint64_t*>(smem) + 512 + 4 * 64 * E;
+  group_topk<E>(key, k, smem, out);
+  for (int i = threadIdx.x; i < k; i += kWG) {
+    uint32_t j = key_index(out[i]);
+    if (j >= (uint32_t)V) j = (uint32_t)V - 1;  // unreachable for k <= V; keeps reads in bounds
+    idx[(int64_t)m * k + i] = (int32_t)j;
+    val[(int64_t)m * k + i] = row[j];
+  }
+}
+
+template <int E>
+void launch_wfinal(const float* logits, int64_t ldl, int M, int V, int k, const uint64_t* cand,
+                   int ncand, int32_t* idx, float* val, hipStream_t st) {
+  hipLaunchKernelGGL((wtopk_final_kernel<E>), dim3(M), dim3(kWG), group_lds<E>(), st, logits, ldl,
+                     V, k, cand, ncand, idx, val);
+}
+
+void wfinal_pass(const float* logits, int64_t ldl, int M, int V, int k, const uint64_t* cand,
+                 int ncand, int32_t* idx, float* val, hipStream_t st) {
+  if (ncand <= 256)
+    launch_wfinal<1>(logits, ldl, M, V, k, cand, ncand, idx, val, st);
+  else if (ncand <= 1024)
+    launch_wfinal<4>(logits, ldl, M, V, k, cand, ncand, idx, val, st);
+  else if (ncand <= 2048)
+    launch_wfinal<8>(logits, ldl, M, V, k, cand, ncand, idx, val, st);
+  else if (ncand <= 4096)
+    launch_wfinal<16>(logits, ldl, M, V, k, cand, ncand, idx, val, st);
+  else
+    launch_wfinal<32>(logits, ldl, M, V, k, cand, ncand, idx, val, st);
+}
+
 template <int E>
 void launch_final(const float* logits, int64_t ldl, int M, int V, int k, const uint64_t* cand,
                   int ncand, int32_t* idx, float* val, hipStream_t st) {
@@ -186,13 +351,34 @@ size_t topk_ws_bytes(int64_t M, int64_t V, int k) {
 
 void launch_topk(const float* logits, int64_t ldl, int M, int V, int k, int32_t* idx, float* val,
                  void* ws, hipStream_t st) {
+  static std::once_flag lds_attr;  // the E = 32 wave kernels use more than 64 KB of LDS
+  std::call_once(lds_attr, [] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(wtopk_chunk_kernel<32>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)group_lds<32>());
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(wtopk_final_kernel<32>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)group_lds<32>());
+  });
+  const bool wave = k <= 64;
   if (V <= 4096) {
-    final_pass(logits, ldl, M, V, k, nullptr, V, idx, val, st);
+    if (wave)
+      wfinal_pass(logits, ldl, M, V, k, nullptr, V, idx, val, st);
+    else
+      final_pass(logits, ldl, M, V, k, nullptr, V, idx, val, st);
     return;
   }
   const int chunk = topk_chunk(V, k);
   const int nchunks = (V + chunk - 1) / chunk;
   uint64_t* cand = reinterpret_cast<uint64_t*>(ws);
+  if (wave) {
+    if (chunk == 4096)
+      hipLaunchKernelGGL((wtopk_chunk_kernel<16>), dim3(nchunks, M), dim3(kWG), group_lds<16>(), st,
+                         logits, ldl, V, k, cand);
+    else
+      hipLaunchKernelGGL((wtopk_chunk_kernel<32>), dim3(nchunks, M), dim3(kWG), group_lds<32>(), st,
+                         logits, ldl, V, k, cand);
+    wfinal_pass(logits, ldl, M, V, k, cand, nchunks * k, idx, val, st);
+    return;
+  }
   if (chunk == 4096)
     hipLaunchKernelGGL((topk_chunk_kernel<16>), dim3(nchunks, M), dim3(kWG), (size_t)chunk * 8, st,
                        logits, ldl, V, k, cand);

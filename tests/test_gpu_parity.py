@@ -321,6 +321,8 @@ def topk_case(w4, logits, k):
 @pytest.mark.parametrize("m,v,k", [
     (1, 1, 1), (1, 2, 1), (16, 2, 1), (3, 5, 5), (2, 100, 40), (1, 4096, 64), (2, 4097, 64),
     (1, 151936, 40), (8, 262144, 64), (1, 262144, 256), (4, 9000, 256), (1, 40000, 1),
+    # last chunk nearly empty (padding fills most of its top-k), 8192-logit chunks, odd k
+    (2, 12293, 64), (3, 4099, 40), (1, 600000, 64), (1, 70000, 63), (2, 8191, 17),
 ])
 def test_topk_random(w4, m, v, k):
     logits = (np.random.default_rng(m * v + k).standard_normal((m, v)) * 0.9).astype(np.float32)
