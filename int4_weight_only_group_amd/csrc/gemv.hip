@@ -250,10 +250,11 @@ __global__ __launch_bounds__(kWG) void gemv1_kernel(const uint32_t* __restrict__
   const uint16_t* sl = sc + (lane >> 1);
   const uint16_t* bl = bi + (lane >> 1);
 
-  // Every load is unconditional (block and chunk indices are clamped to valid addresses, a
-  // chunk past the end of the row is zeroed after the load): with no branch around a load,
-  // the compiler's wait counts stay exact and the next block's loads are never waited for
-  // while the current block is being computed.
+  // Every load is unconditional (block and chunk indices are clamped to valid addresses; a
+  // chunk past the end of the row is neutralised in the math by a zero scale and bias, never
+  // by overwriting the loaded register, which would force a wait for the load).  With no
+  // branch around a load and nothing touching a loaded register before its use, the
+  // compiler's wait counts stay exact: the math of a chunk waits only for that chunk.
   auto valid = [&](int j) { return EXACT || lane + j * L < C; };
   auto load = [&](int blk, Block<R, NIT>& B) {
     blk = min(blk, nblocks - 1);
@@ -269,14 +270,32 @@ __global__ __launch_bounds__(kWG) void gemv1_kernel(const uint32_t* __restrict__
         B.w[r][j] = load_nt(p + jc);
         B.s[r][j] = ps[jc >> 1];
         B.b[r][j] = pb[jc >> 1];
-        if (!valid(j)) {
-          B.w[r][j] = make_uint4(0, 0, 0, 0);  // weight = fma(0, 0, 0) = 0
-          B.s[r][j] = 0;
-          B.b[r][j] = 0;
-        }
       }
     }
   };
+
+  // x is loaded first: it is L2-resident and shared by every row, and loads complete in
+  // order, so issuing it ahead of the weight stream lets the math wait for x without
+  // waiting for the weights.  XL stages it in LDS (NIT 16-byte pieces per thread cover
+  // C * 4 >= the row) behind an LDS-only barrier; otherwise each lane keeps its chunks.
+  constexpr int XR = XL ? NIT : 1;
+  uint4 xr[XR];
+  uint4 xv[XL ? 1 : NIT][4];
+  if constexpr (XL) {
+#pragma unroll
+    for (int t = 0; t < XR; ++t) {
+      const int i = min((int)threadIdx.x + t * kWG, C * 4 - 1);
+      xr[t] = *reinterpret_cast<const uint4*>(x + i * 8);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NIT; ++j) {
+      const int c = min(lane + j * L, C - 1);
+      const uint4* xp = reinterpret_cast<const uint4*>(x + c * 32);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xv[j][i] = xp[i];
+    }
+  }
 
   Block<R, NIT> A, B;
   int blk = team;
@@ -284,9 +303,13 @@ __global__ __launch_bounds__(kWG) void gemv1_kernel(const uint32_t* __restrict__
   __builtin_amdgcn_sched_barrier(0);
   uint4* xs = reinterpret_cast<uint4*>(smem);
   if constexpr (XL) {
-    for (int i = threadIdx.x; i < C * 4; i += kWG)
-      xs[i] = pair_up(*reinterpret_cast<const uint4*>(x + i * 8));
-    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < XR; ++t) {
+      const int i = (int)threadIdx.x + t * kWG;
+      if (i < C * 4) xs[i] = pair_up(xr[t]);
+    }
+    // LDS visibility only: a __syncthreads would also wait for every weight load in flight
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
   if (team >= nblocks) return;
 
@@ -295,19 +318,6 @@ __global__ __launch_bounds__(kWG) void gemv1_kernel(const uint32_t* __restrict__
   k.m_hi = __builtin_amdgcn_readfirstlane(0x00F000F0u);
   k.mag_lo = __builtin_amdgcn_readfirstlane(0x64006400u);
   k.mag_hi = __builtin_amdgcn_readfirstlane(0x54005400u);
-
-  // this lane's slice of x, as pairs; zero past the end of the row
-  uint4 xv[XL ? 1 : NIT][4];
-#pragma unroll
-  for (int j = 0; j < (XL ? 0 : NIT); ++j) {
-    const int c = valid(j) ? lane + j * L : C - 1;
-    const uint4* xp = reinterpret_cast<const uint4*>(x + c * 32);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      xv[j][i] = pair_up(xp[i]);
-      if (!valid(j)) xv[j][i] = make_uint4(0, 0, 0, 0);
-    }
-  }
 
   auto compute = [&](int blk, const Block<R, NIT>& B) {
     float acc[R];
@@ -318,21 +328,23 @@ __global__ __launch_bounds__(kWG) void gemv1_kernel(const uint32_t* __restrict__
     for (int j = 0; j < NIT; ++j) {
       uint4 x0, x1, x2, x3;
       if constexpr (XL) {
-        const int c = valid(j) ? lane + j * L : C - 1;  // invalid chunks have zero weights
+        const int c = min(lane + j * L, C - 1);  // chunks past the row end get zero weights
         x0 = xs[c * 4 + 0];
         x1 = xs[c * 4 + 1];
         x2 = xs[c * 4 + 2];
         x3 = xs[c * 4 + 3];
       } else {
-        x0 = xv[j][0];
-        x1 = xv[j][1];
-        x2 = xv[j][2];
-        x3 = xv[j][3];
+        x0 = pair_up(xv[j][0]);
+        x1 = pair_up(xv[j][1]);
+        x2 = pair_up(xv[j][2]);
+        x3 = pair_up(xv[j][3]);
       }
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const f16 sv = __builtin_bit_cast(f16, (uint16_t)B.s[r][j]);
-        const f16 bv = __builtin_bit_cast(f16, (uint16_t)B.b[r][j]);
+        // past the row end: s = b = 0, so every weight is fma(q, 0, 0) = 0 exactly
+        const uint32_t sb_on = valid(j) ? 0xFFFFu : 0u;
+        const f16 sv = __builtin_bit_cast(f16, (uint16_t)(B.s[r][j] & sb_on));
+        const f16 bv = __builtin_bit_cast(f16, (uint16_t)(B.b[r][j] & sb_on));
         const h2 s2 = {sv, sv}, b2 = {bv, bv};
         a0[r] = word_fma(B.w[r][j].x, s2, b2, x0, a0[r], k);
         a1[r] = word_fma(B.w[r][j].y, s2, b2, x1, a1[r], k);
@@ -435,25 +447,23 @@ void launch_p(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const ui
 }
 
 // M = 1 policy (K / 32 = C chunks per row), measured on MI355X with back-to-back graph
-// launches on distinct weights: rows of 2048 take one 64-lane wave per row, two or four rows
-// per wave once N is large; rows of 6144 keep x in registers; longer rows read x from LDS
-// and very long ones loop two blocks per team.
+// launches on distinct weights: rows of 2048 take one 64-lane wave per row, two rows per
+// wave and two blocks per team once N is large; rows up to 6144 keep x in registers; longer
+// rows read x from LDS and very long ones loop two blocks per team.
 bool launch_gemv_m1(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
                     float* y, int N, int K, hipStream_t st) {
   const int C = K / 32;
   if (C <= 32) {
     launch_m1<32, 1, 1, true>(qw, s, b, x, y, N, K, 1, st);
   } else if (C <= 64) {
-    if (N >= 16384)
-      launch_m1<64, 1, 4, false>(qw, s, b, x, y, N, K, 1, st);
-    else if (N >= 8192)
+    if (N >= 8192)
       launch_m1<64, 1, 2, false>(qw, s, b, x, y, N, K, 2, st);
     else if (N > 2048 || N <= 1024)
       launch_m1<64, 1, 1, false>(qw, s, b, x, y, N, K, 1, st);
     else
       launch_m1<64, 1, 2, false>(qw, s, b, x, y, N, K, 1, st);
   } else if (C <= 128) {
-    launch_m1<64, 2, 2, true>(qw, s, b, x, y, N, K, N >= 16384 ? 2 : 1, st);
+    launch_m1<64, 2, 2, false>(qw, s, b, x, y, N, K, N >= 16384 ? 2 : 1, st);
   } else if (C <= 192) {
     launch_m1<64, 3, 2, false>(qw, s, b, x, y, N, K, 1, st);
   } else if (C <= 256) {

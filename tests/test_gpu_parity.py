@@ -143,9 +143,18 @@ def test_gemv_single_config_full(w4):
     assert ok, worst
 
 
+def _fused(layer, groups):
+    """Row-concatenated shapes of matrices that read the same x (q|k|v, gate|up)."""
+    shape = {name: (n, k) for name, n, k in layer}
+    return {(sum(shape[g][0] for g in grp), shape[grp[0]][1]) for grp in groups if all(g in shape for g in grp)}
+
+
 WORKLOAD_SHAPES = sorted({(n, k) for _, n, k in synth.QWEN25_3B_LAYER}
                          | {(n, k) for _, n, k in synth.QWEN3_1P7B_CLASSIFY}
-                         | {(n, k) for _, n, k in synth.GEMMA12B_LAYER})
+                         | {(n, k) for _, n, k in synth.GEMMA12B_LAYER}
+                         | _fused(synth.QWEN25_3B_LAYER, [["q", "k", "v"], ["gate", "up"]])
+                         | _fused(synth.QWEN3_1P7B_CLASSIFY, [["q", "k", "v"], ["gate", "up"]])
+                         | _fused(synth.GEMMA12B_LAYER, [["gate", "up"]]))
 
 
 @pytest.mark.parametrize("n,k", WORKLOAD_SHAPES)
