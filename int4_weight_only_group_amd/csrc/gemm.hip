@@ -7,12 +7,13 @@
 //    ("What's inside the engine today").
 //
 // Paths, chosen per call by shape and alignment:
-//  * MFMA (M > 8): 128 x 256 block tile, BK = 32, four waves each owning a 64 x 128 tile of
-//    v_mfma_f32_32x32x16_f16.  B arrives [K][N] (N contiguous) but the matrix core wants K
-//    contiguous per lane, so each thread loads a 4 (k) x 8 (n) block of B with 16-byte loads
-//    and transposes it in registers before writing LDS as [n][k].  Tails: rows of A and
-//    column blocks of B are clamped on load (never stored) and the K tail is zero-filled, so
-//    the MFMA loop itself has no guards.
+//  * MFMA (M > 8, K % 32 == 0, 16-byte aligned operands): 256 x 256 block tile, operands
+//    moved HBM -> LDS by LDS DMA through a 4-stage ring, eight waves (two per SIMD) each
+//    owning a 128 x 64 tile of v_mfma_f32_32x32x16_f16; B is read from its [K][N] layout with
+//    transposing LDS reads.  K % 32 != 0 takes a register-staged variant.  Tails: rows of A
+//    and column blocks of B are clamped on load (never stored) and the K tail is zero-filled,
+//    so the MFMA loop itself has no guards.  Too few tiles for the CUs: K is split and the
+//    slices summed in a fixed order by a second kernel.
 //  * small M (M <= 8, decode head): each lane owns 8 contiguous columns and streams B rows
 //    with 16-byte loads; the four waves of a workgroup split K and reduce through LDS.  The
 //    A values of a k are wave-uniform scalar loads.
@@ -187,23 +188,25 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs g) {
 }
 
 // ------------------------------------------------------------- MFMA path, LDS DMA
-// Same 256 x 256 tile and 4 x (128 x 128) wave split as above, but both operands travel
-// HBM -> LDS with gfx950's 16-byte LDS DMA (global_load_lds_dwordx4: lane l's 16 bytes land
-// at the instruction's LDS base + 16 l), so no registers hold tiles in flight.  Four LDS
-// stages of BK = 32 (32 KB each) keep three K-tiles in flight while the matrix cores work on
-// the fourth.  B stays [k][n] in LDS and its MFMA operand (8 consecutive k of one column per
-// lane) is read with two ds_read_b64_tr_b16: within each 16-lane group, result lane i gets
-// element i mod 4 of source lanes 4e + i / 4 (e = 0..3), so source lane L pointing at
-// B[k0 + L / 4][n0 + 4 (L mod 4)] hands lane i the column B[k0 .. k0 + 3][n0 + i].
-// The 16-byte chunks are XOR-swizzled in LDS (A: chunk ^ (row / 2 mod 4) within a 64-byte
-// row; B: chunk ^ (k mod 8) within a 512-byte row) so the operand reads do not pile onto the
-// same banks.  Waits are explicit (vmcnt for this wave's DMA, then a plain s_barrier): a
-// __syncthreads() would drain every K-tile in flight.  Requires K % 32 == 0 (split-K slices
-// are multiples of 32); other K take the register-staged kernel above.
+// Same 256 x 256 tile as above, but both operands travel HBM -> LDS with gfx950's 16-byte
+// LDS DMA (global_load_lds_dwordx4: lane l's 16 bytes land at the instruction's LDS base +
+// 16 l), so no registers hold tiles in flight.  Four LDS stages of BK = 32 (32 KB each) keep
+// three K-tiles in flight while the matrix cores work on the fourth.  Eight waves, two per
+// SIMD, each own 128 x 64 of the tile (4 x 2 accumulators): while one wave of a SIMD waits
+// on its DMA issue or a barrier, the other issues MFMAs (measured 7-13 % faster than four
+// waves of 128 x 128).  B stays [k][n] in LDS and its MFMA operand (8 consecutive k of one
+// column per lane) is read with two ds_read_b64_tr_b16: within each 16-lane group, result
+// lane i gets element i mod 4 of source lanes 4e + i / 4 (e = 0..3), so source lane L
+// pointing at B[k0 + L / 4][n0 + 4 (L mod 4)] hands lane i the column B[k0 .. k0 + 3][n0 + i].
+// The 16-byte chunks are XOR-swizzled in LDS (a_swz, b_swz below).  Waits are explicit
+// (vmcnt for this wave's DMA, then a plain s_barrier): a __syncthreads() would drain every
+// K-tile in flight.  Requires K % 32 == 0 (split-K slices are multiples of 32); other K take
+// the register-staged kernel above.
 constexpr int DBK = 32;
 constexpr int DSTAGES = 4;
 constexpr int DSTAGE_BYTES = (BM + BN) * DBK * 2;      // 32 KB
 constexpr size_t kDmaLds = (size_t)DSTAGES * DSTAGE_BYTES;
+constexpr int kDmaWaves = 8;  // waves per workgroup (4 also builds: one per SIMD, 128 x 128)
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -238,7 +241,24 @@ __device__ __forceinline__ int b_swz(int k) {
   return ((x ^ (x << 1)) & 7) << 1;
 }
 
-__global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs g) {
+// W4_SYNC with a wave-uniform count of DMA instructions allowed to stay in flight
+__device__ __forceinline__ void dma_sync(int n) {
+  switch (n) {
+    case 24: W4_SYNC(24); break;
+    case 16: W4_SYNC(16); break;
+    case 12: W4_SYNC(12); break;
+    case 8: W4_SYNC(8); break;
+    case 4: W4_SYNC(4); break;
+    default: W4_SYNC(0); break;
+  }
+}
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_dma_kernel(GemmArgs g) {
+  constexpr int WN = NW / 2;    // waves along N (two along M)
+  constexpr int WTN = BN / WN;  // columns per wave
+  constexpr int NJ = WTN / 32;  // 32-column MFMA blocks per wave
+  constexpr int DI = 16 / NW;   // A and B DMA instructions per wave and K-tile (each)
   extern __shared__ __align__(16) unsigned char dlds[];
   int tm, tn, split;
   tile_of(g, blockIdx.x, tm, tn, split);
@@ -248,14 +268,15 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs g) {
   const int nk = (kend - kbeg) / DBK;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
 
-  // DMA source addresses (this lane, K-tile 0): wave w issues A and B instructions 4w..4w+3
-  const uint16_t* a_src[4];
-  const uint16_t* b_src[4];
+  // DMA source addresses (this lane, K-tile 0): wave w issues A and B instructions
+  // DI*w .. DI*w + DI - 1 of the 16 each
+  const uint16_t* a_src[DI];
+  const uint16_t* b_src[DI];
 #pragma unroll
-  for (int ii = 0; ii < 4; ++ii) {
-    const int i = wave * 4 + ii;
+  for (int ii = 0; ii < DI; ++ii) {
+    const int i = wave * DI + ii;
     const int row = 16 * i + (lane >> 2);
     const int ca = (lane & 3) ^ a_swz(row);
     a_src[ii] = g.A + (int64_t)min(m0 + row, g.M - 1) * g.lda + kbeg + ca * 8;
@@ -267,12 +288,12 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs g) {
   auto issue = [&](int t) {
     const uint32_t st = lds_base + (uint32_t)((t % DSTAGES) * DSTAGE_BYTES);
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
-      dma16(a_src[ii] + t * DBK, st + (uint32_t)((wave * 4 + ii) * 1024));
+    for (int ii = 0; ii < DI; ++ii)
+      dma16(a_src[ii] + t * DBK, st + (uint32_t)((wave * DI + ii) * 1024));
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
+    for (int ii = 0; ii < DI; ++ii)
       dma16(b_src[ii] + (int64_t)t * DBK * g.ldb,
-            st + (uint32_t)(BM * DBK * 2 + (wave * 4 + ii) * 1024));
+            st + (uint32_t)(BM * DBK * 2 + (wave * DI + ii) * 1024));
   };
 
   // per-lane LDS read offsets (bytes within a stage)
@@ -285,27 +306,27 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs g) {
       const int c = 2 * ks + (lane >> 5);
       a_off[mi][ks] = r * 64 + ((c ^ a_swz(r)) * 16);
     }
-  int b_off[4][2][2];
+  int b_off[NJ][2][2];
   {
     const int grp = lane >> 4, L = lane & 15;
 #pragma unroll
-    for (int nj = 0; nj < 4; ++nj)
+    for (int nj = 0; nj < NJ; ++nj)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int krow = 16 * ks + 8 * (grp >> 1) + 4 * h + (L >> 2);
-          const int ncol = wn * 128 + nj * 32 + (grp & 1) * 16 + 4 * (L & 3);
+          const int ncol = wn * WTN + nj * 32 + (grp & 1) * 16 + 4 * (L & 3);
           const int c = ncol >> 3;
           b_off[nj][ks][h] = BM * DBK * 2 + krow * 512 + ((c ^ b_swz(krow)) * 16) + (L & 1) * 8;
         }
   }
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
@@ -313,13 +334,13 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs g) {
   // transposing b64 reads each).  Two sets alternate so that the reads of the next k-step
   // are in flight while the 16 MFMAs of the current one run.
   struct Frag {
-    f16x8 a[4], b[4];
+    f16x8 a[4], b[NJ];
   };
   auto load = [&](const unsigned char* st, int ks, Frag& f) {
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) f.a[mi] = *reinterpret_cast<const f16x8*>(st + a_off[mi][ks]);
 #pragma unroll
-    for (int nj = 0; nj < 4; ++nj) {
+    for (int nj = 0; nj < NJ; ++nj) {
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) s16x4*)(st + b_off[nj][ks][0]));
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -331,17 +352,19 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs g) {
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-      for (int nj = 0; nj < 4; ++nj)
+      for (int nj = 0; nj < NJ; ++nj)
         acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[mi], f.b[nj], acc[mi][nj], 0, 0, 0);
   };
-  // the 12 LDS reads of the next fragments interleaved with the first 12 of 16 MFMAs
+  // the 4 + 2 * NJ LDS reads of the next fragments interleaved one-to-one with the first of
+  // the 4 * NJ MFMAs
+  constexpr int RD = 4 + 2 * NJ, MF = 4 * NJ;
   auto interleave = [&]() {
 #pragma unroll
-    for (int i = 0; i < 12; ++i) {
+    for (int i = 0; i < RD; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    if constexpr (MF > RD) __builtin_amdgcn_sched_group_barrier(0x008, MF - RD, 0);
   };
 
   // Pipeline: the DMA runs up to 3 K-tiles ahead into a ring of 4 stages.  Iteration t
@@ -351,12 +374,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs g) {
   // of tile t.
   const int pre = min(DSTAGES, nk);
   for (int t = 0; t < pre; ++t) issue(t);
-  switch (pre) {  // tile 0 landed; tiles 1 .. pre-1 (8 instructions each) may be in flight
-    case 4: W4_SYNC(24); break;
-    case 3: W4_SYNC(16); break;
-    case 2: W4_SYNC(8); break;
-    default: W4_SYNC(0); break;
-  }
+  dma_sync((pre - 1) * 2 * DI);  // tile 0 landed; tiles 1 .. pre-1 may be in flight
   Frag f0, f1;
   load(dlds, 0, f0);
   for (int t = 0; t + 1 < nk; ++t) {
@@ -364,13 +382,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs g) {
     mma(f0);
     interleave();
     __builtin_amdgcn_sched_barrier(0);
-    const int later = min(2, nk - 2 - t);  // tiles after t + 1 already issued
-    if (later == 2)
-      W4_SYNC(16);
-    else if (later == 1)
-      W4_SYNC(8);
-    else
-      W4_SYNC(0);
+    dma_sync(min(2, nk - 2 - t) * 2 * DI);  // tiles after t + 1 already issued may fly
     if (t + DSTAGES < nk) issue(t + DSTAGES);
     load(dlds + ((t + 1) % DSTAGES) * DSTAGE_BYTES, 0, f0);
     mma(f1);
@@ -388,8 +400,8 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + wn * 128 + j * 32 + (lane & 31);
+    for (int j = 0; j < NJ; ++j) {
+      const int col = n0 + wn * WTN + j * 32 + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
@@ -560,7 +572,7 @@ void launch_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
       std::call_once(lds_attr, [] {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_mfma_kernel),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_dma_kernel),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_dma_kernel<kDmaWaves>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDmaLds);
       });
       const GemmPlan p = plan_mfma(M, N, K);
@@ -568,7 +580,7 @@ void launch_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                  p.tilesM, p.tilesN, p.ksplit, p.kslice};
       const dim3 grid((unsigned)(p.tilesM * p.tilesN * p.ksplit));
       if (K % DBK == 0)
-        hipLaunchKernelGGL(gemm_dma_kernel, grid, dim3(256), kDmaLds, st, g);
+        hipLaunchKernelGGL(gemm_dma_kernel<kDmaWaves>, grid, dim3(64 * kDmaWaves), kDmaLds, st, g);
       else
         hipLaunchKernelGGL(gemm_mfma_kernel, grid, dim3(256), kGemmLds, st, g);
       if (p.ksplit > 1) {
