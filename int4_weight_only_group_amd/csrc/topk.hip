@@ -115,11 +115,16 @@ __global__ __launch_bounds__(kWG) void topk_chunk_kernel(const float* __restrict
   const int nchunks = gridDim.x;
   const float* row = logits + (int64_t)m * ldl;
   const int base = c * (E * kWG);
+  // all loads first (clamped index, no branch around a load, so none waits for another),
+  // then the keys; positions past V get 0, below every key
+  float lv[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) lv[e] = row[min(base + e * kWG + (int)threadIdx.x, V - 1)];
   uint64_t key[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int v = base + e * kWG + threadIdx.x;  // coalesced: one row segment per e
-    key[e] = v < V ? make_key(row[v], (uint32_t)v) : 0ull;  // 0 sorts below every key
+    key[e] = v < V ? make_key(lv[e], (uint32_t)v) : 0ull;
   }
   block_topk<E>(key, k, s, &cnt);
   uint64_t* out = cand + ((int64_t)m * nchunks + c) * k;
@@ -140,12 +145,21 @@ __global__ __launch_bounds__(kWG) void topk_final_kernel(const float* __restrict
   const int m = blockIdx.x;
   const float* row = logits + (int64_t)m * ldl;
   uint64_t key[E];
+  if (cand) {
+    uint64_t cv[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int i = e * kWG + threadIdx.x;
-    uint64_t kk = 0ull;
-    if (i < ncand) kk = cand ? cand[(int64_t)m * ncand + i] : make_key(row[i], (uint32_t)i);
-    key[e] = kk;
+    for (int e = 0; e < E; ++e) cv[e] = cand[(int64_t)m * ncand + min(e * kWG + (int)threadIdx.x, ncand - 1)];
+#pragma unroll
+    for (int e = 0; e < E; ++e) key[e] = e * kWG + (int)threadIdx.x < ncand ? cv[e] : 0ull;
+  } else {
+    float lv[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) lv[e] = row[min(e * kWG + (int)threadIdx.x, ncand - 1)];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int i = e * kWG + threadIdx.x;
+      key[e] = i < ncand ? make_key(lv[e], (uint32_t)i) : 0ull;
+    }
   }
   block_topk<E>(key, k, s, &cnt);
   for (int i = threadIdx.x; i < k; i += kWG) {
@@ -174,6 +188,31 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t v, int src) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// 16 keys from 128-byte-aligned LDS with eight 16-byte reads issued back to back.
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void load16(const uint64_t* src, uint64_t (&v)[16]) {
+  u64x2 p[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) p[q] = reinterpret_cast<const u64x2*>(src)[q];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    v[2 * q] = p[q][0];
+    v[2 * q + 1] = p[q][1];
+  }
+}
+
+// Number of keys greater than x in a descending list of n <= 64 distinct keys (branchless
+// binary search, seven probes).
+__device__ __forceinline__ int count_greater(const uint64_t* list, int n, uint64_t x) {
+  int lo = 0;
+#pragma unroll
+  for (int step = 64; step >= 1; step >>= 1) {
+    const int probe = min(lo + step, n) - 1;
+    if (lo + step <= n && list[probe] > x) lo += step;
+  }
+  return lo;
+}
+
 // The k largest of this wave's 64 * E distinct keys, sorted descending, into out[0..k).
 // wm: 64 keys of LDS, cand: 64 * E keys of LDS (both private to the wave).
 template <int E>
@@ -185,8 +224,14 @@ __device__ void wave_topk(const uint64_t (&key)[E], int k, uint64_t* wm, uint64_
   for (int e = 1; e < E; ++e) mx = key[e] > mx ? key[e] : mx;
   wm[lane] = mx;
   wave_sync();
-  int rank = 0;
-  for (int j = 0; j < 64; ++j) rank += wm[j] > mx ? 1 : 0;
+  int rank = 0;  // LDS reads in batches of 8 x 16 bytes so their latencies overlap
+#pragma unroll
+  for (int bt = 0; bt < 4; ++bt) {
+    uint64_t v[16];
+    load16(wm + bt * 16, v);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) rank += v[q] > mx ? 1 : 0;
+  }
   const uint64_t who = __ballot(rank == k - 1);  // exactly one lane: maxima are distinct
   const uint64_t T = readlane64(mx, (int)__builtin_ctzll(who));
   int c = 0;
@@ -196,14 +241,25 @@ __device__ void wave_topk(const uint64_t (&key)[E], int k, uint64_t* wm, uint64_
     const uint64_t bits = __ballot(take);
     const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(bits >> 32),
                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)bits, 0));
-    if (take) cand[c + before] = key[e];
+    // lanes that drop their key write it to their own dead slot of wm (read before T was
+    // chosen), so the write needs no branch
+    *(take ? cand + c + before : wm + lane) = key[e];
     c += __builtin_popcountll(bits);
   }
+  // pad the candidates to a multiple of 16 with 0, below every real or padding key (c <= 64E,
+  // a multiple of 16), so the rank scan reads 16 at a time with its LDS reads overlapped
+  const int c16 = (c + 15) & ~15;
+  if (lane < c16 - c) cand[c + lane] = 0ull;
   wave_sync();
   for (int i = lane; i < c; i += 64) {
     const uint64_t ki = cand[i];
     int r = 0;
-    for (int j = 0; j < c; ++j) r += cand[j] > ki ? 1 : 0;
+    for (int j = 0; j < c16; j += 16) {
+      uint64_t v[16];
+      load16(cand + j, v);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) r += v[q] > ki ? 1 : 0;
+    }
     if (r < k) out[r] = ki;
   }
   wave_sync();
@@ -211,7 +267,10 @@ __device__ void wave_topk(const uint64_t (&key)[E], int k, uint64_t* wm, uint64_
 
 // A workgroup of four waves: the k best of 4 * 64 * E keys (key[e] of lane l of wave w is
 // element w * 64 * E + e * 64 + l of the group's range) into out[0..k) (LDS, read after the
-// final barrier).
+// final barrier).  Each wave selects its sorted k best; the four sorted lists are then
+// merged by rank: survivor i of list w is preceded by the i before it in its own list and by
+// the survivors of the other three lists that are larger (binary search), and lands at that
+// rank if it is below k.
 template <int E>
 __device__ void group_topk(const uint64_t (&key)[E], int k, unsigned char* smem, uint64_t* out) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -220,20 +279,19 @@ __device__ void group_topk(const uint64_t (&key)[E], int k, unsigned char* smem,
   uint64_t* cand = reinterpret_cast<uint64_t*>(smem) + 512 + w * 64 * E;    // 4 x 64E
   wave_topk<E>(key, k, wm, cand, surv + w * 64);
   __syncthreads();
-  if (w == 0) {
-    uint64_t k2[4];
+  if (lane < k) {
+    const uint64_t x = surv[w * 64 + lane];
+    int r = lane;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {  // survivors of wave e sit at e * 64 + (0 .. k-1)
-      k2[e] = lane < k ? surv[e * 64 + lane] : pad_key((uint32_t)(e * 64 + lane));
-    }
-    wave_topk<4>(k2, k, wm, cand, out);
+    for (int o = 1; o < 4; ++o) r += count_greater(surv + ((w + o) & 3) * 64, k, x);
+    if (r < k) out[r] = x;
   }
   __syncthreads();
 }
 
 template <int E>
 constexpr size_t group_lds() {
-  return (size_t)(512 + 4 * 64 * E + 64) * 8;
+  return (size_t)(512 + 4 * 64 * E + 64) * 8;  // wm, surv, 4 candidate areas, out
 }
 
 // Pass 1: the k best keys of logits[m][c*chunk, (c+1)*chunk) into cand[m][c][0:k),
@@ -247,11 +305,14 @@ __global__ __launch_bounds__(kWG) void wtopk_chunk_kernel(const float* __restric
   const int nchunks = gridDim.x;
   const float* row = logits + (int64_t)m * ldl;
   const int base = c * (4 * 64 * E) + (threadIdx.x >> 6) * 64 * E + (threadIdx.x & 63);
+  float lv[E];  // all loads first: clamped, unconditional, so none waits for another
+#pragma unroll
+  for (int e = 0; e < E; ++e) lv[e] = row[min(base + e * 64, V - 1)];
   uint64_t key[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int v = base + e * 64;  // coalesced: one 256-byte row segment per e and wave
-    key[e] = v < V ? make_key(row[v], (uint32_t)v) : pad_key(~(uint32_t)v & 0x7fffffffu);
+    key[e] = v < V ? make_key(lv[e], (uint32_t)v) : pad_key(~(uint32_t)v & 0x7fffffffu);
   }
   uint64_t* out = reinterpret_cast<uint64_t*>(smem) + 512 + 4 * 64 * E;
   group_topk<E>(key, k, smem, out);
@@ -272,12 +333,24 @@ __global__ __launch_bounds__(kWG) void wtopk_final_kernel(const float* __restric
   const float* row = logits + (int64_t)m * ldl;
   const int base = (threadIdx.x >> 6) * 64 * E + (threadIdx.x & 63);
   uint64_t key[E];
+  if (cand) {  // all loads first: clamped, unconditional, so none waits for another
+    uint64_t cv[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int i = base + e * 64;
-    uint64_t kk = pad_key(~(uint32_t)i & 0x7fffffffu);
-    if (i < ncand) kk = cand ? cand[(int64_t)m * ncand + i] : make_key(row[i], (uint32_t)i);
-    key[e] = kk;
+    for (int e = 0; e < E; ++e) cv[e] = cand[(int64_t)m * ncand + min(base + e * 64, ncand - 1)];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int i = base + e * 64;
+      key[e] = i < ncand ? cv[e] : pad_key(~(uint32_t)i & 0x7fffffffu);
+    }
+  } else {
+    float lv[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) lv[e] = row[min(base + e * 64, ncand - 1)];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int i = base + e * 64;
+      key[e] = i < ncand ? make_key(lv[e], (uint32_t)i) : pad_key(~(uint32_t)i & 0x7fffffffu);
+    }
   }
   uint64_t* out = reinterpret_cast<uint64_t*>(smem) + 512 + 4 * 64 * E;
   group_topk<E>(key, k, smem, out);
