@@ -204,8 +204,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs g) {
 // the register-staged kernel above.
 constexpr int DBK = 32;
 constexpr int DSTAGES = 4;
-constexpr int DSTAGE_BYTES = (BM + BN) * DBK * 2;      // 32 KB
-constexpr size_t kDmaLds = (size_t)DSTAGES * DSTAGE_BYTES;
+constexpr size_t dma_lds(int bm) { return (size_t)DSTAGES * (bm + BN) * DBK * 2; }  // 128 / 144 KB
 constexpr int kDmaWaves = 8;  // waves per workgroup (4 also builds: one per SIMD, 128 x 128)
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -243,26 +242,34 @@ __device__ __forceinline__ int b_swz(int k) {
 
 // W4_SYNC with a wave-uniform count of DMA instructions allowed to stay in flight
 __device__ __forceinline__ void dma_sync(int n) {
-  switch (n) {
+  switch (n) {  // per-wave instructions per K-tile (4 or 5) times 0 .. 3 K-tiles
     case 24: W4_SYNC(24); break;
     case 16: W4_SYNC(16); break;
+    case 15: W4_SYNC(15); break;
     case 12: W4_SYNC(12); break;
+    case 10: W4_SYNC(10); break;
     case 8: W4_SYNC(8); break;
+    case 5: W4_SYNC(5); break;
     case 4: W4_SYNC(4); break;
     default: W4_SYNC(0); break;
   }
 }
 
-template <int NW>
+template <int NW, int BMT>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_dma_kernel(GemmArgs g) {
-  constexpr int WN = NW / 2;    // waves along N (two along M)
-  constexpr int WTN = BN / WN;  // columns per wave
-  constexpr int NJ = WTN / 32;  // 32-column MFMA blocks per wave
-  constexpr int DI = 16 / NW;   // A and B DMA instructions per wave and K-tile (each)
+  constexpr int WN = NW / 2;            // waves along N (two along M)
+  constexpr int WTN = BN / WN;          // columns per wave
+  constexpr int NJ = WTN / 32;          // 32-column MFMA blocks per wave
+  constexpr int WTM = BMT / 2;          // rows per wave
+  constexpr int MI = WTM / 32;          // 32-row MFMA blocks per wave
+  constexpr int DI = 16 / NW;           // B DMA instructions per wave and K-tile
+  constexpr int AI = BMT / 16;          // A DMA instructions per K-tile (16 rows each)
+  constexpr int AW = (AI + NW - 1) / NW;  // A DMA instructions per wave, at most
+  constexpr int STAGE = (BMT + BN) * DBK * 2;
   extern __shared__ __align__(16) unsigned char dlds[];
   int tm, tn, split;
   tile_of(g, blockIdx.x, tm, tn, split);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * BMT, n0 = tn * BN;
   const int kbeg = split * g.kslice;
   const int kend = min(g.K, kbeg + g.kslice);
   const int nk = (kend - kbeg) / DBK;
@@ -270,42 +277,47 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_dma_kernel(GemmArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
-  // DMA source addresses (this lane, K-tile 0): wave w issues A and B instructions
-  // DI*w .. DI*w + DI - 1 of the 16 each
-  const uint16_t* a_src[DI];
+  // DMA source addresses (this lane, K-tile 0): wave w issues A instructions w, w + NW, ...
+  // (below AI; na of them, wave-uniform) and B instructions DI*w .. DI*w + DI - 1 of 16
+  const int na = (AI - wave + NW - 1) / NW;
+  const int per_tile = na + DI;  // this wave's DMA instructions per K-tile
+  const uint16_t* a_src[AW];
   const uint16_t* b_src[DI];
+#pragma unroll
+  for (int ta = 0; ta < AW; ++ta) {
+    const int i = min(wave + NW * ta, AI - 1);
+    const int row = 16 * i + (lane >> 2);
+    const int ca = (lane & 3) ^ a_swz(row);
+    a_src[ta] = g.A + (int64_t)min(m0 + row, g.M - 1) * g.lda + kbeg + ca * 8;
+  }
 #pragma unroll
   for (int ii = 0; ii < DI; ++ii) {
     const int i = wave * DI + ii;
-    const int row = 16 * i + (lane >> 2);
-    const int ca = (lane & 3) ^ a_swz(row);
-    a_src[ii] = g.A + (int64_t)min(m0 + row, g.M - 1) * g.lda + kbeg + ca * 8;
     const int krow = 2 * i + (lane >> 5);
     const int cb = (lane & 31) ^ b_swz(krow);
     b_src[ii] = g.B + (int64_t)(kbeg + krow) * g.ldb + min(n0 + cb * 8, g.N - 8);
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t*)dlds;
   auto issue = [&](int t) {
-    const uint32_t st = lds_base + (uint32_t)((t % DSTAGES) * DSTAGE_BYTES);
+    const uint32_t st = lds_base + (uint32_t)((t % DSTAGES) * STAGE);
 #pragma unroll
-    for (int ii = 0; ii < DI; ++ii)
-      dma16(a_src[ii] + t * DBK, st + (uint32_t)((wave * DI + ii) * 1024));
+    for (int ta = 0; ta < AW; ++ta)
+      if (ta < na) dma16(a_src[ta] + t * DBK, st + (uint32_t)((wave + NW * ta) * 1024));
 #pragma unroll
     for (int ii = 0; ii < DI; ++ii)
       dma16(b_src[ii] + (int64_t)t * DBK * g.ldb,
-            st + (uint32_t)(BM * DBK * 2 + (wave * DI + ii) * 1024));
+            st + (uint32_t)(BMT * DBK * 2 + (wave * DI + ii) * 1024));
   };
 
   // per-lane LDS read offsets (bytes within a stage)
-  int a_off[4][2];
+  // a_swz depends on row bits 1..4 only, so the row blocks mi differ by a constant 2 KB
+  int a_off[2];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int r = wm * 128 + mi * 32 + (lane & 31);
-      const int c = 2 * ks + (lane >> 5);
-      a_off[mi][ks] = r * 64 + ((c ^ a_swz(r)) * 16);
-    }
+  for (int ks = 0; ks < 2; ++ks) {
+    const int r = wm * WTM + (lane & 31);
+    const int c = 2 * ks + (lane >> 5);
+    a_off[ks] = r * 64 + ((c ^ a_swz(r)) * 16);
+  }
   int b_off[NJ][2][2];
   {
     const int grp = lane >> 4, L = lane & 15;
@@ -318,13 +330,13 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_dma_kernel(GemmArgs g) {
           const int krow = 16 * ks + 8 * (grp >> 1) + 4 * h + (L >> 2);
           const int ncol = wn * WTN + nj * 32 + (grp & 1) * 16 + 4 * (L & 3);
           const int c = ncol >> 3;
-          b_off[nj][ks][h] = BM * DBK * 2 + krow * 512 + ((c ^ b_swz(krow)) * 16) + (L & 1) * 8;
+          b_off[nj][ks][h] = BMT * DBK * 2 + krow * 512 + ((c ^ b_swz(krow)) * 16) + (L & 1) * 8;
         }
   }
 
-  f32x16 acc[4][NJ];
+  f32x16 acc[MI][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -334,11 +346,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_dma_kernel(GemmArgs g) {
   // transposing b64 reads each).  Two sets alternate so that the reads of the next k-step
   // are in flight while the 16 MFMAs of the current one run.
   struct Frag {
-    f16x8 a[4], b[NJ];
+    f16x8 a[MI], b[NJ];
   };
   auto load = [&](const unsigned char* st, int ks, Frag& f) {
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) f.a[mi] = *reinterpret_cast<const f16x8*>(st + a_off[mi][ks]);
+    for (int mi = 0; mi < MI; ++mi) f.a[mi] = *reinterpret_cast<const f16x8*>(st + a_off[ks] + mi * 2048);
 #pragma unroll
     for (int nj = 0; nj < NJ; ++nj) {
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -350,14 +362,14 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_dma_kernel(GemmArgs g) {
   };
   auto mma = [&](const Frag& f) {
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int nj = 0; nj < NJ; ++nj)
         acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[mi], f.b[nj], acc[mi][nj], 0, 0, 0);
   };
-  // the 4 + 2 * NJ LDS reads of the next fragments interleaved one-to-one with the first of
-  // the 4 * NJ MFMAs
-  constexpr int RD = 4 + 2 * NJ, MF = 4 * NJ;
+  // the MI + 2 * NJ LDS reads of the next fragments interleaved one-to-one with the first
+  // of the MI * NJ MFMAs
+  constexpr int RD = MI + 2 * NJ, MF = MI * NJ;
   auto interleave = [&]() {
 #pragma unroll
     for (int i = 0; i < RD; ++i) {
@@ -374,22 +386,22 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_dma_kernel(GemmArgs g) {
   // of tile t.
   const int pre = min(DSTAGES, nk);
   for (int t = 0; t < pre; ++t) issue(t);
-  dma_sync((pre - 1) * 2 * DI);  // tile 0 landed; tiles 1 .. pre-1 may be in flight
+  dma_sync((pre - 1) * per_tile);  // tile 0 landed; tiles 1 .. pre-1 may be in flight
   Frag f0, f1;
   load(dlds, 0, f0);
   for (int t = 0; t + 1 < nk; ++t) {
-    load(dlds + (t % DSTAGES) * DSTAGE_BYTES, 1, f1);
+    load(dlds + (t % DSTAGES) * STAGE, 1, f1);
     mma(f0);
     interleave();
     __builtin_amdgcn_sched_barrier(0);
-    dma_sync(min(2, nk - 2 - t) * 2 * DI);  // tiles after t + 1 already issued may fly
+    dma_sync(min(2, nk - 2 - t) * per_tile);  // tiles after t + 1 already issued may fly
     if (t + DSTAGES < nk) issue(t + DSTAGES);
-    load(dlds + ((t + 1) % DSTAGES) * DSTAGE_BYTES, 0, f0);
+    load(dlds + ((t + 1) % DSTAGES) * STAGE, 0, f0);
     mma(f1);
     interleave();
     __builtin_amdgcn_sched_barrier(0);
   }
-  load(dlds + ((nk - 1) % DSTAGES) * DSTAGE_BYTES, 1, f1);
+  load(dlds + ((nk - 1) % DSTAGES) * STAGE, 1, f1);
   mma(f0);
   interleave();
   __builtin_amdgcn_sched_barrier(0);
@@ -398,13 +410,13 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_dma_kernel(GemmArgs g) {
   float* out = g.ksplit == 1 ? g.C : g.ws + (int64_t)split * g.M * g.N;
   const int64_t ldo = g.ksplit == 1 ? g.ldc : g.N;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int col = n0 + wn * WTN + j * 32 + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int row = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
         if (row < g.M && col < g.N) out[(int64_t)row * ldo + col] = acc[i][j][r];
       }
     }
@@ -424,12 +436,13 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 }
 
 struct GemmPlan {
-  int tilesM, tilesN, ksplit, kslice;
+  int tilesM, tilesN, ksplit, kslice, bm;
 };
 
-GemmPlan plan_mfma(int64_t M, int64_t N, int64_t K) {
+GemmPlan plan_mfma(int64_t M, int64_t N, int64_t K, int bm) {
   GemmPlan p;
-  p.tilesM = (int)((M + BM - 1) / BM);
+  p.bm = bm;
+  p.tilesM = (int)((M + bm - 1) / bm);
   p.tilesN = (int)((N + BN - 1) / BN);
   const int tiles = p.tilesM * p.tilesN;
   const int kt = (int)((K + BK - 1) / BK);
@@ -442,6 +455,20 @@ GemmPlan plan_mfma(int64_t M, int64_t N, int64_t K) {
   return p;
 }
 
+// The LDS-DMA kernel (K % 32 == 0) takes 256- or 320-row tiles, whichever gives the shorter
+// critical path: rounds of workgroups over 256 CUs times the work of one (rows x K-slice).
+// 1570-row prefills take 320 (5 row tiles instead of 7, 2 rounds instead of 3 for 22016
+// columns); the register-staged kernel has 256-row tiles only.
+GemmPlan choose_plan(int64_t M, int64_t N, int64_t K) {
+  const GemmPlan p256 = plan_mfma(M, N, K, 256);
+  if (K % DBK != 0) return p256;
+  const GemmPlan p320 = plan_mfma(M, N, K, 320);
+  auto cost = [](const GemmPlan& p) {
+    const int64_t wgs = (int64_t)p.tilesM * p.tilesN * p.ksplit;
+    return ((wgs + 255) / 256) * (int64_t)p.bm * p.kslice;
+  };
+  return cost(p320) < cost(p256) ? p320 : p256;
+}
 __device__ __forceinline__ uint32_t half_of(uint4 v, int j) {
   const uint32_t d = dword_of(v, j >> 1);
   return (j & 1) ? (d >> 16) : (d & 0xFFFFu);
@@ -552,7 +579,7 @@ __global__ __launch_bounds__(256) void gemm_plain_kernel(const uint16_t* __restr
 size_t gemm_ws_bytes(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M,
                      int64_t N, int64_t K) {
   if (gemm_path(A, lda, B, ldb, M, N, K) != kGemmMfma) return 0;
-  const GemmPlan p = plan_mfma(M, N, K);
+  const GemmPlan p = choose_plan(M, N, K);
   return p.ksplit > 1 ? (size_t)p.ksplit * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
@@ -572,15 +599,19 @@ void launch_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
       std::call_once(lds_attr, [] {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_mfma_kernel),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_dma_kernel<kDmaWaves>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDmaLds);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_dma_kernel<kDmaWaves, 256>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)dma_lds(256));
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_dma_kernel<kDmaWaves, 320>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)dma_lds(320));
       });
-      const GemmPlan p = plan_mfma(M, N, K);
+      const GemmPlan p = choose_plan(M, N, K);
       GemmArgs g{A, B, C, reinterpret_cast<float*>(ws), lda, ldb, ldc, M, N, K,
                  p.tilesM, p.tilesN, p.ksplit, p.kslice};
       const dim3 grid((unsigned)(p.tilesM * p.tilesN * p.ksplit));
-      if (K % DBK == 0)
-        hipLaunchKernelGGL(gemm_dma_kernel<kDmaWaves>, grid, dim3(64 * kDmaWaves), kDmaLds, st, g);
+      if (K % DBK == 0 && p.bm == 320)
+        hipLaunchKernelGGL((gemm_dma_kernel<kDmaWaves, 320>), grid, dim3(64 * kDmaWaves), dma_lds(320), st, g);
+      else if (K % DBK == 0)
+        hipLaunchKernelGGL((gemm_dma_kernel<kDmaWaves, 256>), grid, dim3(64 * kDmaWaves), dma_lds(256), st, g);
       else
         hipLaunchKernelGGL(gemm_mfma_kernel, grid, dim3(256), kGemmLds, st, g);
       if (p.ksplit > 1) {

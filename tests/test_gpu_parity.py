@@ -308,6 +308,23 @@ def test_gemm_prefill_sampled_rows(w4):
     assert ok, worst
 
 
+@pytest.mark.parametrize("m,n,k,sampled", [
+    (600, 25608, 64, False),    # 320-row tiles (2 row tiles instead of 3), ragged M and N
+    (600, 11000, 2048, True),   # 320-row tiles with K split in two, ragged N
+])
+def test_gemm_tall_tiles(w4, m, n, k, sampled):
+    a = synth.activations(m, k, seed=m + n)
+    bmat = synth.activations(k, n, seed=k + 1)
+    c = to_np(w4.gemm_f16(dev(a), dev(bmat)))
+    rows = np.arange(m)
+    if sampled:
+        rows = np.unique(np.concatenate([np.random.default_rng(m).choice(576, 40, replace=False),
+                                         np.arange(576, m)]))
+    c_ref, bound = oracle.gemm_ref(a[rows], bmat)
+    ok, worst = oracle.check_bound(c[rows], c_ref, bound, RTOL)
+    assert ok, worst
+
+
 def test_gemm_deterministic(w4):
     a = dev(synth.activations(300, 512, seed=7))
     b = dev(synth.activations(512, 1024, seed=8))
