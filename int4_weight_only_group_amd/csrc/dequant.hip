@@ -44,8 +44,15 @@ __global__ __launch_bounds__(256) void dequant_t_kernel(const uint32_t* __restri
                                                         int N, int K, bool vec) {
   __shared__ __align__(16) unsigned char t[TK * PITCH];
   __shared__ uint16_t ss[TN][TK / kGroup], bs[TN][TK / kGroup];
-  const int n0 = blockIdx.y * TN;
-  const int k0 = blockIdx.x * TK;
+  // Workgroups are dealt round-robin to the 8 XCDs; all K-tiles of a 64-row block get the
+  // same XCD and run back to back there, so the block's scale and bias lines (shared by its
+  // K-tiles, 8 bytes of each row per tile) are fetched once into that XCD's L2.
+  const int KT = (K + TK - 1) / TK, RB = (N + TN - 1) / TN;
+  const int xcd = blockIdx.x % 8, idx = blockIdx.x / 8;
+  const int rb = xcd + 8 * (idx / KT), kt = idx % KT;
+  if (rb >= RB) return;  // padding of the last group of eight row blocks (whole workgroup)
+  const int n0 = rb * TN;
+  const int k0 = kt * TK;
   const int tid = threadIdx.x;
   const int G = K / kGroup;
 
@@ -139,7 +146,8 @@ __global__ __launch_bounds__(256) void dequant_t_kernel(const uint32_t* __restri
 
 void launch_dequant_t(const uint32_t* qw, const uint16_t* s, const uint16_t* b, uint16_t* wt,
                       int64_t ldwt, int N, int K, hipStream_t st) {
-  const dim3 grid((unsigned)((K + TK - 1) / TK), (unsigned)((N + TN - 1) / TN));
+  const int KT = (K + TK - 1) / TK, RB = (N + TN - 1) / TN;
+  const dim3 grid((unsigned)(8 * ((RB + 7) / 8) * KT));  // see the XCD mapping in the kernel
   // 16-byte stores need every output row to start 16-byte aligned
   const bool vec = ldwt % 8 == 0 && ((uintptr_t)wt & 15u) == 0;
   hipLaunchKernelGGL(dequant_t_kernel, grid, dim3(256), 0, st, qw, s, b, wt, ldwt, N, K, vec);
