@@ -24,6 +24,8 @@
 //    each output within 2e-3 * sum_k |w x| (and exactly 0 when every w x is 0), at 17 VALU
 //    operations per 8 weights, shared by all M activation rows except the 4 dot products.
 //  * Each team reduces its lanes with cross-lane shuffles; one lane stores y.
+//  * From M = 3 rows of x on, the dequantized words feed the matrix cores instead
+//    (gemv_mf_kernel below): the dequant is then the only VALU work per weight.
 #include "w4_internal.h"
 
 namespace w4 {
@@ -446,6 +448,189 @@ void launch_p(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const ui
     launch_r<MT, 64>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
 }
 
+// ------------------------------------------------------------------ 2 <= M <= 16 on MFMA
+// With several activation rows the VALU kernel spends 4 dot products per word and row on
+// top of the 13-operation dequant, so at M = 16 the arithmetic, not HBM, sets its speed.
+// Here the dequantized weights feed v_mfma_f32_16x16x32_f16 instead: D[n][m] += W[n][k] x[m][k]
+// over 16 weight rows n (A operand) and up to 16 activation rows m (B operand), so the only
+// per-row VALU work left is the dequant, shared by every m.
+//
+// Lane l = (i = l % 16, g = l / 16) of a wave holds A row i and B column i, k-group g.  At step
+// t it loads the 16-byte chunk c = 4t + g of weight row 16*rb + i (so a load instruction reads
+// 64 contiguous bytes of each of 16 rows) and the same 32 elements of x row min(i, M - 1).  Word
+// j of the chunk dequantizes into one A operand whose 8 f16 sit in the order the nibbles come
+// out of the word, (q0,q4) (q1,q5) (q2,q6) (q3,q7); the B operand holds the x pairs in that same
+// order, so every product pairs a weight with its own x whatever order the matrix core sums
+// the 32 products in.  D column i, rows 4g..4g+3 come back in the lane's 4 accumulators;
+// columns i >= M are computed on a duplicate x row and never stored.
+//
+// A wave streams RB row blocks (16 RB rows) over one K-range: the NW waves of a workgroup split
+// the steps of the same row blocks and their partial sums are added in LDS in wave order
+// (deterministic).  Loads are unconditional and clamped (steps past the wave's range or chunks
+// past the row end read a valid address, their scale and bias are zeroed so their weights are
+// exactly 0) and run in two ping-pong blocks of V steps, as in the M = 1 kernel.
+
+// (x0x1, x2x3, x4x5, x6x7) -> (x0x4, x1x5, x2x6, x3x7) with byte permutes
+__device__ __forceinline__ uint4 pair_up_perm(uint4 d) {
+  uint4 p;
+  p.x = __builtin_amdgcn_perm(d.z, d.x, 0x05040100u);
+  p.y = __builtin_amdgcn_perm(d.z, d.x, 0x07060302u);
+  p.z = __builtin_amdgcn_perm(d.w, d.y, 0x05040100u);
+  p.w = __builtin_amdgcn_perm(d.w, d.y, 0x07060302u);
+  return p;
+}
+
+// The 8 weights of word w (f16, nibble order) as an MFMA operand.
+__device__ __forceinline__ f16x8 word_operand(uint32_t w, h2 s2, h2 b2, const Consts& k) {
+  const uint32_t w8 = w >> 8;
+  const h2 o1024 = {(f16)1024.0f, (f16)1024.0f}, o64 = {(f16)64.0f, (f16)64.0f};
+  const h2 q0 = as_h2(and_or(w, k.m_lo, k.mag_lo)) - o1024;   // exact
+  const h2 q1 = as_h2(and_or(w, k.m_hi, k.mag_hi)) - o64;
+  const h2 q2 = as_h2(and_or(w8, k.m_lo, k.mag_lo)) - o1024;
+  const h2 q3 = as_h2(and_or(w8, k.m_hi, k.mag_hi)) - o64;
+  const h2 r0 = __builtin_elementwise_fma(q0, s2, b2);         // one rounding each
+  const h2 r1 = __builtin_elementwise_fma(q1, s2, b2);
+  const h2 r2 = __builtin_elementwise_fma(q2, s2, b2);
+  const h2 r3 = __builtin_elementwise_fma(q3, s2, b2);
+  return __builtin_bit_cast(f16x8, make_uint4(as_u32(r0), as_u32(r1), as_u32(r2), as_u32(r3)));
+}
+
+__device__ __forceinline__ f16x8 as_operand(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_bit_cast(f16x8, make_uint4(a, b, c, d));
+}
+
+template <int RB, int V>
+struct MfBlock {
+  uint4 w[V][RB];
+  uint32_t s[V][RB], b[V][RB];  // f16 bits in the low half
+  uint4 x[V][4];                // raw x, 32 elements of this lane's chunk
+};
+
+template <int NW, int RB, int V>
+__global__ __launch_bounds__(NW * 64) void gemv_mf_kernel(const uint32_t* __restrict__ qw,
+                                                          const uint16_t* __restrict__ sc,
+                                                          const uint16_t* __restrict__ bi,
+                                                          const uint16_t* __restrict__ x,
+                                                          int64_t ldx, float* __restrict__ y,
+                                                          int64_t ldy, int M, int N, int K,
+                                                          int U) {
+  __shared__ f32x4 red[NW][RB][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int C = K / 32, G = K / kGroup, T = (C + 3) / 4;
+  const int rb0 = blockIdx.x * RB;
+  const int t0 = wv * U, tend = min(T, t0 + U);
+  const int nb = (U + V - 1) / V;  // blocks per wave, the same for every wave
+
+  const uint4* wrow[RB];
+  const uint16_t* srow[RB];
+  const uint16_t* brow[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const int n = min(16 * (rb0 + r) + i, N - 1);  // tail rows reload the last row, never stored
+    wrow[r] = reinterpret_cast<const uint4*>(qw) + (int64_t)n * C;
+    srow[r] = sc + (int64_t)n * G;
+    brow[r] = bi + (int64_t)n * G;
+  }
+  const uint4* xrow = reinterpret_cast<const uint4*>(x + (int64_t)min(i, M - 1) * ldx);
+
+  auto chunk = [&](int t) { return min(4 * min(t, T - 1) + g, C - 1); };
+  auto valid = [&](int t) { return t < tend && 4 * t + g < C; };
+  auto load = [&](int blk, MfBlock<RB, V>& B) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int c = chunk(t0 + blk * V + v);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) B.x[v][j] = xrow[c * 4 + j];
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        B.w[v][r] = load_nt(wrow[r] + c);
+        B.s[v][r] = srow[r][c >> 1];
+        B.b[v][r] = brow[r][c >> 1];
+      }
+    }
+  };
+
+  Consts k;
+  k.m_lo = __builtin_amdgcn_readfirstlane(0x000F000Fu);
+  k.m_hi = __builtin_amdgcn_readfirstlane(0x00F000F0u);
+  k.mag_lo = __builtin_amdgcn_readfirstlane(0x64006400u);
+  k.mag_hi = __builtin_amdgcn_readfirstlane(0x54005400u);
+
+  f32x4 acc[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int blk, const MfBlock<RB, V>& B) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const uint32_t sb_on = valid(t0 + blk * V + v) ? 0xFFFFu : 0u;
+      uint4 xp[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xp[j] = pair_up_perm(B.x[v][j]);
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        const f16 sv = __builtin_bit_cast(f16, (uint16_t)(B.s[v][r] & sb_on));
+        const f16 bv = __builtin_bit_cast(f16, (uint16_t)(B.b[v][r] & sb_on));
+        const h2 s2 = {sv, sv}, b2 = {bv, bv};
+        const uint32_t wd[4] = {B.w[v][r].x, B.w[v][r].y, B.w[v][r].z, B.w[v][r].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              word_operand(wd[j], s2, b2, k), as_operand(xp[j].x, xp[j].y, xp[j].z, xp[j].w),
+              acc[r], 0, 0, 0);
+      }
+    }
+  };
+
+  MfBlock<RB, V> A, B;
+  load(0, A);
+  __builtin_amdgcn_sched_barrier(0);
+  int bk = 0;
+  for (; bk + 2 < nb; bk += 2) {
+    load(bk + 1, B);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(bk, A);
+    load(bk + 2, A);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(bk + 1, B);
+  }
+  if (nb - bk == 2) {
+    load(bk + 1, B);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(bk, A);
+    compute(bk + 1, B);
+  } else {
+    compute(bk, A);
+  }
+
+  // ---- add the NW partial sums in wave order and store: output (r, m, g, e) is row
+  // n = 16 (rb0 + r) + 4 g + e, column m, held by lane 16 g + m of every wave
+#pragma unroll
+  for (int r = 0; r < RB; ++r) red[wv][r][lane] = acc[r];
+  __syncthreads();
+  for (int o = threadIdx.x; o < RB * 256; o += NW * 64) {
+    const int e = o & 3, gg = (o >> 2) & 3, m = (o >> 4) & 15, r = o >> 8;
+    const int n = 16 * (rb0 + r) + 4 * gg + e;
+    if (m < M && n < N) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) sum += red[w][r][16 * gg + m][e];
+      y[(int64_t)m * ldy + n] = sum;
+    }
+  }
+}
+
+template <int NW, int RB, int V>
+void launch_mf(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
+               int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
+  const int T = (K / 32 + 3) / 4;            // steps of 4 chunks (128 elements) per row
+  const int U = (T + NW - 1) / NW;           // steps per wave
+  const int grid = ((N + 15) / 16 + RB - 1) / RB;
+  hipLaunchKernelGGL((gemv_mf_kernel<NW, RB, V>), dim3(grid), dim3(NW * 64), 0, st, qw, s, b, x,
+                     ldx, y, ldy, M, N, K, U);
+}
+
 // M = 1 policy (K / 32 = C chunks per row), measured on MI355X with back-to-back graph
 // launches on distinct weights: rows of 2048 take one 64-lane wave per row, two rows per
 // wave and two blocks per team once N is large; rows up to 6144 keep x in registers; longer
@@ -480,19 +665,33 @@ bool launch_gemv_m1(const uint32_t* qw, const uint16_t* s, const uint16_t* b, co
 
 }  // namespace
 
+// 3 <= M <= 16 policy, measured on MI355X (back-to-back graph launches on distinct weights):
+// four row blocks per wave once there are >= 768 of them, two from 384, otherwise one with
+// eight waves splitting K when rows are long.  At M = 2 the VALU kernel is still ahead.
+void launch_gemv_mf(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
+                    int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
+  const int nrb = (N + 15) / 16;
+  if (nrb >= 768)
+    launch_mf<8, 4, 1>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+  else if (nrb >= 384)
+    launch_mf<8, 2, 1>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+  else if (K >= 8192)
+    launch_mf<8, 1, 1>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+  else
+    launch_mf<4, 1, 1>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+}
+
 void launch_gemv(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
                  int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
   if (M <= 1 && launch_gemv_m1(qw, s, b, x, y, N, K, st)) return;
+  if (M >= 3) {
+    launch_gemv_mf(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+    return;
+  }
   if (M <= 1)
     launch_p<1>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
-  else if (M <= 2)
-    launch_p<2>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
-  else if (M <= 4)
-    launch_p<4>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
-  else if (M <= 8)
-    launch_p<8>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
   else
-    launch_p<16>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+    launch_p<2>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
 }
 
 }  // namespace w4

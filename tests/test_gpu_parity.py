@@ -163,6 +163,15 @@ def test_gemv_workload_shapes_full(w4, m, n, k):
     gemv_case(w4, m, n, k, seed=n * 7 + k + m)
 
 
+@pytest.mark.parametrize("m", [3, 16])
+@pytest.mark.parametrize("n,k", [(12290, 320), (6150, 448), (100, 8256), (17, 64), (383 * 16 + 1, 192)])
+def test_gemv_matrix_core_edges(w4, m, n, k):
+    # from three rows of x on, the GEMV runs on matrix cores in 16-row blocks grouped by 1, 2 or
+    # 4 per wave; these shapes leave the last group partly filled in each grouping, end rows on
+    # a half step (K % 128 == 64) and give some waves of the K split no step at all
+    gemv_case(w4, m, n, k, seed=31 * n + k + m, ldx_pad=8 * (m % 2), ldy_pad=m % 5)
+
+
 def test_gemv_deterministic(w4):
     q, s, b = synth.w4_weights(2048, 2048, seed=9)
     x = synth.activations(3, 2048, seed=9)
