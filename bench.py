@@ -48,6 +48,7 @@ def parse_args():
     p.add_argument("--unfused", action="store_true", help="run q,k,v and gate,up as separate GEMVs (7 per layer)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-check", action="store_true", help="skip the parity re-check of the timed outputs")
+    p.add_argument("--no-small-m", action="store_true", help="skip the batched (M = 16, 8) and Gemma-shaped GEMVs")
     p.add_argument("--counters", metavar="MANIFEST",
                    help="counter-collection pass: launch each kernel shape of the step 3 times (eagerly, between "
                         "marker kernels) plus a copy of known size, write the launch plan to MANIFEST and exit; "
@@ -414,6 +415,68 @@ def parity_check(torch, np, wl, oracle, synth):
     return res
 
 
+# Batched-decode GEMVs at several activation rows: the batched classify decode (M = 16,
+# Qwen3-1.7B shapes) and the Gemma-12B-shaped layer at M = 8 and M = 1.  Matrices that read
+# the same activations run row-concatenated, as in the decode step.  Each shape is timed
+# over `copies` distinct copies of its weights (together larger than the 256 MB MALL).
+SMALL_M = (("qwen3-1.7b classify", "CLASSIFY_ROWS", "QWEN3_1P7B_CLASSIFY", "W_CLASSIFY",
+            [["q", "k", "v"], ["gate", "up"], ["down"]], 40),
+           ("gemma-12b layer", 8, "GEMMA12B_LAYER", "W_GEMMA", [["gate", "up"], ["down"], ["q"]], 10),
+           ("gemma-12b layer", 1, "GEMMA12B_LAYER", "W_GEMMA", [["gate", "up"], ["down"], ["q"]], 10))
+
+
+def small_m(torch, np, w4, synth, oracle, reps=5):
+    """Per-shape device time (graph of `copies` back-to-back launches on distinct weights),
+    GB/s against HBM peak, and a parity re-check of the last launch on 64 sampled rows."""
+    rng = np.random.default_rng(321)
+    out = []
+    for cfg, (label, m, layer_name, wname, groups, copies) in enumerate(SMALL_M):
+        m = getattr(synth, m) if isinstance(m, str) else m
+        wk = getattr(synth, wname)
+        shapes = {name: (j, n, k) for j, (name, n, k) in enumerate(getattr(synth, layer_name))}
+        rows_out = []
+        tot_b = tot_us = 0.0
+        worst = 0.0
+        ok = True
+        for grp in groups:
+            parts = [synth.w4_weights(shapes[g][1], shapes[g][2], seed=0, workload=wk,
+                                      layer=100 * cfg + shapes[g][0]) for g in grp]
+            q, s, b = (np.concatenate([p[i] for p in parts]) for i in range(3))
+            n, k = q.shape
+            x_host = synth.activations(m, k, seed=0, workload=wk, layer=100 * cfg + 50 + shapes[grp[0]][0])
+            qw0 = w4.w4_pack(torch.from_numpy(q).cuda())
+            s0, b0 = torch.from_numpy(s).cuda(), torch.from_numpy(b).cuda()
+            mats = [(qw0, s0, b0)] + [(qw0.clone(), s0.clone(), b0.clone()) for _ in range(copies - 1)]
+            x = torch.from_numpy(x_host).cuda()
+            y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+            fns = [lambda t=t: w4.w4_gemv(t[0], t[1], t[2], x, out=y) for t in mats]
+            graph = capture(torch, lambda: [f() for f in fns])
+            graph.replay()
+            stream = torch.cuda.current_stream()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+            nb = gemv_bytes(m, n, k)
+            sel = np.sort(rng.choice(n, min(n, 64), replace=False))
+            y_ref, bound = oracle.gemv_ref(oracle.pack(q[sel]), s[sel], b[sel], x_host)
+            okc, wr = oracle.check_bound(y.cpu().numpy()[:, sel], y_ref, bound)
+            ok &= okc
+            worst = max(worst, wr)
+            rows_out.append({"matrix": "|".join(grp), "M": m, "N": n, "K": k, "avg_us": round(us, 3),
+                             "gbps": round(nb / us / 1e3, 1), "frac_hbm": round(nb / us / 1e3 / HBM_PEAK_GBS, 4)})
+            tot_b += nb
+            tot_us += us
+            del mats, fns, graph
+        out.append({"workload": f"{label} at M={m}", "gemvs": rows_out, "gbps": round(tot_b / tot_us / 1e3, 1),
+                    "frac_hbm": round(tot_b / tot_us / 1e3 / HBM_PEAK_GBS, 4), "parity_ok": bool(ok),
+                    "worst_err_over_bound": worst, "copies": copies})
+    return out
+
+
 def cpu_baseline(np, oracle, synth):
     """The oracle's GEMV (unpack + exact dequant + fp64 product) over the seven matrices of as
     many decoder layers as take about 10 s, at M = 1, on this host's cores."""
@@ -520,6 +583,13 @@ def main():
                         "frac": g_fl / g_us / 1e6 / MFMA_F16_PEAK_TFLOPS,
                         "traffic": traffic_for("gemm.hip", "gemm_f16_prefill"), "avg_launch_us": g_us / len(gk)}
 
+    sm = None
+    if not args.no_small_m:
+        import oracle
+        t0 = time.time()
+        sm = small_m(torch, np, w4, synth, oracle)
+        log(f"small-M GEMVs in {time.time() - t0:.1f}s: " + "; ".join(f"{c['workload']} {c['gbps']} GB/s" for c in sm))
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -564,7 +634,11 @@ def main():
                     for k, v in kt.items()},
         "cpu_baseline": cpu,
         "parity": check,
+        "small_m": sm,
     }
+    if sm is not None and not all(c["parity_ok"] for c in sm):
+        check = dict(check or {}, ok=False, small_m_fail=True)
+        out["parity"] = check
     if check is not None and not check["ok"]:
         out["value"] = None
         out["error"] = "parity re-check failed"
