@@ -16,6 +16,7 @@ Sources (page title, then section):
         bit-exact against a host reference; the LM head that streamed
         bf16 weights of shape [2048 x 151936].
       - "Appendix: the remaining gap, itemized": MLX's affine 4-bit format.
+      - "Where it fits": weights quantized to int4 at load (the quantizer).
   * "Engineering investigation: can this MLX port become another 10x faster?"
       - "Selective quantization ...": affine quantization with group size 64.
   * "engine-mlx", "Tech details": in-graph greedy argmax.
@@ -42,6 +43,8 @@ from .w4ref import (  # noqa: F401
     f16_value,
     dequant_exact,
     dequant_f16_t,
+    quantize,
+    quantize_loop,
     gemv_ref,
     gemm_ref,
     topk_ref,

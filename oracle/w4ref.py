@@ -19,6 +19,11 @@ functions follow the order in which the pages describe the path:
   topk_ref       -- greedy / top-k token selection on the logits ("Crossing Mojo
                     1.0"; "What's inside the engine today": bit-exact against a host
                     reference; "engine-mlx", "Tech details": in-graph greedy argmax).
+  quantize       -- the load-time step that turns float weights into the int4
+                    affine format ("The inference engine -- Mojo 1.0 on Metal",
+                    "Where it fits": weights quantized to int4 at load;
+                    "Engineering investigation ...", "Selective quantization ...":
+                    affine, group size 64).
 
 Readings taken where the pages are silent (each is listed in the design notes):
   * layout: q codes row-major [N][K]; packed words [N][K/8], K contiguous; s and b
@@ -32,6 +37,11 @@ Readings taken where the pages are silent (each is listed in the design notes):
     are its actual operands.
   * top-k order: value descending, ties to the lower index, -0.0 equal to +0.0;
     logits must be finite.
+  * quantizer (the pages give no formula): per group of 64 the plain min/max affine
+    fit -- b = min, s = RN16((max - min) / 15), q = clamp(rint_even((w - b) / s), 0, 15),
+    q = 0 where s rounds to 0; a zero min or max counts as +0.  Every step that decides
+    a code is f32 arithmetic (correctly rounded), the precision the GPU kernel decides
+    in, so codes compare bit for bit.  This is the one place the oracle computes in f32.
   * tolerance: |y - y_ref| <= 2e-3 * sum_k |w_k x_k| per output; selection is
     exact on the same f32 logits; against fp64 logits an index must match wherever
     both neighbouring gaps exceed 1e-2, else lie in the near-tie class.
@@ -163,6 +173,77 @@ def dequant_exact(qw: np.ndarray, s, b) -> np.ndarray:
 def dequant_f16_t(qw: np.ndarray, s, b) -> np.ndarray:
     """The transposed f16 prefill scratch: uint16 bits [K][N] of RN16(s*q + b)."""
     return f16_bits(dequant_exact(qw, s, b)).T.copy()
+
+
+# ---------------------------------------------------------------------- quantize
+
+
+def quantize(w) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Float weights -> the affine int4 format: (qw uint32 [N][K/8], s f16 [N][K/64],
+    b f16 [N][K/64]) for w f16 [N][K] (np.float16 values or uint16 bit patterns).
+
+    Per (row, group of 64): lo and hi are the group's smallest and largest value (a zero
+    becomes +0); b = lo; s = RN16(f32(f32(hi - lo) / 15)); each code is
+    q = clamp(rint_even(f32(f32(w - b) / s)), 0, 15), or 0 for the whole group when s is 0.
+    NumPy float32 arithmetic is IEEE single precision with round-to-nearest-even.
+    """
+    w = np.asarray(w)
+    if w.dtype == np.uint16:
+        w = w.view(np.float16)
+    assert w.dtype == np.float16 and w.ndim == 2
+    n, k = w.shape
+    assert k % GROUP == 0
+    assert np.all(np.isfinite(w)), "weights must be finite"
+    g = w.reshape(n, k // GROUP, GROUP).astype(np.float32)        # exact
+    lo = g.min(axis=2)
+    hi = g.max(axis=2)
+    lo = np.where(lo == 0, np.float32(0.0), lo)                  # -0 -> +0
+    hi = np.where(hi == 0, np.float32(0.0), hi)
+    d = (hi - lo).astype(np.float32)
+    t = (d / np.float32(15.0)).astype(np.float32)
+    s16 = t.astype(np.float16)                                   # one RN-even rounding
+    b16 = lo.astype(np.float16)                                  # exact
+    sf = s16.astype(np.float32)[:, :, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = ((g - b16.astype(np.float32)[:, :, None]).astype(np.float32) / sf).astype(np.float32)
+    q = np.where(sf == 0, np.float32(0.0), np.clip(np.rint(r), 0.0, 15.0))
+    return pack(q.reshape(n, k).astype(np.uint8)), s16, b16
+
+
+def _f32(x: float) -> float:
+    """Round a Python float (an fp64 value) to the nearest f32, ties to even."""
+    return struct.unpack("<f", struct.pack("<f", x))[0]
+
+
+def quantize_loop(w) -> tuple[list, list, list]:
+    """Independent scalar restatement of ``quantize`` for small inputs: Python floats with an
+    explicit f32 rounding after each operation (the fp64 difference of two f16 values is
+    exact, and an fp64 quotient of two f32 values rounds to the correctly rounded f32
+    quotient), Python's ``round`` (half to even), ``struct`` for f16.  Returns codes [N][K]
+    and s, b as f16 bit patterns [N][K/64]."""
+    w = np.asarray(w)
+    if w.dtype == np.uint16:
+        w = w.view(np.float16)
+    n, k = w.shape
+    codes, sb, bb = [], [], []
+    for row in range(n):
+        qrow, srow, brow = [], [], []
+        for g0 in range(0, k, GROUP):
+            vals = [float(v) for v in w[row, g0:g0 + GROUP]]
+            lo, hi = min(vals), max(vals)
+            lo = 0.0 if lo == 0 else lo
+            hi = 0.0 if hi == 0 else hi
+            t = _f32(_f32(hi - lo) / 15.0)
+            s_bits = struct.unpack("<H", struct.pack("<e", t))[0]
+            s = struct.unpack("<e", struct.pack("<H", s_bits))[0]
+            srow.append(s_bits)
+            brow.append(struct.unpack("<H", struct.pack("<e", lo))[0])
+            for v in vals:
+                qrow.append(0 if s == 0 else min(15, max(0, round(_f32(_f32(v - lo) / s)))))
+        codes.append(qrow)
+        sb.append(srow)
+        bb.append(brow)
+    return codes, sb, bb
 
 
 # -------------------------------------------------------------------- products

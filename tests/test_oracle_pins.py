@@ -124,11 +124,59 @@ def pins_topk(topk):
     return fails
 
 
+def _quant_group(head, fill):
+    bits = [int(h, 16) for h in head] + [int(fill, 16)] * (64 - len(head))
+    return np.array([bits], dtype=np.uint16).view(np.float16)
+
+
+def _grid_groups(n_rows, n_groups, seed):
+    """Rows of groups that lie exactly on an affine grid: w = b + s*q with s = 2^-e
+    (e = 3..6), b a multiple of 2^-6 in [-2, 2], every group holding a 0 and a 15 code;
+    all values are exact f16 and the fit must give back exactly (q, s, b)."""
+    rng = np.random.default_rng(seed)
+    q = rng.integers(0, 16, size=(n_rows, n_groups, 64))
+    q[:, :, 3] = 0
+    q[:, :, 40] = 15
+    s = 2.0 ** -rng.integers(3, 7, size=(n_rows, n_groups))
+    b = rng.integers(-128, 129, size=(n_rows, n_groups)) / 64.0
+    w = b[:, :, None] + s[:, :, None] * q
+    return (w.reshape(n_rows, -1).astype(np.float16), q.reshape(n_rows, -1).astype(np.uint8),
+            s.astype(np.float16), b.astype(np.float16))
+
+
+def pins_quantize(quantize, unpack):
+    fails = []
+    for c in _gold("quantize_worked.json")["cases"]:
+        qw, sv, bv = quantize(_quant_group(c["head"], c["fill"]))
+        codes = np.asarray(unpack(np.asarray(qw)))[0]
+        s_bits = int(np.asarray(sv, dtype=np.float16).view(np.uint16)[0, 0])
+        b_bits = int(np.asarray(bv, dtype=np.float16).view(np.uint16)[0, 0])
+        want = c["codes_head"]
+        if codes[:len(want)].tolist() != want:
+            fails.append(f"{c['name']}: codes {codes[:len(want)].tolist()} != {want}")
+        fill_code = 0  # every fixture's fill value is its group minimum (or the constant)
+        if np.any(codes[len(c["head"]):] != fill_code):
+            fails.append(f"{c['name']}: fill codes {sorted(set(codes[len(c['head']):].tolist()))}")
+        if s_bits != int(c["s"], 16):
+            fails.append(f"{c['name']}: s {s_bits:#06x} != {c['s']}")
+        if b_bits != int(c["b"], 16):
+            fails.append(f"{c['name']}: b {b_bits:#06x} != {c['b']}")
+    # exact affine grids come back unchanged
+    w, q, s_, b_ = _grid_groups(3, 4, seed=41)
+    qw, sv, bv = quantize(w)
+    if not (np.array_equal(np.asarray(unpack(np.asarray(qw))), q)
+            and np.array_equal(np.asarray(sv, np.float16).view(np.uint16), s_.view(np.uint16))
+            and np.array_equal(np.asarray(bv, np.float16).view(np.uint16), (b_ + np.float16(0)).view(np.uint16))):
+        fails.append("exact grid not reproduced")
+    return fails
+
+
 def test_pins_pass_on_oracle():
     assert pins_pack(oracle.pack, oracle.unpack) == []
     assert pins_gemv(oracle.gemv_ref, oracle.pack) == []
     assert pins_dequant(oracle.dequant_f16_t, oracle.pack) == []
     assert pins_topk(oracle.topk_ref) == []
+    assert pins_quantize(oracle.quantize, oracle.unpack) == []
 
 
 # ------------------------------------------------------------------------------- pack
@@ -352,6 +400,45 @@ def test_page_figures_fix_head_and_logit_dtypes():
     assert abs(g["vocab"] * 2 / 1e3 - g["logits_kb_per_token"]) / g["logits_kb_per_token"] > 0.4
 
 
+# --------------------------------------------------------------------------- quantize
+
+
+def test_quantize_matches_scalar_restatement():
+    rng = np.random.default_rng(44)
+    w = (rng.standard_normal((5, 256)) * 0.02).astype(np.float16)
+    w[1, :64] = 0.5                                    # constant group
+    w[2, 64:128] = -0.0                                # all negative zeros
+    w[3, 128:192] = rng.integers(-3, 4, size=64) * np.float16(2.0 ** -24)  # subnormal range
+    w[4, 192:] = rng.standard_normal(64) * 3000        # large magnitudes
+    qw, s, b = oracle.quantize(w)
+    codes, sb, bb = oracle.quantize_loop(w)
+    assert np.array_equal(oracle.unpack(qw), np.array(codes, dtype=np.uint8))
+    assert np.array_equal(s.view(np.uint16), np.array(sb, dtype=np.uint16))
+    assert np.array_equal(b.view(np.uint16), np.array(bb, dtype=np.uint16))
+
+
+def test_quantize_error_bound():
+    # |w - (s q + b)| <= s/2 away from the clamp; at most 15 |t - s| more where the rounded
+    # scale makes the top code overshoot 15 (t = (max - min) / 15 exactly)
+    rng = np.random.default_rng(45)
+    w = (rng.standard_normal((16, 1024)) * 0.02).astype(np.float16)
+    qw, s, b = oracle.quantize(w)
+    w_hat = oracle.dequant_exact(qw, s, b)
+    g = w.astype(np.float64).reshape(16, 16, 64)
+    t = (g.max(axis=2) - g.min(axis=2)) / 15.0
+    s64 = s.astype(np.float64)
+    bound = 0.5 * s64 * (1 + 2.0 ** -20) + 15 * np.abs(t - s64)
+    err = np.abs(w.astype(np.float64) - w_hat).reshape(16, 16, 64).max(axis=2)
+    assert np.all(err <= bound)
+    assert np.all(oracle.unpack(qw).reshape(16, 16, 64).min(axis=2) == 0)
+
+
+def test_quantize_then_dequant_is_identity_on_grids():
+    w, q, s, b = _grid_groups(8, 8, seed=46)
+    qw, s2, b2 = oracle.quantize(w)
+    assert np.array_equal(oracle.dequant_exact(qw, s2, b2), w.astype(np.float64))
+
+
 # ------------------------------------------------------------------------------ mutants
 
 
@@ -424,6 +511,27 @@ def _topk_ascending(v, k):
     return order, np.take_along_axis(np.asarray(v), order, axis=1)
 
 
+def _quantize_with(w, rnd=np.rint, div=15.0, use_max_as_b=False, clamp=True, wide=False, keep_neg_zero=False,
+                   codes_from_t=False):
+    w = np.asarray(w)
+    n, k = w.shape
+    f = np.float64 if wide else np.float32
+    g = w.reshape(n, k // 64, 64).astype(f)
+    lo, hi = g.min(axis=2), g.max(axis=2)
+    if not keep_neg_zero:
+        lo = np.where(lo == 0, f(0.0), lo)
+    hi = np.where(hi == 0, f(0.0), hi)
+    t = ((hi - lo) / f(div)).astype(f)
+    s16 = t.astype(np.float16)
+    b16 = (hi if use_max_as_b else lo).astype(np.float16)
+    sf = (t if codes_from_t else s16.astype(f))[:, :, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = ((g - b16.astype(f)[:, :, None]).astype(f) / sf).astype(f)
+    r = rnd(r)
+    q = np.where(sf == 0, 0.0, np.clip(r, 0, 15) if clamp else np.maximum(r, 0))
+    return w4ref.pack(q.reshape(n, k).astype(np.uint8)), s16, b16
+
+
 MUTANTS = {
     "unpack high nibble first": lambda: pins_pack(w4ref.pack, _mut_unpack_high_first),
     "pack high nibble first": lambda: pins_pack(_mut_pack_high_first, w4ref.unpack)
@@ -439,6 +547,16 @@ MUTANTS = {
     "argmax ties to last index": lambda: pins_topk(_topk_last_index_ties),
     "raw-bit comparison": lambda: pins_topk(_topk_raw_bits),
     "ascending order": lambda: pins_topk(_topk_ascending),
+    "quantize truncates": lambda: pins_quantize(lambda w: _quantize_with(w, rnd=np.floor), w4ref.unpack),
+    "quantize ties away from zero": lambda: pins_quantize(lambda w: _quantize_with(w, rnd=lambda r: np.floor(r + 0.5)),
+                                                          w4ref.unpack),
+    "quantize over 16 steps": lambda: pins_quantize(lambda w: _quantize_with(w, div=16.0), w4ref.unpack),
+    "quantize bias from the max": lambda: pins_quantize(lambda w: _quantize_with(w, use_max_as_b=True), w4ref.unpack),
+    "quantize without clamp": lambda: pins_quantize(lambda w: _quantize_with(w, clamp=False), w4ref.unpack),
+    "quantize in fp64": lambda: pins_quantize(lambda w: _quantize_with(w, wide=True), w4ref.unpack),
+    "quantize keeps -0 as bias": lambda: pins_quantize(lambda w: _quantize_with(w, keep_neg_zero=True), w4ref.unpack),
+    "quantize codes from unrounded scale": lambda: pins_quantize(lambda w: _quantize_with(w, codes_from_t=True),
+                                                                 w4ref.unpack),
 }
 
 
