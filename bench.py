@@ -48,7 +48,7 @@ def parse_args():
     p.add_argument("--unfused", action="store_true", help="run q,k,v and gate,up as separate GEMVs (7 per layer)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-check", action="store_true", help="skip the parity re-check of the timed outputs")
-    p.add_argument("--no-small-m", action="store_true", help="skip the batched (M = 16, 8) and Gemma-shaped GEMVs")
+    p.add_argument("--no-small-m", action="store_true", help="skip the batched (M = 16, 8) and Gemma-shaped GEMVs and the quantizer")
     p.add_argument("--counters", metavar="MANIFEST",
                    help="counter-collection pass: launch each kernel shape of the step 3 times (eagerly, between "
                         "marker kernels) plus a copy of known size, write the launch plan to MANIFEST and exit; "
@@ -477,6 +477,40 @@ def small_m(torch, np, w4, synth, oracle, reps=5):
     return out
 
 
+def quantize_bench(torch, np, w4, synth, oracle, copies=4, reps=5):
+    """The load-time quantizer on the decode step's gate|up matrix ([22016][2048] f16
+    weights, N(0, 0.02)): graph-timed over `copies` distinct input buffers (together larger
+    than the MALL), GB/s of 2NK bytes read + NK/2 + NK/16 written, and a bit-exact re-check
+    of 64 sampled rows against the oracle."""
+    n = sum(nn for name, nn, _ in synth.QWEN25_3B_LAYER if name in ("gate", "up"))
+    k = synth.QWEN25_3B_HIDDEN
+    w_host = synth.float_weights(n, k, seed=0, workload=synth.W_DECODE, layer=900)
+    w0 = torch.from_numpy(w_host).cuda()
+    ins = [w0] + [w0.clone() for _ in range(copies - 1)]
+    out = (torch.empty((n, k // 8), dtype=torch.int32, device="cuda"),
+           torch.empty((n, k // 64), dtype=torch.float16, device="cuda"),
+           torch.empty((n, k // 64), dtype=torch.float16, device="cuda"))
+    graph = capture(torch, lambda: [w4.w4_quantize(t, out=out) for t in ins])
+    graph.replay()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+    nb = 2 * n * k + n * k // 2 + n * k // 16
+    rows = np.sort(np.random.default_rng(9).choice(n, 64, replace=False))
+    qw_ref, s_ref, b_ref = oracle.quantize(w_host[rows])
+    ok = (np.array_equal(out[0].cpu().numpy().view(np.uint32)[rows], qw_ref)
+          and np.array_equal(out[1].cpu().numpy().view(np.uint16)[rows], s_ref.view(np.uint16))
+          and np.array_equal(out[2].cpu().numpy().view(np.uint16)[rows], b_ref.view(np.uint16)))
+    return {"workload": f"w4_quantize of a [{n}][{k}] f16 matrix (gate|up), N(0, 0.02)", "avg_us": round(us, 3),
+            "gbps": round(nb / us / 1e3, 1), "frac_hbm": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
+            "bytes_per_launch": nb, "parity_ok": bool(ok), "copies": copies}
+
+
 def cpu_baseline(np, oracle, synth):
     """The oracle's GEMV (unpack + exact dequant + fp64 product) over the seven matrices of as
     many decoder layers as take about 10 s, at M = 1, on this host's cores."""
@@ -590,6 +624,12 @@ def main():
         sm = small_m(torch, np, w4, synth, oracle)
         log(f"small-M GEMVs in {time.time() - t0:.1f}s: " + "; ".join(f"{c['workload']} {c['gbps']} GB/s" for c in sm))
 
+    qz = None
+    if not args.no_small_m:
+        import oracle
+        qz = quantize_bench(torch, np, w4, synth, oracle)
+        log(f"quantizer: {qz['avg_us']} us, {qz['gbps']} GB/s, parity {'ok' if qz['parity_ok'] else 'FAILED'}")
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -635,9 +675,10 @@ def main():
         "cpu_baseline": cpu,
         "parity": check,
         "small_m": sm,
+        "quantize": qz,
     }
-    if sm is not None and not all(c["parity_ok"] for c in sm):
-        check = dict(check or {}, ok=False, small_m_fail=True)
+    if (sm is not None and not all(c["parity_ok"] for c in sm)) or (qz is not None and not qz["parity_ok"]):
+        check = dict(check or {}, ok=False, side_section_fail=True)
         out["parity"] = check
     if check is not None and not check["ok"]:
         out["value"] = None

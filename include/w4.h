@@ -73,6 +73,22 @@ const char* w4_strerror(int status);
 int w4_pack(const uint8_t* q, uint32_t* qw, int64_t N, int64_t K, w4_stream_t stream);
 
 /*
+ * w4_quantize -- the load-time step that produces the format ("The inference engine -- Mojo
+ * 1.0 on Metal", "Where it fits": weights quantized to int4 at load; "Engineering
+ * investigation ...", "Selective quantization": affine, group size 64).  The pages give no
+ * fitting rule; per (row n, group g of 64) this is the min/max fit:
+ *   lo, hi = min, max of w[n][64g .. 64g+63] (a zero counts as +0);  biases[n][g] = lo;
+ *   scales[n][g] = RN16(f32(f32(hi - lo) / 15));
+ *   q = clamp(rint_even(f32(f32(w - lo) / s)), 0, 15), or 0 for the group when s == 0,
+ * with every operation a correctly rounded f32 operation; q is packed as by w4_pack.
+ *   w f16 [N][K] with row stride ldw; qw [N][K/8]; scales, biases f16 [N][K/64].
+ * Requires N >= 1, K >= 64, K % 64 == 0, ldw >= K, ldw % 8 == 0; w and qw 16-byte aligned,
+ * scales and biases 2-byte aligned.  w must be finite (not checked).  Deterministic.
+ */
+int w4_quantize(const uint16_t* w, int64_t ldw, uint32_t* qw, uint16_t* scales, uint16_t* biases,
+                int64_t N, int64_t K, w4_stream_t stream);
+
+/*
  * w4_gemv -- decode GEMV over the packed weights ("Crossing Mojo 1.0": the multi-row
  * GEMV that keeps several weight streams in flight; "What's inside the engine today"):
  *   y[m][n] = sum_k (s[n][k/64] * q[n][k] + b[n][k/64]) * x[m][k]      (f32 accumulation)

@@ -18,7 +18,7 @@ import torch
 from ._lib import lib, LIB_PATH  # noqa: F401
 
 __all__ = [
-    "W4Error", "w4_pack", "w4_gemv", "w4_dequant_f16_t", "gemm_f16", "logits_argmax_topk",
+    "W4Error", "w4_pack", "w4_quantize", "w4_gemv", "w4_dequant_f16_t", "gemm_f16", "logits_argmax_topk",
     "topk_workspace_bytes", "gemm_workspace_bytes", "status_string",
 ]
 
@@ -78,6 +78,31 @@ def w4_pack(q: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
         raise ValueError("out must be [N][K/8]")
     _check("w4_pack", lib().w4_pack(q.data_ptr(), out.data_ptr(), n, k, _stream()))
     return out
+
+
+def w4_quantize(w: torch.Tensor, out: tuple | None = None):
+    """float16 weights [N][K] (rows contiguous) -> (qw int32 [N][K/8], scales float16 [N][K/64],
+    biases float16 [N][K/64]): the min/max affine fit per group of 64 (see include/w4.h)."""
+    _dev(w, "w", torch.float16)
+    if w.dim() != 2:
+        raise ValueError("w must be [N][K]")
+    ldw = _rowmajor(w, "w")
+    n, k = w.shape
+    if out is None:
+        out = (torch.empty((n, k // 8), dtype=torch.int32, device=w.device),
+               torch.empty((n, k // 64), dtype=torch.float16, device=w.device),
+               torch.empty((n, k // 64), dtype=torch.float16, device=w.device))
+    qw, s, b = out
+    _dev(qw, "qw", torch.int32)
+    _dev(s, "scales", torch.float16)
+    _dev(b, "biases", torch.float16)
+    for t, nm in ((qw, "qw"), (s, "scales"), (b, "biases")):
+        _contig(t, nm)
+    if tuple(qw.shape) != (n, k // 8) or tuple(s.shape) != (n, k // 64) or tuple(b.shape) != (n, k // 64):
+        raise ValueError("outputs must be [N][K/8], [N][K/64], [N][K/64]")
+    _check("w4_quantize", lib().w4_quantize(w.data_ptr(), ldw, qw.data_ptr(), s.data_ptr(), b.data_ptr(),
+                                            n, k, _stream()))
+    return qw, s, b
 
 
 def _w4_args(qw, scales, biases):

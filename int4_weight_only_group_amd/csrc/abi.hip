@@ -110,6 +110,22 @@ int w4_gemv(const uint32_t* qw, const uint16_t* scales, const uint16_t* biases, 
   }
 }
 
+int w4_quantize(const uint16_t* w, int64_t ldw, uint32_t* qw, uint16_t* scales, uint16_t* biases,
+                int64_t N, int64_t K, w4_stream_t stream) {
+  try {
+    if (!w || !qw || !scales || !biases) return W4_ERR_NULL;
+    if (int e = check_w4_shape(N, K)) return e;
+    if (ldw < K || ldw > kMaxDim) return W4_ERR_SHAPE;
+    if (!al16(w) || ldw % 8 != 0 || !al16(qw) || !al2(scales) || !al2(biases)) return W4_ERR_ALIGN;
+    if (int e = check_device()) return e;
+    (void)hipGetLastError();
+    w4::launch_quantize(w, ldw, qw, scales, biases, N, K, (hipStream_t)stream);
+    return launched();
+  } catch (...) {
+    return W4_ERR_INTERNAL;
+  }
+}
+
 int w4_dequant_f16_t(const uint32_t* qw, const uint16_t* scales, const uint16_t* biases,
                      uint16_t* wt, int64_t ldwt, int64_t N, int64_t K, w4_stream_t stream) {
   try {

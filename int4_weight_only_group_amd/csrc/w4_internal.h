@@ -52,6 +52,8 @@ void launch_pack(const uint8_t* q, uint32_t* qw, int64_t N, int64_t K, hipStream
 void launch_gemv(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
                  int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st);
 
+void launch_quantize(const uint16_t* w, int64_t ldw, uint32_t* qw, uint16_t* s, uint16_t* b,
+                     int64_t N, int64_t K, hipStream_t st);
 void launch_dequant_t(const uint32_t* qw, const uint16_t* s, const uint16_t* b, uint16_t* wt,
                       int64_t ldwt, int N, int K, hipStream_t st);
 

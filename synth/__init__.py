@@ -27,7 +27,7 @@ GROUP = 64
 W_SINGLE, W_DECODE, W_PREFILL, W_CLASSIFY, W_GEMMA, W_TEST = 0, 1, 2, 3, 4, 9
 
 # Tensor ids (fourth key).
-T_Q, T_S, T_B, T_X, T_HEAD, T_IDS = 0, 1, 2, 3, 4, 5
+T_Q, T_S, T_B, T_X, T_HEAD, T_IDS, T_W = 0, 1, 2, 3, 4, 5, 6
 
 # (name, N, K) of the int4 projections of one Qwen2.5-3B decoder layer.
 QWEN25_3B_LAYER = (
@@ -100,6 +100,12 @@ def head_f16(k: int, v: int, *, seed: int = 0, workload: int = W_TEST, layer: in
         if a < b:
             out[a - lo:b - lo] = (block[a - r0:b - r0] * np.float32(0.02)).astype(np.float16)
     return out
+
+
+def float_weights(n: int, k: int, *, seed: int = 0, workload: int = W_TEST, layer: int = 0) -> np.ndarray:
+    """f16 of N(0, 0.02), [n][k]: unquantized weights, the input of the load-time quantizer."""
+    w = rng(seed, workload, layer, T_W).standard_normal((n, k), dtype=np.float32) * np.float32(0.02)
+    return w.astype(np.float16)
 
 
 def class_ids(vocab: int, *, seed: int = 0, workload: int = W_CLASSIFY) -> tuple[int, int]:

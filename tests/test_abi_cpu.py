@@ -86,6 +86,21 @@ def test_gemv_argument_errors():
     assert n.value == 0
 
 
+def test_quantize_argument_errors():
+    lib = _lib()
+    q = lambda **kw: lib.w4_quantize(kw.get("w", P), kw.get("ldw", 128), kw.get("qw", P), kw.get("s", P),
+                                     kw.get("b", P), kw.get("N", 4), kw.get("K", 128), None)
+    assert q(w=None) == W4_ERR_NULL
+    assert q(b=None) == W4_ERR_NULL
+    assert q(N=0) == W4_ERR_SHAPE
+    assert q(K=96, ldw=96) == W4_ERR_SHAPE
+    assert q(ldw=64) == W4_ERR_SHAPE
+    assert q(w=P + 8) == W4_ERR_ALIGN
+    assert q(ldw=132) == W4_ERR_ALIGN
+    assert q(qw=P + 4) == W4_ERR_ALIGN
+    assert q(s=P + 1) == W4_ERR_ALIGN
+
+
 def test_dequant_and_gemm_argument_errors():
     lib = _lib()
     assert lib.w4_dequant_f16_t(P, P, P, None, 8, 8, 64, None) == W4_ERR_NULL

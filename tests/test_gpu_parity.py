@@ -57,6 +57,72 @@ def test_pack_keeps_low_nibble(w4):
     assert np.array_equal(oracle.unpack(got), q & 0xF)
 
 
+# ----------------------------------------------------------------------------- quantize
+
+
+def quantize_case(w4, w, ldw_pad=0):
+    """Run w4_quantize on f16 weights w [N][K] and compare codes, scales and biases bit for bit
+    with the oracle."""
+    n, k = w.shape
+    wd = dev(np.pad(w, ((0, 0), (0, ldw_pad))))[:, :k]
+    qw, s, b = w4.w4_quantize(wd)
+    qw_ref, s_ref, b_ref = oracle.quantize(w)
+    got_q = to_np(qw).view(np.uint32)
+    assert np.array_equal(got_q, qw_ref), f"codes differ at {np.argwhere(got_q != qw_ref)[:4].tolist()}"
+    assert np.array_equal(to_np(s).view(np.uint16), s_ref.view(np.uint16))
+    assert np.array_equal(to_np(b).view(np.uint16), b_ref.view(np.uint16))
+    return qw, s, b
+
+
+@pytest.mark.parametrize("n,k", [(1, 64), (3, 128), (33, 960), (257, 2048), (100, 11008), (31, 64 * 45)])
+def test_quantize_bit_exact(w4, n, k):
+    rng = np.random.default_rng(n * 1000 + k)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float16)
+    quantize_case(w4, w)
+
+
+def test_quantize_worked_groups(w4):
+    # the hand-worked groups of the oracle's fixture, one per row, on the device
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "quantize_worked.json")) as f:
+        cases = json.load(f)["cases"]
+    rows = [[int(h, 16) for h in c["head"]] + [int(c["fill"], 16)] * (64 - len(c["head"])) for c in cases]
+    w = np.array(rows, dtype=np.uint16).view(np.float16)
+    qw, s, b = quantize_case(w4, w)
+    codes = oracle.unpack(to_np(qw).view(np.uint32))
+    for i, c in enumerate(cases):
+        assert codes[i, :len(c["codes_head"])].tolist() == c["codes_head"], c["name"]
+        assert int(to_np(s).view(np.uint16)[i, 0]) == int(c["s"], 16), c["name"]
+        assert int(to_np(b).view(np.uint16)[i, 0]) == int(c["b"], 16), c["name"]
+
+
+def test_quantize_edge_values_and_stride(w4):
+    rng = np.random.default_rng(77)
+    w = (rng.standard_normal((9, 512)) * 0.02).astype(np.float16)
+    w[0] = 0.0
+    w[1] = -0.0
+    w[2, :64] = 0.5
+    w[3] = rng.integers(-5, 6, size=512) * np.float16(2.0 ** -24)     # subnormals
+    w[4] = (rng.standard_normal(512) * 20000).astype(np.float16)      # near the f16 range
+    w[5, ::2] = -0.0
+    w[6] = np.float16(65504.0)
+    w[6, ::64] = np.float16(-65504.0)
+    w[7] = (rng.integers(0, 16, size=512) * 0.125 - 1.0).astype(np.float16)  # exact grid
+    quantize_case(w4, w, ldw_pad=24)
+
+
+def test_quantize_full_matrix_and_roundtrip(w4):
+    # a gate-sized matrix of N(0, 0.02) weights, every code; then dequant of the result
+    n, k = 11008, 2048
+    w = (np.random.default_rng(5).standard_normal((n, k)) * 0.02).astype(np.float16)
+    qw, s, b = quantize_case(w4, w)
+    cols = np.arange(0, n, 97)
+    wt = to_np(w4.w4_dequant_f16_t(qw, s, b)).view(np.uint16)[:, cols]
+    qw_ref, s_ref, b_ref = oracle.quantize(w[cols])
+    assert np.array_equal(wt, oracle.dequant_f16_t(qw_ref, s_ref, b_ref))
+
+
 # ----------------------------------------------------------------------------- GEMV
 
 
