@@ -9,7 +9,10 @@ functions follow the order in which the pages describe the path:
                     into MLX's affine 4-bit layout ("Appendix: the remaining gap,
                     itemized"), group size 64 ("Engineering investigation ...",
                     "Selective quantization ...").
-  dequant        -- w = s*q + b per group of 64 along K (the affine format above).
+  dequant        -- w = s*q + b per group of 64 along K (the affine format above);
+                    also the engine's own symmetric group-128 format, read as
+                    w = s*(q - 8) ("The inference engine -- Mojo 1.0 on Metal",
+                    "Against MLX, today"; "Appendix: the remaining gap, itemized").
   dequant_f16_t  -- "dequantizes each weight once per prefill into a transposed
                     half-precision scratch" ("Crossing Mojo 1.0").
   gemv_ref       -- the decode GEMV y = x W^T ("Crossing Mojo 1.0", the multi-row
@@ -155,24 +158,32 @@ def _f64(a) -> np.ndarray:
 # ----------------------------------------------------------------------- dequant
 
 
-def dequant_exact(qw: np.ndarray, s, b) -> np.ndarray:
-    """Exact weights w[n][k] = s[n][k//64] * q[n][k] + b[n][k//64] in fp64 ([N][K]).
+def dequant_exact(qw: np.ndarray, s, b, group: int = GROUP) -> np.ndarray:
+    """Exact weights in fp64 ([N][K]).
 
-    s and b are f16 ([N][K/64], np.float16 values or uint16 bit patterns).
+    Affine format (b given): w[n][k] = s[n][k//group] * q[n][k] + b[n][k//group].
+    Symmetric format (b is None): the engine's own int4 ("The inference engine -- Mojo 1.0 on
+    Metal": group-128 in "Against MLX, today" and "What's inside the engine today",
+    symmetric in "Appendix: the remaining gap, itemized"), read as w = s * (q - 8) with
+    group = 128 (zero point 8, no bias), an exact zero taken as +0.  s and b are f16 ([N][K/group], np.float16 values or uint16 bits).
     """
     q = unpack(qw).astype(np.float64)
     n, k = q.shape
-    assert k % GROUP == 0
+    assert k % group == 0
     s64 = _f64(s)
+    assert s64.shape == (n, k // group)
+    grp = np.arange(k) // group
+    if b is None:
+        return s64[:, grp] * (q - 8.0) + 0.0      # + 0.0 turns -0 into +0
     b64 = _f64(b)
-    assert s64.shape == (n, k // GROUP) and b64.shape == (n, k // GROUP)
-    grp = np.arange(k) // GROUP
+    assert b64.shape == (n, k // group)
     return s64[:, grp] * q + b64[:, grp]
 
 
-def dequant_f16_t(qw: np.ndarray, s, b) -> np.ndarray:
-    """The transposed f16 prefill scratch: uint16 bits [K][N] of RN16(s*q + b)."""
-    return f16_bits(dequant_exact(qw, s, b)).T.copy()
+def dequant_f16_t(qw: np.ndarray, s, b, group: int = GROUP) -> np.ndarray:
+    """The transposed f16 prefill scratch: uint16 bits [K][N] of RN16(w), w as in
+    dequant_exact (one rounding of the exact value)."""
+    return f16_bits(dequant_exact(qw, s, b, group)).T.copy()
 
 
 # ---------------------------------------------------------------------- quantize
@@ -249,13 +260,13 @@ def quantize_loop(w) -> tuple[list, list, list]:
 # -------------------------------------------------------------------- products
 
 
-def gemv_ref(qw: np.ndarray, s, b, x) -> tuple[np.ndarray, np.ndarray]:
+def gemv_ref(qw: np.ndarray, s, b, x, group: int = GROUP) -> tuple[np.ndarray, np.ndarray]:
     """Decode GEMV: y[m][n] = sum_k w[n][k] * x[m][k] in fp64, with the error scale.
 
     Returns (y_ref, bound), both fp64 [M][N], where bound = sum_k |w[n][k] x[m][k]|.
-    x is f16 [M][K]; w is the exact dequantized weight.
+    x is f16 [M][K]; w is the exact dequantized weight (either format, see dequant_exact).
     """
-    w = dequant_exact(qw, s, b)
+    w = dequant_exact(qw, s, b, group)
     x64 = _f64(x)
     assert x64.ndim == 2 and x64.shape[1] == w.shape[1]
     return x64 @ w.T, np.abs(x64) @ np.abs(w).T

@@ -124,6 +124,31 @@ def pins_topk(topk):
     return fails
 
 
+def pins_sym128(gemv, dequant_f16_t, pack):
+    """The symmetric group-128 format: hand-worked GEMVs and dequantized bit patterns."""
+    fails = []
+    gold = _gold("sym128_handworked.json")
+    for c in gold["gemv"]:
+        k = c["K"]
+        q = _pattern(c["q"], k).astype(np.uint8)[None, :]
+        sv = np.array([c["s"]], dtype=np.float16)
+        x = np.stack([_pattern(p_, k) for p_ in c["x"]]).astype(np.float16)
+        y, _ = gemv(pack(q), sv, None, x, group=128)
+        if not np.array_equal(np.asarray(y), np.array(c["y"], dtype=np.float64)[:, None]):
+            fails.append(f"{c['name']}: {np.asarray(y).ravel()} != {c['y']}")
+    for c in gold["dequant"]:
+        q = np.full((1, 128), 8, dtype=np.uint8)
+        q[0, 5] = c["q"]
+        sv = np.array([[int(c["s"], 16)]], dtype=np.uint16).view(np.float16)
+        with np.errstate(over="ignore"):
+            wt = np.asarray(dequant_f16_t(pack(q), sv, None, group=128))
+        if int(wt[5, 0]) != int(c["w"], 16):
+            fails.append(f"s={c['s']} q={c['q']}: {int(wt[5, 0]):#06x} != {c['w']}")
+        if int(wt[0, 0]) != 0:
+            fails.append(f"s={c['s']} q=8: {int(wt[0, 0]):#06x} != +0")
+    return fails
+
+
 def _quant_group(head, fill):
     bits = [int(h, 16) for h in head] + [int(fill, 16)] * (64 - len(head))
     return np.array([bits], dtype=np.uint16).view(np.float16)
@@ -177,6 +202,7 @@ def test_pins_pass_on_oracle():
     assert pins_dequant(oracle.dequant_f16_t, oracle.pack) == []
     assert pins_topk(oracle.topk_ref) == []
     assert pins_quantize(oracle.quantize, oracle.unpack) == []
+    assert pins_sym128(oracle.gemv_ref, oracle.dequant_f16_t, oracle.pack) == []
 
 
 # ------------------------------------------------------------------------------- pack
@@ -439,6 +465,23 @@ def test_quantize_then_dequant_is_identity_on_grids():
     assert np.array_equal(oracle.dequant_exact(qw, s2, b2), w.astype(np.float64))
 
 
+def test_sym128_equals_affine_with_bias_minus_8s():
+    # the symmetric format is the affine one at group 64 with each scale repeated over its two
+    # halves and b = -8 s (exact: a power-of-two multiple), dequantized through the other path
+    rng = np.random.default_rng(47)
+    q = rng.integers(0, 16, size=(6, 512)).astype(np.uint8)
+    s128 = (rng.standard_normal((6, 4)) * 0.02).astype(np.float16)
+    s64 = np.repeat(s128, 2, axis=1)
+    b64 = (-8.0 * s64.astype(np.float64)).astype(np.float16)
+    assert np.array_equal(b64.astype(np.float64), -8.0 * s64.astype(np.float64))
+    qw = oracle.pack(q)
+    assert np.array_equal(oracle.dequant_f16_t(qw, s128, None, group=128), oracle.dequant_f16_t(qw, s64, b64))
+    x = synth.activations(3, 512, seed=48)
+    y1, b1 = oracle.gemv_ref(qw, s128, None, x, group=128)
+    y2, b2 = oracle.gemv_ref(qw, s64, b64, x)
+    assert np.allclose(y1, y2, rtol=0, atol=1e-12) and np.allclose(b1, b2, rtol=0, atol=1e-12)
+
+
 # ------------------------------------------------------------------------------ mutants
 
 
@@ -532,6 +575,28 @@ def _quantize_with(w, rnd=np.rint, div=15.0, use_max_as_b=False, clamp=True, wid
     return w4ref.pack(q.reshape(n, k).astype(np.uint8)), s16, b16
 
 
+def _sym_dequant(zero=8.0, group=128, plus_zero=True, flip=False):
+    def dq(qw, sv, b, group_arg=None):
+        q = w4ref.unpack(qw).astype(np.float64)
+        n, k = q.shape
+        grp = np.minimum(np.arange(k) // group, sv.shape[1] - 1)
+        w = sv.astype(np.float64)[:, grp] * ((zero - q) if flip else (q - zero))
+        return w + 0.0 if plus_zero else w
+    return dq
+
+
+def _sym_pins_with(dq):
+    def gemv(qw, sv, b, x, group=128):
+        w = dq(qw, sv, b)
+        x64 = x.astype(np.float64)
+        return x64 @ w.T, np.abs(x64) @ np.abs(w).T
+
+    def deq(qw, sv, b, group=128):
+        with np.errstate(over="ignore"):
+            return w4ref.f16_bits(dq(qw, sv, b)).T.copy()
+    return pins_sym128(gemv, deq, w4ref.pack)
+
+
 MUTANTS = {
     "unpack high nibble first": lambda: pins_pack(w4ref.pack, _mut_unpack_high_first),
     "pack high nibble first": lambda: pins_pack(_mut_pack_high_first, w4ref.unpack)
@@ -557,6 +622,10 @@ MUTANTS = {
     "quantize keeps -0 as bias": lambda: pins_quantize(lambda w: _quantize_with(w, keep_neg_zero=True), w4ref.unpack),
     "quantize codes from unrounded scale": lambda: pins_quantize(lambda w: _quantize_with(w, codes_from_t=True),
                                                                  w4ref.unpack),
+    "symmetric zero point 7": lambda: _sym_pins_with(_sym_dequant(zero=7.0)),
+    "symmetric over groups of 64": lambda: _sym_pins_with(_sym_dequant(group=64)),
+    "symmetric zero keeps its sign": lambda: _sym_pins_with(_sym_dequant(plus_zero=False)),
+    "symmetric sign flipped": lambda: _sym_pins_with(_sym_dequant(flip=True)),
 }
 
 
