@@ -48,7 +48,7 @@ def parse_args():
     p.add_argument("--unfused", action="store_true", help="run q,k,v and gate,up as separate GEMVs (7 per layer)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-check", action="store_true", help="skip the parity re-check of the timed outputs")
-    p.add_argument("--no-small-m", action="store_true", help="skip the batched (M = 16, 8) and Gemma-shaped GEMVs and the quantizer")
+    p.add_argument("--no-small-m", action="store_true", help="skip the side sections: batched (M = 16, 8), Gemma-shaped and symmetric group-128 GEMVs, speculative verify, the quantizer")
     p.add_argument("--counters", metavar="MANIFEST",
                    help="counter-collection pass: launch each kernel shape of the step 3 times (eagerly, between "
                         "marker kernels) plus a copy of known size, write the launch plan to MANIFEST and exit; "
@@ -420,9 +420,13 @@ def parity_check(torch, np, wl, oracle, synth):
 # the same activations run row-concatenated, as in the decode step.  Each shape is timed
 # over `copies` distinct copies of its weights (together larger than the 256 MB MALL).
 SMALL_M = (("qwen3-1.7b classify", "CLASSIFY_ROWS", "QWEN3_1P7B_CLASSIFY", "W_CLASSIFY",
-            [["q", "k", "v"], ["gate", "up"], ["down"]], 40),
-           ("gemma-12b layer", 8, "GEMMA12B_LAYER", "W_GEMMA", [["gate", "up"], ["down"], ["q"]], 10),
-           ("gemma-12b layer", 1, "GEMMA12B_LAYER", "W_GEMMA", [["gate", "up"], ["down"], ["q"]], 10))
+            [["q", "k", "v"], ["gate", "up"], ["down"]], 40, "affine64"),
+           ("gemma-12b layer", 8, "GEMMA12B_LAYER", "W_GEMMA", [["gate", "up"], ["down"], ["q"]], 10, "affine64"),
+           ("gemma-12b layer", 1, "GEMMA12B_LAYER", "W_GEMMA", [["gate", "up"], ["down"], ["q"]], 10, "affine64"),
+           # the engine's own format on the decode step's shapes (a per-layer figure: q|k|v, o,
+           # gate|up, down once each, 36 copies apiece)
+           ("qwen2.5-3b decode layer, symmetric group-128", 1, "QWEN25_3B_LAYER", "W_DECODE",
+            [["q", "k", "v"], ["o"], ["gate", "up"], ["down"]], 36, "sym128"))
 
 
 def small_m(torch, np, w4, synth, oracle, reps=5):
@@ -430,7 +434,8 @@ def small_m(torch, np, w4, synth, oracle, reps=5):
     GB/s against HBM peak, and a parity re-check of the last launch on 64 sampled rows."""
     rng = np.random.default_rng(321)
     out = []
-    for cfg, (label, m, layer_name, wname, groups, copies) in enumerate(SMALL_M):
+    for cfg, (label, m, layer_name, wname, groups, copies, fmt) in enumerate(SMALL_M):
+        sym = fmt == "sym128"
         m = getattr(synth, m) if isinstance(m, str) else m
         wk = getattr(synth, wname)
         shapes = {name: (j, n, k) for j, (name, n, k) in enumerate(getattr(synth, layer_name))}
@@ -439,17 +444,27 @@ def small_m(torch, np, w4, synth, oracle, reps=5):
         worst = 0.0
         ok = True
         for grp in groups:
-            parts = [synth.w4_weights(shapes[g][1], shapes[g][2], seed=0, workload=wk,
-                                      layer=100 * cfg + shapes[g][0]) for g in grp]
-            q, s, b = (np.concatenate([p[i] for p in parts]) for i in range(3))
+            if sym:
+                parts = [synth.w4_sym128_weights(shapes[g][1], shapes[g][2], seed=0, workload=wk,
+                                                 layer=100 * cfg + shapes[g][0]) for g in grp]
+                q, s = (np.concatenate([p[i] for p in parts]) for i in range(2))
+                b = None
+            else:
+                parts = [synth.w4_weights(shapes[g][1], shapes[g][2], seed=0, workload=wk,
+                                          layer=100 * cfg + shapes[g][0]) for g in grp]
+                q, s, b = (np.concatenate([p[i] for p in parts]) for i in range(3))
             n, k = q.shape
             x_host = synth.activations(m, k, seed=0, workload=wk, layer=100 * cfg + 50 + shapes[grp[0]][0])
             qw0 = w4.w4_pack(torch.from_numpy(q).cuda())
-            s0, b0 = torch.from_numpy(s).cuda(), torch.from_numpy(b).cuda()
-            mats = [(qw0, s0, b0)] + [(qw0.clone(), s0.clone(), b0.clone()) for _ in range(copies - 1)]
+            s0 = torch.from_numpy(s).cuda()
+            b0 = None if sym else torch.from_numpy(b).cuda()
+            mats = [(qw0, s0, b0)] + [(qw0.clone(), s0.clone(), None if sym else b0.clone()) for _ in range(copies - 1)]
             x = torch.from_numpy(x_host).cuda()
             y = torch.empty((m, n), dtype=torch.float32, device="cuda")
-            fns = [lambda t=t: w4.w4_gemv(t[0], t[1], t[2], x, out=y) for t in mats]
+            if sym:
+                fns = [lambda t=t: w4.w4_gemv_sym128(t[0], t[1], x, out=y) for t in mats]
+            else:
+                fns = [lambda t=t: w4.w4_gemv(t[0], t[1], t[2], x, out=y) for t in mats]
             graph = capture(torch, lambda: [f() for f in fns])
             graph.replay()
             stream = torch.cuda.current_stream()
@@ -460,9 +475,12 @@ def small_m(torch, np, w4, synth, oracle, reps=5):
             e1.record(stream)
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
-            nb = gemv_bytes(m, n, k)
+            nb = n * k // 2 + n * k // 64 + 2 * m * k + 4 * m * n if sym else gemv_bytes(m, n, k)
             sel = np.sort(rng.choice(n, min(n, 64), replace=False))
-            y_ref, bound = oracle.gemv_ref(oracle.pack(q[sel]), s[sel], b[sel], x_host)
+            if sym:
+                y_ref, bound = oracle.gemv_ref(oracle.pack(q[sel]), s[sel], None, x_host, group=128)
+            else:
+                y_ref, bound = oracle.gemv_ref(oracle.pack(q[sel]), s[sel], b[sel], x_host)
             okc, wr = oracle.check_bound(y.cpu().numpy()[:, sel], y_ref, bound)
             ok &= okc
             worst = max(worst, wr)
@@ -471,10 +489,48 @@ def small_m(torch, np, w4, synth, oracle, reps=5):
             tot_b += nb
             tot_us += us
             del mats, fns, graph
-        out.append({"workload": f"{label} at M={m}", "gemvs": rows_out, "gbps": round(tot_b / tot_us / 1e3, 1),
+        out.append({"workload": f"{label} at M={m}", "format": fmt, "gemvs": rows_out, "gbps": round(tot_b / tot_us / 1e3, 1),
                     "frac_hbm": round(tot_b / tot_us / 1e3 / HBM_PEAK_GBS, 4), "parity_ok": bool(ok),
                     "worst_err_over_bound": worst, "copies": copies})
     return out
+
+
+SPEC_ROWS = 8  # draft positions verified per step
+
+
+def spec_verify(torch, np, w4, synth, oracle, wl, reps=20):
+    """Speculative-verify greedy check: SPEC_ROWS draft positions through the decode step's
+    f16 head (one gemm_f16 at M = 8, which streams the head once for all rows) and a per-row
+    argmax (logits_argmax_topk with k = 1), as one graph.  Parity: every row's argmax against
+    the fp64 logits wherever the top-2 margin exceeds 1e-2 (else within the near-tie class)."""
+    m = SPEC_ROWS
+    x_host = synth.activations(m, wl.H, seed=0, workload=synth.W_DECODE, layer=997)
+    x = torch.from_numpy(x_host).cuda()
+    logits = torch.empty((m, wl.V), dtype=torch.float32, device="cuda")
+    idx = torch.empty((m, 1), dtype=torch.int32, device="cuda")
+    val = torch.empty((m, 1), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(16, w4.topk_workspace_bytes(m, wl.V, 1)), dtype=torch.uint8, device="cuda")
+    gws = torch.empty(max(16, w4.gemm_workspace_bytes(x, wl.head)), dtype=torch.uint8, device="cuda")
+
+    def step():
+        w4.gemm_f16(x, wl.head, out=logits, workspace=gws)
+        w4.logits_argmax_topk(logits, 1, idx=idx, val=val, workspace=ws)
+    graph = capture(torch, step)
+    graph.replay()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    c_ref, _ = oracle.gemm_ref(x_host, wl.head_host)
+    ok, loose = oracle.check_topk_vs_exact(c_ref, idx.cpu().numpy(), 1)
+    nb = 2 * wl.H * wl.V + 2 * m * wl.H + 8 * m * wl.V  # head + x + logits written and read
+    return {"workload": f"speculative verify: {m} draft positions x f16 head [{wl.H}][{wl.V}] + per-row argmax",
+            "us": round(us, 3), "gbps": round(nb / us / 1e3, 1), "frac_hbm": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
+            "parity_ok": bool(ok), "rows_in_near_tie": int(loose)}
 
 
 def quantize_bench(torch, np, w4, synth, oracle, copies=4, reps=5):
@@ -624,9 +680,11 @@ def main():
         sm = small_m(torch, np, w4, synth, oracle)
         log(f"small-M GEMVs in {time.time() - t0:.1f}s: " + "; ".join(f"{c['workload']} {c['gbps']} GB/s" for c in sm))
 
-    qz = None
+    qz = sv = None
     if not args.no_small_m:
         import oracle
+        sv = spec_verify(torch, np, w4, synth, oracle, wl)
+        log(f"speculative verify: {sv['us']} us, parity {'ok' if sv['parity_ok'] else 'FAILED'}")
         qz = quantize_bench(torch, np, w4, synth, oracle)
         log(f"quantizer: {qz['avg_us']} us, {qz['gbps']} GB/s, parity {'ok' if qz['parity_ok'] else 'FAILED'}")
 
@@ -676,8 +734,10 @@ def main():
         "parity": check,
         "small_m": sm,
         "quantize": qz,
+        "spec_verify": sv,
     }
-    if (sm is not None and not all(c["parity_ok"] for c in sm)) or (qz is not None and not qz["parity_ok"]):
+    if ((sm is not None and not all(c["parity_ok"] for c in sm)) or (qz is not None and not qz["parity_ok"])
+            or (sv is not None and not sv["parity_ok"])):
         check = dict(check or {}, ok=False, side_section_fail=True)
         out["parity"] = check
     if check is not None and not check["ok"]:

@@ -116,6 +116,21 @@ int w4_dequant_f16_t(const uint32_t* qw, const uint16_t* scales, const uint16_t*
                      uint16_t* wt, int64_t ldwt, int64_t N, int64_t K, w4_stream_t stream);
 
 /*
+ * The engine's own symmetric group-128 int4 ("The inference engine -- Mojo 1.0 on Metal":
+ * group-128 int4 in "Against MLX, today" and "What's inside the engine today", symmetric in
+ * "Appendix: the remaining gap, itemized"), read as
+ *   w[n][k] = s[n][k/128] * (q[n][k] - 8)      (zero point 8, no bias),
+ * with the same packed codes as above and scales f16 [N][K/128].  These two calls are
+ * w4_gemv and w4_dequant_f16_t for that format: same arguments without the biases, same
+ * requirements plus K % 128 == 0; the dequant rounds s (q - 8) once (an exact zero is +0)
+ * and is bit-exact; the GEMV meets the same per-output bound.  No workspace.
+ */
+int w4_gemv_sym128(const uint32_t* qw, const uint16_t* scales, const uint16_t* x, int64_t ldx,
+                   float* y, int64_t ldy, int64_t M, int64_t N, int64_t K, w4_stream_t stream);
+int w4_dequant_f16_t_sym128(const uint32_t* qw, const uint16_t* scales, uint16_t* wt, int64_t ldwt,
+                            int64_t N, int64_t K, w4_stream_t stream);
+
+/*
  * gemm_f16 -- C = A * B with f16 inputs and f32 accumulation and output: the prefill GEMM
  * on the f16 scratch ("Crossing Mojo 1.0") and the f16 LM head ("What's inside the engine
  * today": the head streamed as a [hidden x vocab] matrix per token).

@@ -18,7 +18,7 @@ import torch
 from ._lib import lib, LIB_PATH  # noqa: F401
 
 __all__ = [
-    "W4Error", "w4_pack", "w4_quantize", "w4_gemv", "w4_dequant_f16_t", "gemm_f16", "logits_argmax_topk",
+    "W4Error", "w4_pack", "w4_quantize", "w4_gemv", "w4_gemv_sym128", "w4_dequant_f16_t_sym128", "w4_dequant_f16_t", "gemm_f16", "logits_argmax_topk",
     "topk_workspace_bytes", "gemm_workspace_bytes", "status_string",
 ]
 
@@ -152,6 +152,53 @@ def w4_dequant_f16_t(qw: torch.Tensor, scales: torch.Tensor, biases: torch.Tenso
     _check("w4_dequant_f16_t", lib().w4_dequant_f16_t(qw.data_ptr(), scales.data_ptr(),
                                                       biases.data_ptr(), out.data_ptr(), ldwt, n,
                                                       k, _stream()))
+    return out
+
+
+def _sym_args(qw, scales):
+    _dev(qw, "qw", torch.int32)
+    _dev(scales, "scales", torch.float16)
+    _contig(qw, "qw")
+    _contig(scales, "scales")
+    n, kw = qw.shape
+    k = kw * 8
+    if k % 128 != 0 or tuple(scales.shape) != (n, k // 128):
+        raise ValueError("the symmetric group-128 format needs K % 128 == 0 and scales [N][K/128]")
+    return n, k
+
+
+def w4_gemv_sym128(qw: torch.Tensor, scales: torch.Tensor, x: torch.Tensor,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """Symmetric group-128 GEMV: y[m][n] = sum_k scales[n][k//128] (q[n][k] - 8) x[m][k]."""
+    n, k = _sym_args(qw, scales)
+    _dev(x, "x", torch.float16)
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError("x must be [M][K]")
+    ldx = _rowmajor(x, "x")
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32)
+    if tuple(out.shape) != (m, n):
+        raise ValueError("out must be [M][N]")
+    ldy = _rowmajor(out, "out")
+    _check("w4_gemv_sym128", lib().w4_gemv_sym128(qw.data_ptr(), scales.data_ptr(), x.data_ptr(), ldx,
+                                                  out.data_ptr(), ldy, m, n, k, _stream()))
+    return out
+
+
+def w4_dequant_f16_t_sym128(qw: torch.Tensor, scales: torch.Tensor,
+                            out: torch.Tensor | None = None) -> torch.Tensor:
+    """Transposed f16 scratch of the symmetric group-128 format: out[k][n] = RN16(s (q - 8))."""
+    n, k = _sym_args(qw, scales)
+    if out is None:
+        out = torch.empty((k, n), dtype=torch.float16, device=qw.device)
+    _dev(out, "out", torch.float16)
+    if tuple(out.shape) != (k, n):
+        raise ValueError("out must be [K][N]")
+    ldwt = _rowmajor(out, "out")
+    _check("w4_dequant_f16_t_sym128", lib().w4_dequant_f16_t_sym128(qw.data_ptr(), scales.data_ptr(),
+                                                                    out.data_ptr(), ldwt, n, k, _stream()))
     return out
 
 

@@ -17,7 +17,8 @@
 // so that each k becomes one 8-byte LDS write of four consecutive n.  After a barrier the
 // workgroup writes 256 k-rows of 64 contiguous f16 (128 bytes) along N with 16-byte stores
 // (2-byte stores when the output rows are not 16-byte aligned, e.g. N not a multiple of 8).
-// HBM-bound: 0.5625 bytes read and 2 bytes written per weight.
+// HBM-bound: 0.5625 bytes read and 2 bytes written per weight.  The same kernel serves the
+// symmetric group-128 format (w = s (q - 8)), with its scales staged per 128 codes.
 #include "w4_internal.h"
 
 namespace w4 {
@@ -37,13 +38,17 @@ __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uin
 // 16 apart) hit distinct banks.
 __device__ __forceinline__ int slot(int kk, int q) { return kk * PITCH + 8 * (q ^ ((kk >> 4) & 15)); }
 
+// SYM: the symmetric group-128 format, w = RN16(s (q - 8)) (no bias; the OR trick's offsets
+// grow by 8 so the exact f16 is q - 8, and the FMA's addend +0 makes an exact zero +0).
+template <bool SYM>
 __global__ __launch_bounds__(256) void dequant_t_kernel(const uint32_t* __restrict__ qw,
                                                         const uint16_t* __restrict__ sc,
                                                         const uint16_t* __restrict__ bi,
                                                         uint16_t* __restrict__ wt, int64_t ldwt,
                                                         int N, int K, bool vec) {
   __shared__ __align__(16) unsigned char t[TK * PITCH];
-  __shared__ uint16_t ss[TN][TK / kGroup], bs[TN][TK / kGroup];
+  constexpr int GRP = SYM ? 128 : kGroup, NGT = TK / GRP;  // groups per tile row
+  __shared__ uint16_t ss[TN][NGT], bs[TN][NGT];
   // Workgroups are dealt round-robin to the 8 XCDs; all K-tiles of a 64-row block get the
   // same XCD and run back to back there, so the block's scale and bias lines (shared by its
   // K-tiles, 8 bytes of each row per tile) are fetched once into that XCD's L2.
@@ -54,7 +59,7 @@ __global__ __launch_bounds__(256) void dequant_t_kernel(const uint32_t* __restri
   const int n0 = rb * TN;
   const int k0 = kt * TK;
   const int tid = threadIdx.x;
-  const int G = K / kGroup;
+  const int G = K / GRP;
 
   // this thread's codes: rows n0 + 4rq + i, codes k .. k + 15 (none past the row end: K is a
   // multiple of 64 and the 16 codes never straddle it)
@@ -68,27 +73,30 @@ __global__ __launch_bounds__(256) void dequant_t_kernel(const uint32_t* __restri
     if (n < N && k < K)
       w[i] = *reinterpret_cast<const uint2*>(qw + (int64_t)n * (K / 8) + k / 8);
   }
-  // the tile's scales and biases (64 rows x 4 groups), zero outside the matrix
+  // the tile's scales and biases (64 rows x 4 or 2 groups), zero outside the matrix
   {
     const int r = tid >> 2, g = tid & 3;
-    const int n = n0 + r, gk = k0 / kGroup + g;
+    const int n = n0 + r, gk = k0 / GRP + g;
     uint16_t sv = 0, bv = 0;
-    if (n < N && gk < G) {
+    if (g < NGT && n < N && gk < G) {
       sv = sc[(int64_t)n * G + gk];
-      bv = bi[(int64_t)n * G + gk];
+      bv = SYM ? 0 : bi[(int64_t)n * G + gk];
     }
-    ss[r][g] = sv;
-    bs[r][g] = bv;
+    if (g < NGT) {
+      ss[r][g] = sv;
+      bs[r][g] = bv;
+    }
   }
   __syncthreads();
 
   // dequantize: pair p of word wi holds codes 8wi + p and 8wi + p + 4 of a row
-  const h2 o1024 = {(f16)1024.0f, (f16)1024.0f}, o64 = {(f16)64.0f, (f16)64.0f};
+  constexpr float kLo = SYM ? 1032.0f : 1024.0f, kHi = SYM ? 72.0f : 64.0f;
+  const h2 o1024 = {(f16)kLo, (f16)kLo}, o64 = {(f16)kHi, (f16)kHi};
   uint32_t v[4][2][4];  // [row][word][pair]
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const f16 sv = __builtin_bit_cast(f16, ss[4 * rq + i][kp >> 2]);
-    const f16 bv = __builtin_bit_cast(f16, bs[4 * rq + i][kp >> 2]);
+    const f16 sv = __builtin_bit_cast(f16, ss[4 * rq + i][kp / (GRP / 16)]);
+    const f16 bv = __builtin_bit_cast(f16, bs[4 * rq + i][kp / (GRP / 16)]);
     const h2 s2 = {sv, sv}, b2 = {bv, bv};
     const uint32_t words[2] = {w[i].x, w[i].y};
 #pragma unroll
@@ -144,13 +152,25 @@ __global__ __launch_bounds__(256) void dequant_t_kernel(const uint32_t* __restri
 
 }  // namespace
 
-void launch_dequant_t(const uint32_t* qw, const uint16_t* s, const uint16_t* b, uint16_t* wt,
-                      int64_t ldwt, int N, int K, hipStream_t st) {
+template <bool SYM>
+void launch_dequant_fmt(const uint32_t* qw, const uint16_t* s, const uint16_t* b, uint16_t* wt,
+                        int64_t ldwt, int N, int K, hipStream_t st) {
   const int KT = (K + TK - 1) / TK, RB = (N + TN - 1) / TN;
   const dim3 grid((unsigned)(8 * ((RB + 7) / 8) * KT));  // see the XCD mapping in the kernel
   // 16-byte stores need every output row to start 16-byte aligned
   const bool vec = ldwt % 8 == 0 && ((uintptr_t)wt & 15u) == 0;
-  hipLaunchKernelGGL(dequant_t_kernel, grid, dim3(256), 0, st, qw, s, b, wt, ldwt, N, K, vec);
+  hipLaunchKernelGGL((dequant_t_kernel<SYM>), grid, dim3(256), 0, st, qw, s, b, wt, ldwt, N, K,
+                     vec);
+}
+
+void launch_dequant_t(const uint32_t* qw, const uint16_t* s, const uint16_t* b, uint16_t* wt,
+                      int64_t ldwt, int N, int K, hipStream_t st) {
+  launch_dequant_fmt<false>(qw, s, b, wt, ldwt, N, K, st);
+}
+
+void launch_dequant_t_sym128(const uint32_t* qw, const uint16_t* s, uint16_t* wt, int64_t ldwt,
+                             int N, int K, hipStream_t st) {
+  launch_dequant_fmt<true>(qw, s, s, wt, ldwt, N, K, st);
 }
 
 }  // namespace w4

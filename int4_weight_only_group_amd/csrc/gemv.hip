@@ -45,10 +45,21 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 
+// Weight formats: the affine group-64 format (w = s q + b) and the symmetric group-128 one
+// (w = s (q - 8), no bias).  For the latter the OR trick's offsets grow by 8, so the exact
+// f16 it yields is q - 8, and the FMA's addend is +0 (w = RN(s (q - 8)), an exact zero +0).
+template <bool SYM>
+struct Fmt {
+  static constexpr int kGroupSize = SYM ? 128 : 64;
+  static constexpr int kChunkShift = SYM ? 2 : 1;  // 16-byte chunk index -> group index
+  static constexpr float kLo = SYM ? 1032.0f : 1024.0f, kHi = SYM ? 72.0f : 64.0f;
+};
+
 // The 8 weights of word w as f16 pairs matching the x pair order (see file comment).
+template <bool SYM>
 __device__ __forceinline__ uint4 word_weights(uint32_t w, h2 s2, h2 b2) {
   const uint32_t w8 = w >> 8;
-  const h2 o1024 = {(f16)1024.0f, (f16)1024.0f}, o64 = {(f16)64.0f, (f16)64.0f};
+  const h2 o1024 = {(f16)Fmt<SYM>::kLo, (f16)Fmt<SYM>::kLo}, o64 = {(f16)Fmt<SYM>::kHi, (f16)Fmt<SYM>::kHi};
   const h2 q0 = as_h2((w & 0x000F000Fu) | 0x64006400u) - o1024;   // exact
   const h2 q1 = as_h2((w & 0x00F000F0u) | 0x54005400u) - o64;
   const h2 q2 = as_h2((w8 & 0x000F000Fu) | 0x64006400u) - o1024;
@@ -79,7 +90,7 @@ __device__ __forceinline__ uint4 pair_up(uint4 d) {
   return p;
 }
 
-template <int MT, int R, int P>
+template <int MT, int R, int P, bool SYM>
 __global__ __launch_bounds__(kWG) void gemv_kernel(const uint32_t* __restrict__ qw,
                                                    const uint16_t* __restrict__ sc,
                                                    const uint16_t* __restrict__ bi,
@@ -96,7 +107,7 @@ __global__ __launch_bounds__(kWG) void gemv_kernel(const uint32_t* __restrict__ 
   const int team = tid / P;
   const int row0 = (blockIdx.x * TEAMS + team) * R;
   const int64_t KW = K / 8;  // words per row
-  const int G = K / kGroup;  // groups per row
+  const int G = K / Fmt<SYM>::kGroupSize;  // groups per row
 
   const uint4* rowp[R];
   const uint16_t* sp[R];
@@ -106,7 +117,7 @@ __global__ __launch_bounds__(kWG) void gemv_kernel(const uint32_t* __restrict__ 
     const int n = min(row0 + r, N - 1);  // clamp: tail rows reload the last row, never stored
     rowp[r] = reinterpret_cast<const uint4*>(qw + (int64_t)n * KW);
     sp[r] = sc + (int64_t)n * G;
-    bp[r] = bi + (int64_t)n * G;
+    bp[r] = SYM ? sc : bi + (int64_t)n * G;
   }
 
   float acc[R][MT];
@@ -139,18 +150,18 @@ __global__ __launch_bounds__(kWG) void gemv_kernel(const uint32_t* __restrict__ 
       for (int r = 0; r < R; ++r) w[r] = load_nt(rowp[r] + c);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        sbits[r] = sp[r][c >> 1];
-        bbits[r] = bp[r][c >> 1];
+        sbits[r] = sp[r][c >> Fmt<SYM>::kChunkShift];
+        bbits[r] = SYM ? 0 : bp[r][c >> Fmt<SYM>::kChunkShift];
       }
       uint4 wv[R][4];  // dequantized f16 pairs of the chunk, per row and word
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const f16 sv = __builtin_bit_cast(f16, sbits[r]), bv = __builtin_bit_cast(f16, bbits[r]);
         const h2 s2 = {sv, sv}, b2 = {bv, bv};
-        wv[r][0] = word_weights(w[r].x, s2, b2);
-        wv[r][1] = word_weights(w[r].y, s2, b2);
-        wv[r][2] = word_weights(w[r].z, s2, b2);
-        wv[r][3] = word_weights(w[r].w, s2, b2);
+        wv[r][0] = word_weights<SYM>(w[r].x, s2, b2);
+        wv[r][1] = word_weights<SYM>(w[r].y, s2, b2);
+        wv[r][2] = word_weights<SYM>(w[r].z, s2, b2);
+        wv[r][3] = word_weights<SYM>(w[r].w, s2, b2);
       }
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
@@ -211,10 +222,11 @@ struct Consts {
 };
 
 // One word's 8 weights (f16 pairs ordered like the x pairs), accumulated into acc.
+template <bool SYM>
 __device__ __forceinline__ float word_fma(uint32_t w, h2 s2, h2 b2, const uint4& xp, float acc,
                                           const Consts& k) {
   const uint32_t w8 = w >> 8;
-  const h2 o1024 = {(f16)1024.0f, (f16)1024.0f}, o64 = {(f16)64.0f, (f16)64.0f};
+  const h2 o1024 = {(f16)Fmt<SYM>::kLo, (f16)Fmt<SYM>::kLo}, o64 = {(f16)Fmt<SYM>::kHi, (f16)Fmt<SYM>::kHi};
   const h2 q0 = as_h2(and_or(w, k.m_lo, k.mag_lo)) - o1024;   // exact
   const h2 q1 = as_h2(and_or(w, k.m_hi, k.mag_hi)) - o64;
   const h2 q2 = as_h2(and_or(w8, k.m_lo, k.mag_lo)) - o1024;
@@ -234,7 +246,7 @@ struct Block {
 
 // XL: x is staged once per workgroup in LDS (pairs, K * 2 bytes) and read per chunk instead
 // of being held in 16 * NIT registers per lane; fewer registers allow more waves.
-template <int L, int NIT, int R, bool EXACT, bool XL>
+template <int L, int NIT, int R, bool EXACT, bool XL, bool SYM>
 __global__ __launch_bounds__(kWG) void gemv1_kernel(const uint32_t* __restrict__ qw,
                                                     const uint16_t* __restrict__ sc,
                                                     const uint16_t* __restrict__ bi,
@@ -246,11 +258,12 @@ __global__ __launch_bounds__(kWG) void gemv1_kernel(const uint32_t* __restrict__
   const int lane = threadIdx.x % L;
   const int team = blockIdx.x * TEAMS + threadIdx.x / L;
   const int T = gridDim.x * TEAMS;
-  const int C = K / 32;       // 16-byte chunks per row
-  const int G = K / kGroup;   // groups per row
+  constexpr int GS = Fmt<SYM>::kChunkShift;
+  const int C = K / 32;                    // 16-byte chunks per row
+  const int G = K / Fmt<SYM>::kGroupSize;  // groups per row
   const uint4* q4 = reinterpret_cast<const uint4*>(qw) + lane;
-  const uint16_t* sl = sc + (lane >> 1);
-  const uint16_t* bl = bi + (lane >> 1);
+  const uint16_t* sl = sc + (lane >> GS);  // L is a multiple of 4: (lane + jL) >> GS splits
+  const uint16_t* bl = (SYM ? sc : bi) + (lane >> GS);
 
   // Every load is unconditional (block and chunk indices are clamped to valid addresses; a
   // chunk past the end of the row is neutralised in the math by a zero scale and bias, never
@@ -270,8 +283,8 @@ __global__ __launch_bounds__(kWG) void gemv1_kernel(const uint32_t* __restrict__
       for (int j = 0; j < NIT; ++j) {
         const int jc = valid(j) ? j * L : (C - 1 - lane);  // in-row chunk for this lane
         B.w[r][j] = load_nt(p + jc);
-        B.s[r][j] = ps[jc >> 1];
-        B.b[r][j] = pb[jc >> 1];
+        B.s[r][j] = ps[jc >> GS];
+        B.b[r][j] = SYM ? 0u : pb[jc >> GS];
       }
     }
   };
@@ -348,10 +361,10 @@ __global__ __launch_bounds__(kWG) void gemv1_kernel(const uint32_t* __restrict__
         const f16 sv = __builtin_bit_cast(f16, (uint16_t)(B.s[r][j] & sb_on));
         const f16 bv = __builtin_bit_cast(f16, (uint16_t)(B.b[r][j] & sb_on));
         const h2 s2 = {sv, sv}, b2 = {bv, bv};
-        a0[r] = word_fma(B.w[r][j].x, s2, b2, x0, a0[r], k);
-        a1[r] = word_fma(B.w[r][j].y, s2, b2, x1, a1[r], k);
-        a2[r] = word_fma(B.w[r][j].z, s2, b2, x2, a2[r], k);
-        a3[r] = word_fma(B.w[r][j].w, s2, b2, x3, a3[r], k);
+        a0[r] = word_fma<SYM>(B.w[r][j].x, s2, b2, x0, a0[r], k);
+        a1[r] = word_fma<SYM>(B.w[r][j].y, s2, b2, x1, a1[r], k);
+        a2[r] = word_fma<SYM>(B.w[r][j].z, s2, b2, x2, a2[r], k);
+        a3[r] = word_fma<SYM>(B.w[r][j].w, s2, b2, x3, a3[r], k);
       }
     }
 #pragma unroll
@@ -392,7 +405,7 @@ __global__ __launch_bounds__(kWG) void gemv1_kernel(const uint32_t* __restrict__
 
 // per: blocks each team walks; the grid is sized so that teams * per just covers the blocks
 // (no team is left with a surplus block to load and discard).
-template <int L, int NIT, int R, bool XL>
+template <int L, int NIT, int R, bool XL, bool SYM>
 void launch_m1(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
                float* y, int N, int K, int per, hipStream_t st) {
   constexpr int teams = kWG / L;
@@ -402,14 +415,14 @@ void launch_m1(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const u
   const int grid = (T + teams - 1) / teams;
   const size_t lds = XL ? (size_t)K * 2 : 0;
   if (L * NIT == K / 32)
-    hipLaunchKernelGGL((gemv1_kernel<L, NIT, R, true, XL>), dim3(grid), dim3(kWG), lds, st, qw, s,
+    hipLaunchKernelGGL((gemv1_kernel<L, NIT, R, true, XL, SYM>), dim3(grid), dim3(kWG), lds, st, qw, s,
                        b, x, y, N, K, nblocks);
   else
-    hipLaunchKernelGGL((gemv1_kernel<L, NIT, R, false, XL>), dim3(grid), dim3(kWG), lds, st, qw,
+    hipLaunchKernelGGL((gemv1_kernel<L, NIT, R, false, XL, SYM>), dim3(grid), dim3(kWG), lds, st, qw,
                        s, b, x, y, N, K, nblocks);
 }
 
-template <int MT, int R, int P>
+template <int MT, int R, int P, bool SYM>
 void launch_t(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
               int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
   // K-tile: as much of x as fits the LDS budget (64 bytes per 32-element chunk and row).
@@ -421,31 +434,31 @@ void launch_t(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const ui
   const size_t lds = (size_t)MT * ct * 64;
   constexpr int rows_per_wg = (kWG / P) * R;
   const unsigned grid = (unsigned)((N + rows_per_wg - 1) / rows_per_wg);
-  hipLaunchKernelGGL((gemv_kernel<MT, R, P>), dim3(grid), dim3(kWG), lds, st, qw, s, b, x, ldx,
+  hipLaunchKernelGGL((gemv_kernel<MT, R, P, SYM>), dim3(grid), dim3(kWG), lds, st, qw, s, b, x, ldx,
                      y, ldy, M, N, K, KT);
 }
 
-template <int MT, int P>
+template <int MT, int P, bool SYM>
 void launch_r(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
               int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
   // Rows per team: enough workgroups to fill 256 CUs twice before giving a lane more rows.
   constexpr int teams = kWG / P;
   const int64_t want = 512;
   if (MT <= 4 && (int64_t)N / (teams * 4) >= want)
-    launch_t<MT, 4, P>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+    launch_t<MT, 4, P, SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
   else if ((int64_t)N / (teams * 2) >= want)
-    launch_t<MT, 2, P>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+    launch_t<MT, 2, P, SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
   else
-    launch_t<MT, 1, P>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+    launch_t<MT, 1, P, SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
 }
 
-template <int MT>
+template <int MT, bool SYM>
 void launch_p(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
               int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
   if (K / 32 <= 32)
-    launch_r<MT, 32>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+    launch_r<MT, 32, SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
   else
-    launch_r<MT, 64>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+    launch_r<MT, 64, SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
 }
 
 // ------------------------------------------------------------------ 2 <= M <= 16 on MFMA
@@ -481,9 +494,10 @@ __device__ __forceinline__ uint4 pair_up_perm(uint4 d) {
 }
 
 // The 8 weights of word w (f16, nibble order) as an MFMA operand.
+template <bool SYM>
 __device__ __forceinline__ f16x8 word_operand(uint32_t w, h2 s2, h2 b2, const Consts& k) {
   const uint32_t w8 = w >> 8;
-  const h2 o1024 = {(f16)1024.0f, (f16)1024.0f}, o64 = {(f16)64.0f, (f16)64.0f};
+  const h2 o1024 = {(f16)Fmt<SYM>::kLo, (f16)Fmt<SYM>::kLo}, o64 = {(f16)Fmt<SYM>::kHi, (f16)Fmt<SYM>::kHi};
   const h2 q0 = as_h2(and_or(w, k.m_lo, k.mag_lo)) - o1024;   // exact
   const h2 q1 = as_h2(and_or(w, k.m_hi, k.mag_hi)) - o64;
   const h2 q2 = as_h2(and_or(w8, k.m_lo, k.mag_lo)) - o1024;
@@ -506,7 +520,7 @@ struct MfBlock {
   uint4 x[V][4];                // raw x, 32 elements of this lane's chunk
 };
 
-template <int NW, int RB, int V>
+template <int NW, int RB, int V, bool SYM>
 __global__ __launch_bounds__(NW * 64) void gemv_mf_kernel(const uint32_t* __restrict__ qw,
                                                           const uint16_t* __restrict__ sc,
                                                           const uint16_t* __restrict__ bi,
@@ -517,7 +531,8 @@ __global__ __launch_bounds__(NW * 64) void gemv_mf_kernel(const uint32_t* __rest
   __shared__ f32x4 red[NW][RB][64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int i = lane & 15, g = lane >> 4;
-  const int C = K / 32, G = K / kGroup, T = (C + 3) / 4;
+  constexpr int GS = Fmt<SYM>::kChunkShift;
+  const int C = K / 32, G = K / Fmt<SYM>::kGroupSize, T = (C + 3) / 4;
   const int rb0 = blockIdx.x * RB;
   const int t0 = wv * U, tend = min(T, t0 + U);
   const int nb = (U + V - 1) / V;  // blocks per wave, the same for every wave
@@ -530,7 +545,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_mf_kernel(const uint32_t* __rest
     const int n = min(16 * (rb0 + r) + i, N - 1);  // tail rows reload the last row, never stored
     wrow[r] = reinterpret_cast<const uint4*>(qw) + (int64_t)n * C;
     srow[r] = sc + (int64_t)n * G;
-    brow[r] = bi + (int64_t)n * G;
+    brow[r] = (SYM ? sc : bi) + (int64_t)n * G;
   }
   const uint4* xrow = reinterpret_cast<const uint4*>(x + (int64_t)min(i, M - 1) * ldx);
 
@@ -545,8 +560,8 @@ __global__ __launch_bounds__(NW * 64) void gemv_mf_kernel(const uint32_t* __rest
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
         B.w[v][r] = load_nt(wrow[r] + c);
-        B.s[v][r] = srow[r][c >> 1];
-        B.b[v][r] = brow[r][c >> 1];
+        B.s[v][r] = srow[r][c >> GS];
+        B.b[v][r] = SYM ? 0u : brow[r][c >> GS];
       }
     }
   };
@@ -577,7 +592,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_mf_kernel(const uint32_t* __rest
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              word_operand(wd[j], s2, b2, k), as_operand(xp[j].x, xp[j].y, xp[j].z, xp[j].w),
+              word_operand<SYM>(wd[j], s2, b2, k), as_operand(xp[j].x, xp[j].y, xp[j].z, xp[j].w),
               acc[r], 0, 0, 0);
       }
     }
@@ -621,13 +636,13 @@ __global__ __launch_bounds__(NW * 64) void gemv_mf_kernel(const uint32_t* __rest
   }
 }
 
-template <int NW, int RB, int V>
+template <int NW, int RB, int V, bool SYM>
 void launch_mf(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
                int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
   const int T = (K / 32 + 3) / 4;            // steps of 4 chunks (128 elements) per row
   const int U = (T + NW - 1) / NW;           // steps per wave
   const int grid = ((N + 15) / 16 + RB - 1) / RB;
-  hipLaunchKernelGGL((gemv_mf_kernel<NW, RB, V>), dim3(grid), dim3(NW * 64), 0, st, qw, s, b, x,
+  hipLaunchKernelGGL((gemv_mf_kernel<NW, RB, V, SYM>), dim3(grid), dim3(NW * 64), 0, st, qw, s, b, x,
                      ldx, y, ldy, M, N, K, U);
 }
 
@@ -635,63 +650,76 @@ void launch_mf(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const u
 // launches on distinct weights: rows of 2048 take one 64-lane wave per row, two rows per
 // wave and two blocks per team once N is large; rows up to 6144 keep x in registers; longer
 // rows read x from LDS and very long ones loop two blocks per team.
+template <bool SYM>
 bool launch_gemv_m1(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
                     float* y, int N, int K, hipStream_t st) {
   const int C = K / 32;
   if (C <= 32) {
-    launch_m1<32, 1, 1, true>(qw, s, b, x, y, N, K, 1, st);
+    launch_m1<32, 1, 1, true, SYM>(qw, s, b, x, y, N, K, 1, st);
   } else if (C <= 64) {
     if (N >= 8192)
-      launch_m1<64, 1, 2, false>(qw, s, b, x, y, N, K, 2, st);
+      launch_m1<64, 1, 2, false, SYM>(qw, s, b, x, y, N, K, 2, st);
     else if (N > 2048 || N <= 1024)
-      launch_m1<64, 1, 1, false>(qw, s, b, x, y, N, K, 1, st);
+      launch_m1<64, 1, 1, false, SYM>(qw, s, b, x, y, N, K, 1, st);
     else
-      launch_m1<64, 1, 2, false>(qw, s, b, x, y, N, K, 1, st);
+      launch_m1<64, 1, 2, false, SYM>(qw, s, b, x, y, N, K, 1, st);
   } else if (C <= 128) {
-    launch_m1<64, 2, 2, false>(qw, s, b, x, y, N, K, N >= 16384 ? 2 : 1, st);
+    launch_m1<64, 2, 2, false, SYM>(qw, s, b, x, y, N, K, N >= 16384 ? 2 : 1, st);
   } else if (C <= 192) {
-    launch_m1<64, 3, 2, false>(qw, s, b, x, y, N, K, 1, st);
+    launch_m1<64, 3, 2, false, SYM>(qw, s, b, x, y, N, K, 1, st);
   } else if (C <= 256) {
-    launch_m1<64, 4, 1, true>(qw, s, b, x, y, N, K, 1, st);
+    launch_m1<64, 4, 1, true, SYM>(qw, s, b, x, y, N, K, 1, st);
   } else if (C <= 384) {
-    launch_m1<64, 6, 1, true>(qw, s, b, x, y, N, K, 1, st);
+    launch_m1<64, 6, 1, true, SYM>(qw, s, b, x, y, N, K, 1, st);
   } else if (C <= 512) {
-    launch_m1<64, 8, 1, true>(qw, s, b, x, y, N, K, 2, st);
+    launch_m1<64, 8, 1, true, SYM>(qw, s, b, x, y, N, K, 2, st);
   } else {
     return false;
   }
   return true;
 }
 
-}  // namespace
-
 // 3 <= M <= 16 policy, measured on MI355X (back-to-back graph launches on distinct weights):
 // four row blocks per wave once there are >= 768 of them, two from 384, otherwise one with
 // eight waves splitting K when rows are long.  At M = 2 the VALU kernel is still ahead.
+template <bool SYM>
 void launch_gemv_mf(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
                     int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
   const int nrb = (N + 15) / 16;
   if (nrb >= 768)
-    launch_mf<8, 4, 1>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+    launch_mf<8, 4, 1, SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
   else if (nrb >= 384)
-    launch_mf<8, 2, 1>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+    launch_mf<8, 2, 1, SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
   else if (K >= 8192)
-    launch_mf<8, 1, 1>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+    launch_mf<8, 1, 1, SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
   else
-    launch_mf<4, 1, 1>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+    launch_mf<4, 1, 1, SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
 }
 
-void launch_gemv(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
-                 int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
-  if (M <= 1 && launch_gemv_m1(qw, s, b, x, y, N, K, st)) return;
+template <bool SYM>
+void launch_gemv_fmt(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
+                     int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
+  if (M <= 1 && launch_gemv_m1<SYM>(qw, s, b, x, y, N, K, st)) return;
   if (M >= 3) {
-    launch_gemv_mf(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+    launch_gemv_mf<SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
     return;
   }
   if (M <= 1)
-    launch_p<1>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+    launch_p<1, SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
   else
-    launch_p<2>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+    launch_p<2, SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+}
+
+}  // namespace
+
+void launch_gemv(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
+                 int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
+  launch_gemv_fmt<false>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+}
+
+void launch_gemv_sym128(const uint32_t* qw, const uint16_t* s, const uint16_t* x, int64_t ldx,
+                        float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
+  launch_gemv_fmt<true>(qw, s, nullptr, x, ldx, y, ldy, M, N, K, st);
 }
 
 }  // namespace w4

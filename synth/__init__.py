@@ -80,6 +80,16 @@ def w4_weights(n: int, k: int, *, seed: int = 0, workload: int = W_TEST,
     return q, s, b
 
 
+def w4_sym128_weights(n: int, k: int, *, seed: int = 0, workload: int = W_TEST,
+                      layer: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """(q uint8 [n][k], s f16 [n][k/128]) of the symmetric group-128 format: uniform codes and
+    scales |N(0,0.02)| + 1e-3, the affine format's distributions without the bias."""
+    assert k % 128 == 0
+    q = codes(n, k, seed=seed, workload=workload, layer=layer)
+    s = (np.abs(rng(seed, workload, layer, T_S).standard_normal((n, k // 128))) * 0.02 + 1e-3).astype(np.float16)
+    return q, s
+
+
 def activations(m: int, k: int, *, seed: int = 0, workload: int = W_TEST, layer: int = 0) -> np.ndarray:
     """f16 of N(0,1), [m][k]."""
     return rng(seed, workload, layer, T_X).standard_normal((m, k)).astype(np.float16)

@@ -101,6 +101,22 @@ def test_quantize_argument_errors():
     assert q(s=P + 1) == W4_ERR_ALIGN
 
 
+def test_sym128_argument_errors():
+    lib = _lib()
+    g = lambda **kw: lib.w4_gemv_sym128(kw.get("qw", P), kw.get("s", P), P, kw.get("ldx", 256), P, 8,
+                                        kw.get("M", 1), 8, kw.get("K", 256), None)
+    assert g(qw=None) == W4_ERR_NULL
+    assert g(K=192, ldx=192) == W4_ERR_SHAPE     # K % 128 != 0
+    assert g(M=17) == W4_ERR_SHAPE
+    assert g(s=P + 2) == W4_ERR_ALIGN
+    d = lambda **kw: lib.w4_dequant_f16_t_sym128(P, P, kw.get("wt", P), kw.get("ldwt", 8), 8,
+                                                 kw.get("K", 128), None)
+    assert d(wt=None) == W4_ERR_NULL
+    assert d(K=64) == W4_ERR_SHAPE
+    assert d(ldwt=4) == W4_ERR_SHAPE
+    assert d(wt=P + 1) == W4_ERR_ALIGN
+
+
 def test_dequant_and_gemm_argument_errors():
     lib = _lib()
     assert lib.w4_dequant_f16_t(P, P, P, None, 8, 8, 64, None) == W4_ERR_NULL

@@ -123,6 +123,87 @@ def test_quantize_full_matrix_and_roundtrip(w4):
     assert np.array_equal(wt, oracle.dequant_f16_t(qw_ref, s_ref, b_ref))
 
 
+# ------------------------------------------------------------ symmetric group-128 format
+
+
+def sym_case(w4, m, n, k, seed, ldx_pad=0, ldy_pad=0):
+    q, s = synth.w4_sym128_weights(n, k, seed=seed)
+    x = synth.activations(m, k, seed=seed)
+    qw, sd = w4.w4_pack(dev(q)), dev(s)
+    xd = dev(np.pad(x, ((0, 0), (0, ldx_pad))))[:, :k]
+    yd_full = torch.full((m, n + ldy_pad), 7.0, dtype=torch.float32, device="cuda")
+    w4.w4_gemv_sym128(qw, sd, xd, out=yd_full[:, :n])
+    y = to_np(yd_full)
+    assert np.all(y[:, n:] == 7.0), "write outside y"
+    y_ref, bound = oracle.gemv_ref(oracle.pack(q), s, None, x, group=128)
+    ok, worst = oracle.check_bound(y[:, :n], y_ref, bound, RTOL)
+    assert ok, f"(M,N,K)=({m},{n},{k}) worst err/bound {worst:.3g}"
+    return q, s, x, qw, sd, y[:, :n]
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 8, 16])
+@pytest.mark.parametrize("n,k", [(1, 128), (3, 256), (257, 896), (70, 2048), (33, 2176), (5, 11008)])
+def test_sym128_gemv(w4, m, n, k):
+    sym_case(w4, m, n, k, seed=500 * m + n + k, ldx_pad=8 * (m % 2), ldy_pad=m % 3)
+
+
+@pytest.mark.parametrize("m", [1, 2, 16])
+@pytest.mark.parametrize("n,k", [(2560, 2048), (22016, 2048), (2048, 11008)])
+def test_sym128_gemv_equals_affine_kernel_with_bias_minus_8s(w4, m, n, k):
+    # w = s (q - 8) is the affine weight with b = -8 s (exact), so with each scale repeated over
+    # its two 64-groups the affine kernel must give the same bits
+    q, s, x, qw, sd, y = sym_case(w4, m, n, k, seed=n + k + m)
+    s64 = np.repeat(s, 2, axis=1)
+    b64 = (-8.0 * s64.astype(np.float64)).astype(np.float16)
+    y_aff = to_np(w4.w4_gemv(qw, dev(s64), dev(b64), dev(x)))
+    assert np.array_equal(y.view(np.uint32), y_aff.view(np.uint32))
+
+
+@pytest.mark.parametrize("n,k", [(1, 128), (64, 256), (100, 384), (11008, 2048), (2048, 11008)])
+def test_sym128_dequant_bit_exact(w4, n, k):
+    q, s = synth.w4_sym128_weights(n, k, seed=n * 3 + k)
+    got = to_np(w4.w4_dequant_f16_t_sym128(w4.w4_pack(dev(q)), dev(s))).view(np.uint16)
+    assert np.array_equal(got, oracle.dequant_f16_t(oracle.pack(q), s, None, group=128))
+
+
+def test_sym128_worked_values(w4):
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "sym128_handworked.json")) as f:
+        gold = json.load(f)
+    # bit patterns: one row per case, the case's code at k = 5 and code 8 elsewhere
+    cases = gold["dequant"]
+    q = np.full((len(cases), 128), 8, dtype=np.uint8)
+    s = np.zeros((len(cases), 1), dtype=np.uint16)
+    for i, c in enumerate(cases):
+        q[i, 5] = c["q"]
+        s[i, 0] = int(c["s"], 16)
+    wt = to_np(w4.w4_dequant_f16_t_sym128(w4.w4_pack(dev(q)), dev(s.view(np.float16)))).view(np.uint16)
+    for i, c in enumerate(cases):
+        assert int(wt[5, i]) == int(c["w"], 16), c
+        assert int(wt[0, i]) == 0, c
+    # hand-worked GEMVs
+    pats = {"mod16": lambda k: np.arange(k) % 16, "rev16": lambda k: 15 - np.arange(k) % 16}
+    for c in gold["gemv"]:
+        k = c["K"]
+        kind = c["q"].split()
+        qq = (np.full(k, int(kind[1])) if kind[0] == "const" else pats[kind[0]](k)).astype(np.uint8)[None, :]
+        xs = []
+        for p_ in c["x"]:
+            a = p_.split()
+            if a[0] == "const":
+                xs.append(np.full(k, float(a[1])))
+            elif a[0] == "alt":
+                xs.append(np.where(np.arange(k) % 2 == 0, 1.0, -1.0))
+            else:
+                v = np.zeros(k)
+                v[int(a[1])] = 1.0
+                xs.append(v)
+        x = np.stack(xs).astype(np.float16)
+        y = to_np(w4.w4_gemv_sym128(w4.w4_pack(dev(qq)), dev(np.array([c["s"]], dtype=np.float16)), dev(x)))
+        assert np.array_equal(y[:, 0].astype(np.float64), np.array(c["y"])), c["name"]
+
+
 # ----------------------------------------------------------------------------- GEMV
 
 
@@ -450,6 +531,19 @@ def test_topk_strided_rows(w4):
     full = dev(np.pad(logits, ((0, 0), (0, 13))))
     idx, val = w4.logits_argmax_topk(full[:, :6000], 33)
     assert oracle.check_topk_selection(logits, to_np(idx), to_np(val), 33)
+
+
+def test_speculative_verify_argmax(w4):
+    # draft positions verified greedily: 8 rows through the f16 head, then a per-row argmax
+    m, kdim, v = 8, 2048, 151936
+    x = synth.activations(m, kdim, seed=61)
+    head = synth.head_f16(kdim, v, seed=62)
+    logits = w4.gemm_f16(dev(x), dev(head))
+    idx, val = w4.logits_argmax_topk(logits, 1)
+    lg = to_np(logits)
+    assert oracle.check_topk_selection(lg, to_np(idx), to_np(val), 1)
+    c_ref, _ = oracle.gemm_ref(x, head)
+    assert oracle.check_topk_vs_exact(c_ref, to_np(idx), 1)[0]
 
 
 def test_topk_deterministic(w4):
