@@ -495,6 +495,43 @@ def small_m(torch, np, w4, synth, oracle, reps=5):
     return out
 
 
+def int4_head(torch, np, w4, synth, oracle, wl, reps=20):
+    """The LM head stored in the int4 format (group-64 affine, [vocab][hidden] = 151936 x 2048,
+    the pages' 622 MB f16 head at 175 MB) at M = 1: w4_gemv to f32 logits, then the top-40
+    selection, as one graph.  Parity: 64 sampled logits against the fp64 oracle, and the
+    selection bit-exact on the GPU's own logits."""
+    V, K = wl.V, wl.H
+    q, s, b = synth.w4_weights(V, K, seed=0, workload=synth.W_DECODE, layer=990)
+    qw = w4.w4_pack(torch.from_numpy(q).cuda())
+    sd, bd = torch.from_numpy(s).cuda(), torch.from_numpy(b).cuda()
+    logits = torch.empty((1, V), dtype=torch.float32, device="cuda")
+    idx = torch.empty((1, TOPK), dtype=torch.int32, device="cuda")
+    val = torch.empty((1, TOPK), dtype=torch.float32, device="cuda")
+
+    def step():
+        w4.w4_gemv(qw, sd, bd, wl.x_head, out=logits)
+        w4.logits_argmax_topk(logits, TOPK, idx=idx, val=val, workspace=wl.topk_ws)
+    graph = capture(torch, step)
+    graph.replay()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    lg = logits.cpu().numpy()
+    rows = np.sort(np.random.default_rng(11).choice(V, 64, replace=False))
+    y_ref, bound = oracle.gemv_ref(oracle.pack(q[rows]), s[rows], b[rows], wl.x_head_host)
+    ok = oracle.check_bound(lg[:, rows], y_ref, bound)[0]
+    ok &= oracle.check_topk_selection(lg, idx.cpu().numpy(), val.cpu().numpy(), TOPK)
+    nb = gemv_bytes(1, V, K) + 4 * V
+    return {"workload": f"int4 LM head [{V}][{K}] (affine group 64) at M=1 + top-{TOPK}", "us": round(us, 3),
+            "gbps": round(nb / us / 1e3, 1), "frac_hbm": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
+            "head_bytes": gemv_bytes(1, V, K), "parity_ok": bool(ok)}
+
+
 SPEC_ROWS = 8  # draft positions verified per step
 
 
@@ -701,10 +738,12 @@ def main():
         sm = small_m(torch, np, w4, synth, oracle)
         log(f"small-M GEMVs in {time.time() - t0:.1f}s: " + "; ".join(f"{c['workload']} {c['gbps']} GB/s" for c in sm))
 
-    qz = sv = None
+    qz = sv = ih = None
     if not args.no_small_m:
         import oracle
         sv = spec_verify(torch, np, w4, synth, oracle, wl)
+        ih = int4_head(torch, np, w4, synth, oracle, wl)
+        log(f"int4 head + top-{TOPK}: {ih['us']} us ({ih['gbps']} GB/s), parity {'ok' if ih['parity_ok'] else 'FAILED'}")
         log(f"speculative verify: {sv['us']} us, parity {'ok' if sv['parity_ok'] else 'FAILED'}")
         qz = quantize_bench(torch, np, w4, synth, oracle)
         log(f"quantizer: {qz['avg_us']} us, {qz['gbps']} GB/s, parity {'ok' if qz['parity_ok'] else 'FAILED'}")
@@ -757,9 +796,10 @@ def main():
         "small_m": sm,
         "quantize": qz,
         "spec_verify": sv,
+        "int4_head": ih,
     }
     if ((sm is not None and not all(c["parity_ok"] for c in sm)) or (qz is not None and not qz["parity_ok"])
-            or (sv is not None and not sv["parity_ok"])):
+            or (sv is not None and not sv["parity_ok"]) or (ih is not None and not ih["parity_ok"])):
         check = dict(check or {}, ok=False, side_section_fail=True)
         out["parity"] = check
     if check is not None and not check["ok"]:

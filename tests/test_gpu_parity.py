@@ -533,6 +533,21 @@ def test_topk_strided_rows(w4):
     assert oracle.check_topk_selection(logits, to_np(idx), to_np(val), 33)
 
 
+def test_int4_head_topk(w4):
+    # the LM head in the int4 format ([vocab][hidden]), GEMV to logits then top-40
+    v, kdim = 151936, 2048
+    q, s, b = synth.w4_weights(v, kdim, seed=71)
+    x = synth.activations(1, kdim, seed=72)
+    qw, sd, bd = upload_layer(w4, q, s, b)
+    logits = w4.w4_gemv(qw, sd, bd, dev(x))
+    idx, val = w4.logits_argmax_topk(logits, 40)
+    lg = to_np(logits)
+    rows = np.sort(np.random.default_rng(73).choice(v, 256, replace=False))
+    y_ref, bound = oracle.gemv_ref(oracle.pack(q[rows]), s[rows], b[rows], x)
+    assert oracle.check_bound(lg[:, rows], y_ref, bound, RTOL)[0]
+    assert oracle.check_topk_selection(lg, to_np(idx), to_np(val), 40)
+
+
 def test_speculative_verify_argmax(w4):
     # draft positions verified greedily: 8 rows through the f16 head, then a per-row argmax
     m, kdim, v = 8, 2048, 151936
