@@ -214,26 +214,59 @@ __device__ __forceinline__ int count_greater(const uint64_t* list, int n, uint64
 }
 
 // The k largest of this wave's 64 * E distinct keys, sorted descending, into out[0..k).
-// wm: 64 keys of LDS, cand: 64 * E keys of LDS (both private to the wave).
-template <int E>
+// wm: 128 keys of LDS, cand: 64 * E keys of LDS (both private to the wave).
+// Threshold: every lane offers its largest key, or with TWO (k > 48, E > 1) its two largest; the
+// one of the offered keys with exactly k - 1 larger ones among them is T, and at least k
+// keys reach it.  With one key per lane and k near 64, T is about the smallest lane maximum
+// and most keys pass (the rank scan below then goes quadratic); two keys per lane keep the
+// candidates near k.  For smaller k one key per lane already does and costs less.
+template <int E, bool TWO>
 __device__ void wave_topk(const uint64_t (&key)[E], int k, uint64_t* wm, uint64_t* cand,
                           uint64_t* out) {
   const int lane = threadIdx.x & 63;
-  uint64_t mx = key[0];
+  constexpr bool two = E > 1 && TWO;
+  uint64_t m1 = key[0], m2 = 0;
+  if constexpr (two) {
 #pragma unroll
-  for (int e = 1; e < E; ++e) mx = key[e] > mx ? key[e] : mx;
-  wm[lane] = mx;
+    for (int e = 1; e < E; ++e) {
+      const uint64_t hi = key[e] > m1 ? key[e] : m1, lo = key[e] > m1 ? m1 : key[e];
+      m1 = hi;
+      m2 = lo > m2 ? lo : m2;
+    }
+    wm[64 + lane] = m2;
+  } else {
+#pragma unroll
+    for (int e = 1; e < E; ++e) m1 = key[e] > m1 ? key[e] : m1;
+  }
+  wm[lane] = m1;
   wave_sync();
-  int rank = 0;  // LDS reads in batches of 8 x 16 bytes so their latencies overlap
+  int r1 = 0, r2 = 0;  // LDS reads in batches of 8 x 16 bytes so their latencies overlap
 #pragma unroll
-  for (int bt = 0; bt < 4; ++bt) {
+  for (int bt = 0; bt < 4; ++bt) {  // the 64 lane maxima
     uint64_t v[16];
     load16(wm + bt * 16, v);
 #pragma unroll
-    for (int q = 0; q < 16; ++q) rank += v[q] > mx ? 1 : 0;
+    for (int q = 0; q < 16; ++q) {
+      r1 += v[q] > m1 ? 1 : 0;
+      if constexpr (two) r2 += v[q] > m2 ? 1 : 0;
+    }
   }
-  const uint64_t who = __ballot(rank == k - 1);  // exactly one lane: maxima are distinct
-  const uint64_t T = readlane64(mx, (int)__builtin_ctzll(who));
+  if constexpr (two) {
+#pragma unroll
+    for (int bt = 4; bt < 8; ++bt) {  // the 64 second keys
+      uint64_t v[16];
+      load16(wm + bt * 16, v);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        r1 += v[q] > m1 ? 1 : 0;
+        r2 += v[q] > m2 ? 1 : 0;
+      }
+    }
+  }
+  // exactly one offered key has rank k - 1: offered keys are distinct
+  const bool mine = r1 == k - 1 || (two && r2 == k - 1);
+  const uint64_t who = __ballot(mine);
+  const uint64_t T = readlane64(r1 == k - 1 ? m1 : m2, (int)__builtin_ctzll(who));
   int c = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -271,13 +304,15 @@ __device__ void wave_topk(const uint64_t (&key)[E], int k, uint64_t* wm, uint64_
 // merged by rank: survivor i of list w is preceded by the i before it in its own list and by
 // the survivors of the other three lists that are larger (binary search), and lands at that
 // rank if it is below k.
-template <int E>
+constexpr int kGrpWm = 0, kGrpSurv = 512, kGrpCand = 768;  // key offsets in a group's LDS
+
+template <int E, bool TWO>
 __device__ void group_topk(const uint64_t (&key)[E], int k, unsigned char* smem, uint64_t* out) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  uint64_t* wm = reinterpret_cast<uint64_t*>(smem) + w * 64;                // 4 x 64
-  uint64_t* surv = reinterpret_cast<uint64_t*>(smem) + 256;                 // 4 x 64
-  uint64_t* cand = reinterpret_cast<uint64_t*>(smem) + 512 + w * 64 * E;    // 4 x 64E
-  wave_topk<E>(key, k, wm, cand, surv + w * 64);
+  uint64_t* wm = reinterpret_cast<uint64_t*>(smem) + kGrpWm + w * 128;            // 4 x 128
+  uint64_t* surv = reinterpret_cast<uint64_t*>(smem) + kGrpSurv;                  // 4 x 64
+  uint64_t* cand = reinterpret_cast<uint64_t*>(smem) + kGrpCand + w * 64 * E;     // 4 x 64E
+  wave_topk<E, TWO>(key, k, wm, cand, surv + w * 64);
   __syncthreads();
   if (lane < k) {
     const uint64_t x = surv[w * 64 + lane];
@@ -291,12 +326,18 @@ __device__ void group_topk(const uint64_t (&key)[E], int k, unsigned char* smem,
 
 template <int E>
 constexpr size_t group_lds() {
-  return (size_t)(512 + 4 * 64 * E + 64) * 8;  // wm, surv, 4 candidate areas, out
+  return (size_t)(kGrpCand + 4 * 64 * E + 64) * 8;  // wm, surv, 4 candidate areas, out
+}
+
+template <int E>
+__device__ __forceinline__ uint64_t* group_out(unsigned char* smem) {
+  return reinterpret_cast<uint64_t*>(smem) + kGrpCand + 4 * 64 * E;
 }
 
 // Pass 1: the k best keys of logits[m][c*chunk, (c+1)*chunk) into cand[m][c][0:k),
 // chunk = 4 * 64 * E.
-template <int E>
+// TWO: k > 48 (two offered keys per lane in the wave selection, lists stored rotated).
+template <int E, bool TWO>
 __global__ __launch_bounds__(kWG) void wtopk_chunk_kernel(const float* __restrict__ logits,
                                                           int64_t ldl, int V, int k,
                                                           uint64_t* __restrict__ cand) {
@@ -314,15 +355,20 @@ __global__ __launch_bounds__(kWG) void wtopk_chunk_kernel(const float* __restric
     const int v = base + e * 64;  // coalesced: one 256-byte row segment per e and wave
     key[e] = v < V ? make_key(lv[e], (uint32_t)v) : pad_key(~(uint32_t)v & 0x7fffffffu);
   }
-  uint64_t* out = reinterpret_cast<uint64_t*>(smem) + 512 + 4 * 64 * E;
-  group_topk<E>(key, k, smem, out);
+  uint64_t* out = group_out<E>(smem);
+  group_topk<E, TWO>(key, k, smem, out);
+  // With TWO the list is stored rotated by 17 c: pass 2 reads candidate i into lane i % 64, so sorted
+  // lists stored as-is would give lane l the rank-l key of every list (k = 64: lane 63 then
+  // holds a high maximum, the threshold admits almost every key and the rank scan goes
+  // quadratic).  Rotated, each lane sees mixed ranks.  Pass 2 selects by key, so the order of
+  // the stored keys is free.
   uint64_t* dst = cand + ((int64_t)m * nchunks + c) * k;
-  for (int i = threadIdx.x; i < k; i += kWG) dst[i] = out[i];
+  for (int i = threadIdx.x; i < k; i += kWG) dst[TWO ? (i + 17 * c) % k : i] = out[i];
 }
 
 // Pass 2: the k best of a row's ncand keys (from cand, or the logits themselves when
 // cand == nullptr) -> indices and logits.
-template <int E>
+template <int E, bool TWO>
 __global__ __launch_bounds__(kWG) void wtopk_final_kernel(const float* __restrict__ logits,
                                                           int64_t ldl, int V, int k,
                                                           const uint64_t* __restrict__ cand,
@@ -352,8 +398,8 @@ __global__ __launch_bounds__(kWG) void wtopk_final_kernel(const float* __restric
       key[e] = i < ncand ? make_key(lv[e], (uint32_t)i) : pad_key(~(uint32_t)i & 0x7fffffffu);
     }
   }
-  uint64_t* out = reinterpret_cast<uint64_t*>(smem) + 512 + 4 * 64 * E;
-  group_topk<E>(key, k, smem, out);
+  uint64_t* out = group_out<E>(smem);
+  group_topk<E, TWO>(key, k, smem, out);
   for (int i = threadIdx.x; i < k; i += kWG) {
     uint32_t j = key_index(out[i]);
     if (j >= (uint32_t)V) j = (uint32_t)V - 1;  // unreachable for k <= V; keeps reads in bounds
@@ -365,8 +411,12 @@ __global__ __launch_bounds__(kWG) void wtopk_final_kernel(const float* __restric
 template <int E>
 void launch_wfinal(const float* logits, int64_t ldl, int M, int V, int k, const uint64_t* cand,
                    int ncand, int32_t* idx, float* val, hipStream_t st) {
-  hipLaunchKernelGGL((wtopk_final_kernel<E>), dim3(M), dim3(kWG), group_lds<E>(), st, logits, ldl,
-                     V, k, cand, ncand, idx, val);
+  if (k > 48)
+    hipLaunchKernelGGL((wtopk_final_kernel<E, true>), dim3(M), dim3(kWG), group_lds<E>(), st, logits,
+                       ldl, V, k, cand, ncand, idx, val);
+  else
+    hipLaunchKernelGGL((wtopk_final_kernel<E, false>), dim3(M), dim3(kWG), group_lds<E>(), st, logits,
+                       ldl, V, k, cand, ncand, idx, val);
 }
 
 void wfinal_pass(const float* logits, int64_t ldl, int M, int V, int k, const uint64_t* cand,
@@ -426,10 +476,11 @@ void launch_topk(const float* logits, int64_t ldl, int M, int V, int k, int32_t*
                  void* ws, hipStream_t st) {
   static std::once_flag lds_attr;  // the E = 32 wave kernels use more than 64 KB of LDS
   std::call_once(lds_attr, [] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(wtopk_chunk_kernel<32>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)group_lds<32>());
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(wtopk_final_kernel<32>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)group_lds<32>());
+    for (const void* f : {reinterpret_cast<const void*>(wtopk_chunk_kernel<32, false>),
+                          reinterpret_cast<const void*>(wtopk_chunk_kernel<32, true>),
+                          reinterpret_cast<const void*>(wtopk_final_kernel<32, false>),
+                          reinterpret_cast<const void*>(wtopk_final_kernel<32, true>)})
+      (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)group_lds<32>());
   });
   const bool wave = k <= 64;
   if (V <= 4096) {
@@ -443,12 +494,19 @@ void launch_topk(const float* logits, int64_t ldl, int M, int V, int k, int32_t*
   const int nchunks = (V + chunk - 1) / chunk;
   uint64_t* cand = reinterpret_cast<uint64_t*>(ws);
   if (wave) {
-    if (chunk == 4096)
-      hipLaunchKernelGGL((wtopk_chunk_kernel<16>), dim3(nchunks, M), dim3(kWG), group_lds<16>(), st,
-                         logits, ldl, V, k, cand);
+    const dim3 grid(nchunks, M);
+    if (chunk == 4096 && k > 48)
+      hipLaunchKernelGGL((wtopk_chunk_kernel<16, true>), grid, dim3(kWG), group_lds<16>(), st, logits,
+                         ldl, V, k, cand);
+    else if (chunk == 4096)
+      hipLaunchKernelGGL((wtopk_chunk_kernel<16, false>), grid, dim3(kWG), group_lds<16>(), st, logits,
+                         ldl, V, k, cand);
+    else if (k > 48)
+      hipLaunchKernelGGL((wtopk_chunk_kernel<32, true>), grid, dim3(kWG), group_lds<32>(), st, logits,
+                         ldl, V, k, cand);
     else
-      hipLaunchKernelGGL((wtopk_chunk_kernel<32>), dim3(nchunks, M), dim3(kWG), group_lds<32>(), st,
-                         logits, ldl, V, k, cand);
+      hipLaunchKernelGGL((wtopk_chunk_kernel<32, false>), grid, dim3(kWG), group_lds<32>(), st, logits,
+                         ldl, V, k, cand);
     wfinal_pass(logits, ldl, M, V, k, cand, nchunks * k, idx, val, st);
     return;
   }

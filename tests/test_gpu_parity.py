@@ -505,10 +505,25 @@ def topk_case(w4, logits, k):
     (1, 151936, 40), (8, 262144, 64), (1, 262144, 256), (4, 9000, 256), (1, 40000, 1),
     # last chunk nearly empty (padding fills most of its top-k), 8192-logit chunks, odd k
     (2, 12293, 64), (3, 4099, 40), (1, 600000, 64), (1, 70000, 63), (2, 8191, 17),
+    # either side of the switch to two offered keys per lane (k > 48)
+    (1, 300000, 48), (3, 300000, 49), (2, 4096, 49),
 ])
 def test_topk_random(w4, m, v, k):
     logits = (np.random.default_rng(m * v + k).standard_normal((m, v)) * 0.9).astype(np.float32)
     topk_case(w4, logits, k)
+
+
+def test_topk_sorted_and_tied_chunks(w4):
+    # logits whose chunk winners arrive as aligned sorted lists (every 4096-chunk a ramp), and a
+    # long run of ties: the second pass must stay exact whatever the candidates' layout
+    v = 262144
+    ramp = np.tile(np.arange(4096, dtype=np.float32) / 4096.0, v // 4096)
+    ties = np.full(v, 0.5, np.float32)
+    ties[::1000] = 0.75
+    lg = np.stack([ramp, ties, ramp[::-1].copy()])
+    for k in (40, 64):
+        idx, val = w4.logits_argmax_topk(dev(lg), k)
+        assert oracle.check_topk_selection(lg, to_np(idx), to_np(val), k)
 
 
 def test_topk_ties_and_signed_zero(w4):
