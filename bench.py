@@ -532,6 +532,78 @@ def int4_head(torch, np, w4, synth, oracle, wl, reps=20):
             "head_bytes": gemv_bytes(1, V, K), "parity_ok": bool(ok)}
 
 
+def head_sections(torch, np, w4, synth, oracle, wl, reps=10):
+    """The two other head steps of the workloads, each as one graph:
+    * batched classify: the yes/no columns of the decode step's f16 head [2048][151936]
+      (B = H + id, ldb = V) for 16 rows, then a per-row argmax over the 2 logits;
+    * Gemma-12B-shaped head: f16 [3840][262144] (N(0, 0.02), drawn on the GPU from a seeded
+      generator: 2 GB) at M = 1 and M = 8, then the top-64 per row.
+    Parity: the classify logits against the fp64 oracle and its argmax wherever the margin
+    exceeds 1e-2; for the Gemma head 64 sampled logit columns against the oracle and the top-64
+    bit-exact against the host selection on the GPU's own logits."""
+    out = {}
+    stream = torch.cuda.current_stream()
+
+    def timed(step):
+        graph = capture(torch, step)
+        graph.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    m = synth.CLASSIFY_ROWS
+    ids = synth.class_ids(wl.V)
+    x_host = synth.activations(m, wl.H, seed=0, workload=synth.W_CLASSIFY, layer=996)
+    x = torch.from_numpy(x_host).cuda()
+    lg2 = torch.empty((m, 2), dtype=torch.float32, device="cuda")
+    idx = torch.empty((m, 1), dtype=torch.int32, device="cuda")
+    val = torch.empty((m, 1), dtype=torch.float32, device="cuda")
+
+    def classify():
+        for j, i in enumerate(ids):
+            w4.gemm_f16(x, wl.head[:, i:i + 1], out=lg2[:, j:j + 1])
+        w4.logits_argmax_topk(lg2, 1, idx=idx, val=val)
+    us = timed(classify)
+    c_ref, bound = oracle.gemm_ref(x_host, wl.head_host[:, list(ids)])
+    ok = oracle.check_bound(lg2.cpu().numpy(), c_ref, bound)[0] and oracle.check_topk_vs_exact(c_ref, idx.cpu().numpy(), 1)[0]
+    out["classify"] = {"workload": f"batched classify: {m} rows x 2 columns (ids {ids[0]}, {ids[1]}) of the f16 head "
+                                   f"[{wl.H}][{wl.V}] + per-row argmax over 2", "us": round(us, 3), "parity_ok": bool(ok)}
+
+    kd, vg, topk = synth.GEMMA12B_HIDDEN, synth.GEMMA12B_VOCAB, 64
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(12)
+    head = (torch.randn((kd, vg), generator=gen, device="cuda") * 0.02).half()
+    cols = np.sort(np.random.default_rng(13).choice(vg, 64, replace=False))
+    head_cols = head[:, torch.from_numpy(cols).cuda()].cpu().numpy()
+    ws = torch.empty(max(16, w4.topk_workspace_bytes(8, vg, topk)), dtype=torch.uint8, device="cuda")
+    for mm in (1, 8):
+        xg_host = synth.activations(mm, kd, seed=0, workload=synth.W_GEMMA, layer=995 - mm)
+        xg = torch.from_numpy(xg_host).cuda()
+        lg = torch.empty((mm, vg), dtype=torch.float32, device="cuda")
+        gws = torch.empty(max(16, w4.gemm_workspace_bytes(xg, head)), dtype=torch.uint8, device="cuda")
+        gi = torch.empty((mm, topk), dtype=torch.int32, device="cuda")
+        gv = torch.empty((mm, topk), dtype=torch.float32, device="cuda")
+
+        def gemma(xg=xg, lg=lg, gws=gws, gi=gi, gv=gv):
+            w4.gemm_f16(xg, head, out=lg, workspace=gws)
+            w4.logits_argmax_topk(lg, topk, idx=gi, val=gv, workspace=ws)
+        us = timed(gemma)
+        lgh = lg.cpu().numpy()
+        c_ref, bound = oracle.gemm_ref(xg_host, head_cols)
+        ok = oracle.check_bound(lgh[:, cols], c_ref, bound)[0]
+        ok &= oracle.check_topk_selection(lgh, gi.cpu().numpy(), gv.cpu().numpy(), topk)
+        nb = 2 * kd * vg + 2 * mm * kd + 8 * mm * vg
+        out[f"gemma_m{mm}"] = {"workload": f"Gemma-12B-shaped f16 head [{kd}][{vg}] at M={mm} + top-{topk}",
+                               "us": round(us, 3), "gbps": round(nb / us / 1e3, 1),
+                               "frac_hbm": round(nb / us / 1e3 / HBM_PEAK_GBS, 4), "parity_ok": bool(ok)}
+    del head
+    return out
+
+
 SPEC_ROWS = 8  # draft positions verified per step
 
 
@@ -738,11 +810,13 @@ def main():
         sm = small_m(torch, np, w4, synth, oracle)
         log(f"small-M GEMVs in {time.time() - t0:.1f}s: " + "; ".join(f"{c['workload']} {c['gbps']} GB/s" for c in sm))
 
-    qz = sv = ih = None
+    qz = sv = ih = hs = None
     if not args.no_small_m:
         import oracle
         sv = spec_verify(torch, np, w4, synth, oracle, wl)
         ih = int4_head(torch, np, w4, synth, oracle, wl)
+        hs = head_sections(torch, np, w4, synth, oracle, wl)
+        log("heads: " + "; ".join(f"{k_} {v_['us']} us" for k_, v_ in hs.items()))
         log(f"int4 head + top-{TOPK}: {ih['us']} us ({ih['gbps']} GB/s), parity {'ok' if ih['parity_ok'] else 'FAILED'}")
         log(f"speculative verify: {sv['us']} us, parity {'ok' if sv['parity_ok'] else 'FAILED'}")
         qz = quantize_bench(torch, np, w4, synth, oracle)
@@ -797,9 +871,11 @@ def main():
         "quantize": qz,
         "spec_verify": sv,
         "int4_head": ih,
+        "heads": hs,
     }
     if ((sm is not None and not all(c["parity_ok"] for c in sm)) or (qz is not None and not qz["parity_ok"])
-            or (sv is not None and not sv["parity_ok"]) or (ih is not None and not ih["parity_ok"])):
+            or (sv is not None and not sv["parity_ok"]) or (ih is not None and not ih["parity_ok"])
+            or (hs is not None and not all(v_["parity_ok"] for v_ in hs.values()))):
         check = dict(check or {}, ok=False, side_section_fail=True)
         out["parity"] = check
     if check is not None and not check["ok"]:

@@ -555,11 +555,26 @@ __global__ __launch_bounds__(256) void gemm_plain_kernel(const uint16_t* __restr
   float acc[PL_ROWS];
 #pragma unroll
   for (int i = 0; i < PL_ROWS; ++i) acc[i] = 0.f;
-  for (int k = threadIdx.x; k < K; k += 256) {
-    const float b = h2f(B[(int64_t)k * ldb + n]);
+  // PL_KU k-values per thread per round, every load unconditional (clamped row and k, the
+  // clamped terms zeroed through b) so that a round's loads are all in flight together: a
+  // column of B has one element per cache line, and loads behind a branch would wait in turn
+  constexpr int PL_KU = 8;
+  for (int k0 = threadIdx.x; k0 < K; k0 += 256 * PL_KU) {
+    float b[PL_KU];
+    uint16_t a[PL_KU][PL_ROWS];
 #pragma unroll
-    for (int i = 0; i < PL_ROWS; ++i)
-      if (i < rows) acc[i] = __builtin_fmaf(h2f(A[(int64_t)(m0 + i) * lda + k]), b, acc[i]);
+    for (int u = 0; u < PL_KU; ++u) {
+      const int k = min(k0 + u * 256, K - 1);
+      b[u] = h2f(B[(int64_t)k * ldb + n]);
+#pragma unroll
+      for (int i = 0; i < PL_ROWS; ++i) a[u][i] = A[(int64_t)(m0 + min(i, rows - 1)) * lda + k];
+    }
+#pragma unroll
+    for (int u = 0; u < PL_KU; ++u) {
+      const float bu = k0 + u * 256 < K ? b[u] : 0.f;
+#pragma unroll
+      for (int i = 0; i < PL_ROWS; ++i) acc[i] = __builtin_fmaf(h2f(a[u][i]), bu, acc[i]);
+    }
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
