@@ -7,14 +7,16 @@
 //    ("What's inside the engine today").
 //
 // Paths, chosen per call by shape and alignment:
-//  * MFMA (M > 8, K % 32 == 0, 16-byte aligned operands): 256 x 256 block tile, operands
-//    moved HBM -> LDS by LDS DMA through a 4-stage ring, eight waves (two per SIMD) each
-//    owning a 128 x 64 tile of v_mfma_f32_32x32x16_f16; B is read from its [K][N] layout with
-//    transposing LDS reads.  K % 32 != 0 takes a register-staged variant.  Tails: rows of A
+//  * MFMA (M > 8, or M >= 5 with K % 32 == 0; 16-byte aligned operands): 256- or 320-row x
+//    256-column block tiles, operands moved HBM -> LDS by LDS DMA through a 4-stage ring,
+//    eight waves (two per SIMD) each owning a 128 (160) x 64 tile of v_mfma_f32_32x32x16_f16;
+//    up to 32 rows, 32-row tiles with every wave on 32 x 32 (a stream of B, e.g. a head read
+//    by 8 speculative rows).  B is read from its [K][N] layout with transposing LDS reads.  K % 32 != 0 takes a register-staged variant.  Tails: rows of A
 //    and column blocks of B are clamped on load (never stored) and the K tail is zero-filled,
 //    so the MFMA loop itself has no guards.  Too few tiles for the CUs: K is split and the
 //    slices summed in a fixed order by a second kernel.
-//  * small M (M <= 8, decode head): each lane owns 8 contiguous columns and streams B rows
+//  * small M (M <= 4, or M <= 8 with K % 32 != 0; the decode head): each lane owns 8
+//    contiguous columns and streams B rows
 //    with 16-byte loads; the four waves of a workgroup split K and reduce through LDS.  The
 //    A values of a k are wave-uniform scalar loads.
 //  * plain (any other shape or alignment, e.g. one strided column of a head): a workgroup
@@ -242,25 +244,32 @@ __device__ __forceinline__ int b_swz(int k) {
 
 // W4_SYNC with a wave-uniform count of DMA instructions allowed to stay in flight
 __device__ __forceinline__ void dma_sync(int n) {
-  switch (n) {  // per-wave instructions per K-tile (4 or 5) times 0 .. 3 K-tiles
+  switch (n) {  // per-wave instructions per K-tile (2 to 5) times 0 .. 3 K-tiles
     case 24: W4_SYNC(24); break;
     case 16: W4_SYNC(16); break;
     case 15: W4_SYNC(15); break;
     case 12: W4_SYNC(12); break;
     case 10: W4_SYNC(10); break;
+    case 9: W4_SYNC(9); break;
     case 8: W4_SYNC(8); break;
+    case 6: W4_SYNC(6); break;
     case 5: W4_SYNC(5); break;
     case 4: W4_SYNC(4); break;
+    case 3: W4_SYNC(3); break;
+    case 2: W4_SYNC(2); break;
     default: W4_SYNC(0); break;
   }
 }
 
-template <int NW, int BMT>
+// WMW waves along M and NW / WMW along N (two along M for the prefill tiles; one for the
+// 32-row tiles of small M, where every wave takes 32 rows x 32 columns).
+template <int NW, int BMT, int WMW>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_dma_kernel(GemmArgs g) {
-  constexpr int WN = NW / 2;            // waves along N (two along M)
+  constexpr int WN = NW / WMW;          // waves along N
   constexpr int WTN = BN / WN;          // columns per wave
   constexpr int NJ = WTN / 32;          // 32-column MFMA blocks per wave
-  constexpr int WTM = BMT / 2;          // rows per wave
+  constexpr int WTM = BMT / WMW;        // rows per wave
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tiles of whole 32 x 32 blocks");
   constexpr int MI = WTM / 32;          // 32-row MFMA blocks per wave
   constexpr int DI = 16 / NW;           // B DMA instructions per wave and K-tile
   constexpr int AI = BMT / 16;          // A DMA instructions per K-tile (16 rows each)
@@ -370,13 +379,15 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_dma_kernel(GemmArgs g) {
   // the MI + 2 * NJ LDS reads of the next fragments interleaved one-to-one with the first
   // of the MI * NJ MFMAs
   constexpr int RD = MI + 2 * NJ, MF = MI * NJ;
+  constexpr int PAIRS = RD < MF ? RD : MF;
   auto interleave = [&]() {
 #pragma unroll
-    for (int i = 0; i < RD; ++i) {
+    for (int i = 0; i < PAIRS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     }
     if constexpr (MF > RD) __builtin_amdgcn_sched_group_barrier(0x008, MF - RD, 0);
+    if constexpr (RD > MF) __builtin_amdgcn_sched_group_barrier(0x100, RD - MF, 0);
   };
 
   // Pipeline: the DMA runs up to 3 K-tiles ahead into a ring of 4 stages.  Iteration t
@@ -460,6 +471,9 @@ GemmPlan plan_mfma(int64_t M, int64_t N, int64_t K, int bm) {
 // 1570-row prefills take 320 (5 row tiles instead of 7, 2 rounds instead of 3 for 22016
 // columns); the register-staged kernel has 256-row tiles only.
 GemmPlan choose_plan(int64_t M, int64_t N, int64_t K) {
+  // up to 32 rows (with the LDS-DMA kernel): 32-row tiles, every wave 32 x 32, so the B
+  // stream is not spread over mostly padding rows
+  if (M <= 32 && K % DBK == 0) return plan_mfma(M, N, K, 32);
   const GemmPlan p256 = plan_mfma(M, N, K, 256);
   if (K % DBK != 0) return p256;
   const GemmPlan p320 = plan_mfma(M, N, K, 320);
@@ -603,7 +617,10 @@ GemmPath gemm_path(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ld
   const bool vec = K % 8 == 0 && N % 8 == 0 && lda % 8 == 0 && ldb % 8 == 0 && aligned16(A) &&
                    aligned16(B);
   if (!vec) return kGemmPlain;
-  return M > 8 ? kGemmMfma : kGemmSmallM;
+  // 5 <= M <= 8 with K % 32 == 0 streams B faster through 32-row MFMA tiles than through the
+  // VALU small-M kernel (measured on the 2048 x 151936 head); M <= 4 stays on the latter
+  if (M > 8 || (M >= 5 && K % DBK == 0)) return kGemmMfma;
+  return kGemmSmallM;
 }
 
 void launch_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C,
@@ -614,19 +631,23 @@ void launch_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
       std::call_once(lds_attr, [] {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_mfma_kernel),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_dma_kernel<kDmaWaves, 256>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_dma_kernel<kDmaWaves, 256, 2>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)dma_lds(256));
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_dma_kernel<kDmaWaves, 320>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_dma_kernel<kDmaWaves, 320, 2>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)dma_lds(320));
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_dma_kernel<kDmaWaves, 32, 1>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)dma_lds(32));
       });
       const GemmPlan p = choose_plan(M, N, K);
       GemmArgs g{A, B, C, reinterpret_cast<float*>(ws), lda, ldb, ldc, M, N, K,
                  p.tilesM, p.tilesN, p.ksplit, p.kslice};
       const dim3 grid((unsigned)(p.tilesM * p.tilesN * p.ksplit));
-      if (K % DBK == 0 && p.bm == 320)
-        hipLaunchKernelGGL((gemm_dma_kernel<kDmaWaves, 320>), grid, dim3(64 * kDmaWaves), dma_lds(320), st, g);
+      if (K % DBK == 0 && p.bm == 32)
+        hipLaunchKernelGGL((gemm_dma_kernel<kDmaWaves, 32, 1>), grid, dim3(64 * kDmaWaves), dma_lds(32), st, g);
+      else if (K % DBK == 0 && p.bm == 320)
+        hipLaunchKernelGGL((gemm_dma_kernel<kDmaWaves, 320, 2>), grid, dim3(64 * kDmaWaves), dma_lds(320), st, g);
       else if (K % DBK == 0)
-        hipLaunchKernelGGL((gemm_dma_kernel<kDmaWaves, 256>), grid, dim3(64 * kDmaWaves), dma_lds(256), st, g);
+        hipLaunchKernelGGL((gemm_dma_kernel<kDmaWaves, 256, 2>), grid, dim3(64 * kDmaWaves), dma_lds(256), st, g);
       else
         hipLaunchKernelGGL(gemm_mfma_kernel, grid, dim3(256), kGemmLds, st, g);
       if (p.ksplit > 1) {
