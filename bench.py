@@ -532,6 +532,50 @@ def int4_head(torch, np, w4, synth, oracle, wl, reps=20):
             "head_bytes": gemv_bytes(1, V, K), "parity_ok": bool(ok)}
 
 
+def single_gemv(torch, np, w4, synth, oracle, copies=512, reps=5):
+    """The single W4A16 GEMV (M, N, K) = (1, 4864, 896), seed 0: (i) one launch between two
+    events after a synchronize (latency of a lone call), (ii) steady state over `copies`
+    distinct weight copies (1.27 GB, above the last-level cache) as one graph.  Parity: every
+    output of the lone call against the oracle."""
+    n, k = 4864, 896
+    q, s, b = synth.w4_weights(n, k, seed=0, workload=synth.W_SINGLE)
+    x_host = synth.activations(1, k, seed=0, workload=synth.W_SINGLE)
+    qw0 = w4.w4_pack(torch.from_numpy(q).cuda())
+    s0, b0 = torch.from_numpy(s).cuda(), torch.from_numpy(b).cuda()
+    x = torch.from_numpy(x_host).cuda()
+    y = torch.empty((1, n), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        w4.w4_gemv(qw0, s0, b0, x, out=y)
+    lat = []
+    for _ in range(20):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        w4.w4_gemv(qw0, s0, b0, x, out=y)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        lat.append(e0.elapsed_time(e1) * 1e3)
+    y_ref, bound = oracle.gemv_ref(oracle.pack(q), s, b, x_host)
+    ok = oracle.check_bound(y.cpu().numpy(), y_ref, bound)[0]
+    mats = [(qw0.clone(), s0.clone(), b0.clone()) for _ in range(copies)]
+    graph = capture(torch, lambda: [w4.w4_gemv(t[0], t[1], t[2], x, out=y) for t in mats])
+    graph.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+    nb = gemv_bytes(1, n, k)
+    del mats, graph
+    return {"workload": f"single W4A16 GEMV (1, {n}, {k}), seed 0", "bytes": nb,
+            "lone_launch_us_median": round(float(np.median(lat)), 3),
+            "steady_state_us": round(us, 3), "steady_state_gbps": round(nb / us / 1e3, 1),
+            "frac_hbm": round(nb / us / 1e3 / HBM_PEAK_GBS, 4), "copies": copies, "parity_ok": bool(ok)}
+
+
 def head_sections(torch, np, w4, synth, oracle, wl, reps=10):
     """The two other head steps of the workloads, each as one graph:
     * batched classify: the yes/no columns of the decode step's f16 head [2048][151936]
@@ -810,12 +854,15 @@ def main():
         sm = small_m(torch, np, w4, synth, oracle)
         log(f"small-M GEMVs in {time.time() - t0:.1f}s: " + "; ".join(f"{c['workload']} {c['gbps']} GB/s" for c in sm))
 
-    qz = sv = ih = hs = None
+    qz = sv = ih = hs = sg = None
     if not args.no_small_m:
         import oracle
         sv = spec_verify(torch, np, w4, synth, oracle, wl)
         ih = int4_head(torch, np, w4, synth, oracle, wl)
         hs = head_sections(torch, np, w4, synth, oracle, wl)
+        sg = single_gemv(torch, np, w4, synth, oracle)
+        log(f"single GEMV: lone launch {sg['lone_launch_us_median']} us, steady state {sg['steady_state_us']} us "
+            f"({sg['steady_state_gbps']} GB/s)")
         log("heads: " + "; ".join(f"{k_} {v_['us']} us" for k_, v_ in hs.items()))
         log(f"int4 head + top-{TOPK}: {ih['us']} us ({ih['gbps']} GB/s), parity {'ok' if ih['parity_ok'] else 'FAILED'}")
         log(f"speculative verify: {sv['us']} us, parity {'ok' if sv['parity_ok'] else 'FAILED'}")
@@ -872,10 +919,12 @@ def main():
         "spec_verify": sv,
         "int4_head": ih,
         "heads": hs,
+        "single_gemv": sg,
     }
     if ((sm is not None and not all(c["parity_ok"] for c in sm)) or (qz is not None and not qz["parity_ok"])
             or (sv is not None and not sv["parity_ok"]) or (ih is not None and not ih["parity_ok"])
-            or (hs is not None and not all(v_["parity_ok"] for v_ in hs.values()))):
+            or (hs is not None and not all(v_["parity_ok"] for v_ in hs.values()))
+            or (sg is not None and not sg["parity_ok"])):
         check = dict(check or {}, ok=False, side_section_fail=True)
         out["parity"] = check
     if check is not None and not check["ok"]:
