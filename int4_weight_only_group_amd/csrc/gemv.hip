@@ -646,14 +646,188 @@ void launch_mf(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const u
                      ldx, y, ldy, M, N, K, U);
 }
 
-// M = 1 policy (K / 32 = C chunks per row), measured on MI355X with back-to-back graph
-// launches on distinct weights: rows of 2048 take one 64-lane wave per row, two rows per
-// wave and two blocks per team once N is large; rows up to 6144 keep x in registers; longer
-// rows read x from LDS and very long ones loop two blocks per team.
+// ------------------------------------------------------------------ M = 1 on row slices
+// The M = 1 GEMV is bound by its VALU work as much as by HBM: with the weights already in
+// cache the arithmetic alone takes most of a launch.  This kernel cuts the instructions per
+// weight and the per-row overhead:
+//  * Work unit = one row x one slice of 64 chunks (2048 elements) of K: lane l of the wave on
+//    slice j holds chunk 64 j + l of the row, so a load instruction reads 1 KB of one row.
+//    KS = ceil(C / 64) slices of the same R rows run as the KS waves of one workgroup and
+//    their row sums are added through LDS in slice order (deterministic); with KS = 1 a
+//    workgroup holds four independent waves.  Each lane keeps the 32 x values of its chunk
+//    in registers.  Lanes past the row end load a clamped chunk with a zero scale and bias.
+//  * Loads are buffer loads whose row offset is wave-uniform and sits in a scalar register,
+//    so no vector instruction computes an address.
+//  * Codes become exact f16 through the fp8 converter: in the e4m3 encoding a byte holding
+//    0..15 is the number q * 2^-9 exactly (the subnormals and the first normal binade are one
+//    evenly spaced range), so converting with the scale 2^9 yields q.  The word's low
+//    nibbles (w & 0x0F0F0F0F) and high nibbles ((w >> 4) & 0x0F0F0F0F) give the pairs
+//    (q0,q2) (q4,q6) and (q1,q3) (q5,q7): 7 instructions for 8 codes instead of 9, so 15 per
+//    word with the FMA and the dot products.  The symmetric format subtracts 8 (exact) before
+//    its FMA, so both formats pair and sum their products in the same order and give the same
+//    bits where their weights agree (b = -8 s).
+template <bool SYM>
+__device__ __forceinline__ float word_fma_cvt(uint32_t w, h2 s2, h2 b2, const uint4& xp, float acc) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  h2 q0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, false);  // (q0, q2), exact
+  h2 q1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, true);   // (q4, q6)
+  h2 q2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, false);  // (q1, q3)
+  h2 q3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, true);   // (q5, q7)
+  if constexpr (SYM) {  // q - 8, exact
+    const h2 o8 = {(f16)8.0f, (f16)8.0f};
+    q0 -= o8;
+    q1 -= o8;
+    q2 -= o8;
+    q3 -= o8;
+  }
+  acc = dot2(as_u32(__builtin_elementwise_fma(q0, s2, b2)), xp.x, acc);  // one rounding each
+  acc = dot2(as_u32(__builtin_elementwise_fma(q1, s2, b2)), xp.y, acc);
+  acc = dot2(as_u32(__builtin_elementwise_fma(q2, s2, b2)), xp.z, acc);
+  acc = dot2(as_u32(__builtin_elementwise_fma(q3, s2, b2)), xp.w, acc);
+  return acc;
+}
+
+// (x0x1, x2x3, x4x5, x6x7) -> (x0x2, x4x6, x1x3, x5x7): the converter's code order
+__device__ __forceinline__ uint4 pair_up_cvt(uint4 d) {
+  uint4 p;
+  p.x = __builtin_amdgcn_perm(d.y, d.x, 0x05040100u);
+  p.y = __builtin_amdgcn_perm(d.w, d.z, 0x05040100u);
+  p.z = __builtin_amdgcn_perm(d.y, d.x, 0x07060302u);
+  p.w = __builtin_amdgcn_perm(d.w, d.z, 0x07060302u);
+  return p;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* p) {
+  // raw buffer (stride 0), the whole 31-bit offset range; callers keep offsets below 2^31
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, 0x7FFFFFFF, 0x00020000);
+}
+
+template <int R, int KS, bool SYM>
+__global__ __launch_bounds__(KS == 1 ? kWG : KS * 64) void gemv1s_kernel(
+    const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc, const uint16_t* __restrict__ bi,
+    const uint16_t* __restrict__ x, float* __restrict__ y, int N, int K, int nblocks) {
+  __shared__ float red[KS][R];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slice = KS == 1 ? 0 : wave;
+  const int blk = KS == 1 ? (int)blockIdx.x * (kWG / 64) + wave : (int)blockIdx.x;
+  const int C = K / 32, G = K / Fmt<SYM>::kGroupSize;
+  const int c = slice * 64 + lane;
+  const int cc = min(c, C - 1);
+  const uint32_t sb_on = c < C ? 0xFFFFu : 0u;  // past the row end: s = b = 0, every weight 0
+  const __amdgpu_buffer_rsrc_t rq = buffer_of(qw), rs = buffer_of(sc), rb = buffer_of(SYM ? sc : bi);
+  const int voff_q = cc * 16, voff_s = (cc >> Fmt<SYM>::kChunkShift) * 2;
+
+  // x first: loads complete in order, so the math can wait for x without the weights
+  uint4 xv[4];
+  {
+    const uint4* xp = reinterpret_cast<const uint4*>(x + cc * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xv[i] = xp[i];
+  }
+  uint4 w[R];
+  uint32_t sv[R], bv[R];
+  const int b0 = min(blk, nblocks - 1);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int n = min(b0 * R + r, N - 1);  // tail rows reload the last row, never stored
+    w[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, voff_q, n * C * 16, 2));
+    sv[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, voff_s, n * G * 2, 0);
+    bv[r] = SYM ? 0u : __builtin_amdgcn_raw_buffer_load_b16(rb, voff_s, n * G * 2, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (KS == 1 && blk >= nblocks) return;
+
+  uint4 xp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xp[i] = pair_up_cvt(xv[i]);
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const h2 s2 = __builtin_bit_cast(h2, (sv[r] & sb_on) * 0x10001u);
+    const h2 b2 = __builtin_bit_cast(h2, (bv[r] & sb_on) * 0x10001u);
+    float a0 = word_fma_cvt<SYM>(w[r].x, s2, b2, xp[0], 0.f);
+    float a1 = word_fma_cvt<SYM>(w[r].y, s2, b2, xp[1], 0.f);
+    a0 = word_fma_cvt<SYM>(w[r].z, s2, b2, xp[2], a0);
+    a1 = word_fma_cvt<SYM>(w[r].w, s2, b2, xp[3], a1);
+    acc[r] = group_sum<64>(a0 + a1);
+  }
+  if constexpr (KS == 1) {
+    if (lane == 63) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (blk * R + r < N) y[blk * R + r] = acc[r];
+    }
+  } else {
+    if (lane == 63) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) red[slice][r] = acc[r];
+    }
+    __syncthreads();
+    if (wave == 0 && lane < R && blk * R + lane < N) {
+      float v = red[0][lane];
+#pragma unroll
+      for (int j = 1; j < KS; ++j) v += red[j][lane];
+      y[blk * R + lane] = v;
+    }
+  }
+}
+
+template <int R, int KS, bool SYM>
+void launch_m1s(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
+                float* y, int N, int K, hipStream_t st) {
+  const int nblocks = (N + R - 1) / R;
+  const int grid = KS == 1 ? (nblocks + kWG / 64 - 1) / (kWG / 64) : nblocks;
+  hipLaunchKernelGGL((gemv1s_kernel<R, KS, SYM>), dim3(grid), dim3(KS == 1 ? kWG : KS * 64), 0, st, qw,
+                     s, b, x, y, N, K, nblocks);
+}
+
+template <int KS, bool SYM>
+void launch_m1s_r(int R, const uint32_t* qw, const uint16_t* s, const uint16_t* b,
+                  const uint16_t* x, float* y, int N, int K, hipStream_t st) {
+  if (R >= 4)
+    launch_m1s<4, KS, SYM>(qw, s, b, x, y, N, K, st);
+  else if (KS == 1 && R == 3)
+    launch_m1s<3, KS, SYM>(qw, s, b, x, y, N, K, st);
+  else
+    launch_m1s<2, KS, SYM>(qw, s, b, x, y, N, K, st);
+}
+
+// Row-slice policy, measured on MI355X (graph launches on distinct weights): rows per wave
+// from the number of (row, slice) units -- 4 from 30000 units, 3 from 16000 when rows are one
+// slice long, else 2.  Returns false when the shape is not covered (rows of at most 32 chunks,
+// more than 8 slices, or offsets past 2^31 bytes).
+template <bool SYM>
+bool launch_gemv_m1s(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
+                     float* y, int N, int K, hipStream_t st) {
+  const int C = K / 32;
+  const int KS = (C + 63) / 64;
+  if (C <= 32 || KS > 8 || (int64_t)N * C * 16 >= ((int64_t)1 << 31)) return false;
+  const int64_t units = (int64_t)N * KS;
+  const int R = units >= 30000 ? 4 : (units >= 16000 && KS == 1) ? 3 : 2;
+  switch (KS) {
+    case 1: launch_m1s_r<1, SYM>(R, qw, s, b, x, y, N, K, st); break;
+    case 2: launch_m1s_r<2, SYM>(R, qw, s, b, x, y, N, K, st); break;
+    case 3: launch_m1s_r<3, SYM>(R, qw, s, b, x, y, N, K, st); break;
+    case 4: launch_m1s_r<4, SYM>(R, qw, s, b, x, y, N, K, st); break;
+    case 5: launch_m1s_r<5, SYM>(R, qw, s, b, x, y, N, K, st); break;
+    case 6: launch_m1s_r<6, SYM>(R, qw, s, b, x, y, N, K, st); break;
+    case 7: launch_m1s_r<7, SYM>(R, qw, s, b, x, y, N, K, st); break;
+    default: launch_m1s_r<8, SYM>(R, qw, s, b, x, y, N, K, st); break;
+  }
+  return true;
+}
+
+// M = 1 policy for the shapes the row-slice kernel does not cover (K / 32 = C chunks per
+// row), measured on MI355X with back-to-back graph launches on distinct weights: rows of
+// 2048 take one 64-lane wave per row, two rows per wave and two blocks per team once N is
+// large; rows up to 6144 keep x in registers; longer rows read x from LDS and very long
+// ones loop two blocks per team.
 template <bool SYM>
 bool launch_gemv_m1(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
                     float* y, int N, int K, hipStream_t st) {
   const int C = K / 32;
+  if (launch_gemv_m1s<SYM>(qw, s, b, x, y, N, K, st)) return true;
   if (C <= 32) {
     launch_m1<32, 1, 1, true, SYM>(qw, s, b, x, y, N, K, 1, st);
   } else if (C <= 64) {

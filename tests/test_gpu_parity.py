@@ -319,6 +319,50 @@ def test_gemv_matrix_core_edges(w4, m, n, k):
     gemv_case(w4, m, n, k, seed=31 * n + k + m, ldx_pad=8 * (m % 2), ldy_pad=m % 5)
 
 
+def _sampled_rows(n, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([np.arange(min(n, 8)), np.arange(max(0, n - 8), n),
+                                     rng.choice(n, min(n, 48), replace=False)]))
+
+
+# M = 1 runs on row slices of 64 chunks (2048 elements of K), 1 to 8 slices per row in one
+# workgroup, with 2, 3 or 4 rows per wave chosen from the number of (row, slice) units.  These
+# shapes give every slice count, a partly filled last slice, rows-per-wave tails (N not a
+# multiple of the rows per wave) and the unit thresholds of each rows-per-wave choice.
+ROW_SLICE_SHAPES = [(5, 1088), (16001, 2048), (30001, 2048), (101, 2112), (4099, 4160), (1000, 6208),
+                    (7501, 8256), (3, 10304), (33, 13312), (7, 14400), (257, 16384), (1025, 16320)]
+
+
+@pytest.mark.parametrize("n,k", ROW_SLICE_SHAPES)
+def test_gemv_m1_row_slices(w4, n, k):
+    q, s, b = synth.w4_weights(n, k, seed=n + 3 * k)
+    x = synth.activations(1, k, seed=n + 3 * k)
+    qw, sd, bd = upload_layer(w4, q, s, b)
+    y = to_np(w4.w4_gemv(qw, sd, bd, dev(x)))
+    rows = _sampled_rows(n, n + k)
+    y_ref, bound = oracle.gemv_ref(oracle.pack(q[rows]), s[rows], b[rows], x)
+    ok, worst = oracle.check_bound(y[:, rows], y_ref, bound, RTOL)
+    assert ok, f"(1,{n},{k}) worst err/bound {worst:.3g}"
+
+
+@pytest.mark.parametrize("n,k", [(5, 1152), (16001, 2048), (101, 2176), (7501, 8320), (257, 16384)])
+def test_sym128_m1_row_slices_equal_affine_bits(w4, n, k):
+    # the symmetric format on the row-slice kernel: against the oracle on sampled rows, and bit
+    # for bit against the affine kernel with b = -8 s (the same weights)
+    q, s = synth.w4_sym128_weights(n, k, seed=n + k)
+    x = synth.activations(1, k, seed=n + k)
+    qw, sd = w4.w4_pack(dev(q)), dev(s)
+    y = to_np(w4.w4_gemv_sym128(qw, sd, dev(x)))
+    rows = _sampled_rows(n, n + 2 * k)
+    y_ref, bound = oracle.gemv_ref(oracle.pack(q[rows]), s[rows], None, x, group=128)
+    ok, worst = oracle.check_bound(y[:, rows], y_ref, bound, RTOL)
+    assert ok, f"(1,{n},{k}) worst err/bound {worst:.3g}"
+    s64 = np.repeat(s, 2, axis=1)
+    b64 = (-8.0 * s64.astype(np.float64)).astype(np.float16)
+    y_aff = to_np(w4.w4_gemv(qw, dev(s64), dev(b64), dev(x)))
+    assert np.array_equal(y.view(np.uint32), y_aff.view(np.uint32))
+
+
 def test_gemv_deterministic(w4):
     q, s, b = synth.w4_weights(2048, 2048, seed=9)
     x = synth.activations(3, 2048, seed=9)
