@@ -21,6 +21,7 @@
 //    A values of a k are wave-uniform scalar loads.
 //  * plain (any other shape or alignment, e.g. one strided column of a head): a workgroup
 //    per (column, 16 rows), threads split K.
+#include <cmath>
 #include <mutex>
 
 #include "w4_internal.h"
@@ -489,35 +490,58 @@ __device__ __forceinline__ uint32_t half_of(uint4 v, int j) {
 }
 
 // -------------------------------------------------------------------- small-M path
-constexpr int SM_COLS = 512;  // 64 lanes x 8 columns
+// Each lane owns CPL contiguous columns (CPL = 8, 4 or 2: 16-, 8- or 4-byte loads of a B row),
+// so a workgroup covers 64 CPL columns; the launcher picks CPL so that the workgroups spread
+// evenly over the CUs (a head of 151936 columns in 512-column blocks leaves 41 CUs with twice
+// the work of the others).
+template <int CPL>
+struct BRow;  // CPL f16 of one B row, loaded with one non-temporal load
+template <>
+struct BRow<8> {
+  u32x4 v;
+  __device__ __forceinline__ void load(const uint16_t* p) { v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); }
+  __device__ __forceinline__ uint32_t dw(int i) const { return v[i]; }
+};
+template <>
+struct BRow<4> {
+  u32x2 v;
+  __device__ __forceinline__ void load(const uint16_t* p) { v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p)); }
+  __device__ __forceinline__ uint32_t dw(int i) const { return v[i]; }
+};
+template <>
+struct BRow<2> {
+  uint32_t v;
+  __device__ __forceinline__ void load(const uint16_t* p) { v = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p)); }
+  __device__ __forceinline__ uint32_t dw(int) const { return v; }
+};
 
-template <int MT>
+template <int MT, int CPL>
 __global__ __launch_bounds__(256) void gemm_smallm_kernel(const uint16_t* __restrict__ A,
                                                           int64_t lda,
                                                           const uint16_t* __restrict__ B,
                                                           int64_t ldb, float* __restrict__ C,
                                                           int64_t ldc, int M, int N, int K,
                                                           int KS) {
-  __shared__ float red[3][MT][SM_COLS];
+  constexpr int COLS = 64 * CPL;
+  __shared__ float red[3][MT][COLS];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int n = blockIdx.x * SM_COLS + lane * 8;
-  const int nn = min(n, N - 8);  // clamp: columns past N are computed, never stored
+  const int n = blockIdx.x * COLS + lane * CPL;
+  const int nn = min(n, N - CPL);  // clamp: columns past N are computed, never stored
   const int kb = wave * KS;
   const int ke = min(K, kb + KS);
 
-  float acc[MT][8];
+  float acc[MT][CPL];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[m][j] = 0.f;
+    for (int j = 0; j < CPL; ++j) acc[m][j] = 0.f;
 
   const uint16_t* bcol = B + nn;
   for (int k = kb; k < ke; k += 8) {
-    uint4 h[8];
+    BRow<CPL> h[8];
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      h[kk] = load_nt(bcol + (int64_t)(k + kk) * ldb);
+    for (int kk = 0; kk < 8; ++kk) h[kk].load(bcol + (int64_t)(k + kk) * ldb);
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       const int mm = m < M ? m : M - 1;
@@ -526,7 +550,10 @@ __global__ __launch_bounds__(256) void gemm_smallm_kernel(const uint16_t* __rest
       for (int kk = 0; kk < 8; ++kk) {
         const float a = h2f((uint16_t)half_of(a8, kk));
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[m][j] = __builtin_fmaf(h2f((uint16_t)half_of(h[kk], j)), a, acc[m][j]);
+        for (int j = 0; j < CPL; ++j) {
+          const uint32_t d = h[kk].dw(j >> 1);
+          acc[m][j] = __builtin_fmaf(h2f((uint16_t)((j & 1) ? (d >> 16) : (d & 0xFFFFu))), a, acc[m][j]);
+        }
       }
     }
   }
@@ -535,7 +562,7 @@ __global__ __launch_bounds__(256) void gemm_smallm_kernel(const uint16_t* __rest
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) red[wave - 1][m][lane * 8 + j] = acc[m][j];
+      for (int j = 0; j < CPL; ++j) red[wave - 1][m][lane * CPL + j] = acc[m][j];
   }
   __syncthreads();
   if (wave == 0 && n < N) {
@@ -543,15 +570,40 @@ __global__ __launch_bounds__(256) void gemm_smallm_kernel(const uint16_t* __rest
     for (int m = 0; m < MT; ++m) {
       if (m >= M) break;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < CPL; ++j) {
         float v = acc[m][j];
-        v += red[0][m][lane * 8 + j];
-        v += red[1][m][lane * 8 + j];
-        v += red[2][m][lane * 8 + j];
+        v += red[0][m][lane * CPL + j];
+        v += red[1][m][lane * CPL + j];
+        v += red[2][m][lane * CPL + j];
         C[(int64_t)m * ldc + n + j] = v;
       }
     }
   }
+}
+
+template <int MT>
+void launch_smallm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C,
+                   int64_t ldc, int M, int N, int K, hipStream_t st) {
+  const int KS = ((K + 3) / 4 + 7) / 8 * 8;  // k-rows per wave, a multiple of 8
+  // columns per lane: the largest whose busiest CU holds at most 10 % more workgroups than the
+  // average (measured: the 151936-column head 111 -> 92 us at 2 columns per lane; a
+  // 262144-column head is fastest at 8, two workgroups on every CU)
+  int cpl = 2;
+  for (int c : {8, 4}) {
+    const double wgs = (double)((N + 64 * c - 1) / (64 * c));
+    const double per_cu = wgs / 256.0;
+    if (std::ceil(per_cu) <= 1.10 * per_cu) {
+      cpl = c;
+      break;
+    }
+  }
+  const dim3 grid((unsigned)((N + 64 * cpl - 1) / (64 * cpl)));
+  if (cpl == 8)
+    hipLaunchKernelGGL((gemm_smallm_kernel<MT, 8>), grid, dim3(256), 0, st, A, lda, B, ldb, C, ldc, M, N, K, KS);
+  else if (cpl == 4)
+    hipLaunchKernelGGL((gemm_smallm_kernel<MT, 4>), grid, dim3(256), 0, st, A, lda, B, ldb, C, ldc, M, N, K, KS);
+  else
+    hipLaunchKernelGGL((gemm_smallm_kernel<MT, 2>), grid, dim3(256), 0, st, A, lda, B, ldb, C, ldc, M, N, K, KS);
 }
 
 // ------------------------------------------------------------------------ plain path
@@ -660,16 +712,14 @@ void launch_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
       break;
     }
     case kGemmSmallM: {
-      int KS = ((K + 3) / 4 + 7) / 8 * 8;
-      const dim3 grid((unsigned)((N + SM_COLS - 1) / SM_COLS));
       if (M <= 1)
-        hipLaunchKernelGGL(gemm_smallm_kernel<1>, grid, dim3(256), 0, st, A, lda, B, ldb, C, ldc, M, N, K, KS);
+        launch_smallm<1>(A, lda, B, ldb, C, ldc, M, N, K, st);
       else if (M <= 2)
-        hipLaunchKernelGGL(gemm_smallm_kernel<2>, grid, dim3(256), 0, st, A, lda, B, ldb, C, ldc, M, N, K, KS);
+        launch_smallm<2>(A, lda, B, ldb, C, ldc, M, N, K, st);
       else if (M <= 4)
-        hipLaunchKernelGGL(gemm_smallm_kernel<4>, grid, dim3(256), 0, st, A, lda, B, ldb, C, ldc, M, N, K, KS);
+        launch_smallm<4>(A, lda, B, ldb, C, ldc, M, N, K, st);
       else
-        hipLaunchKernelGGL(gemm_smallm_kernel<8>, grid, dim3(256), 0, st, A, lda, B, ldb, C, ldc, M, N, K, KS);
+        launch_smallm<8>(A, lda, B, ldb, C, ldc, M, N, K, st);
       break;
     }
     default: {
