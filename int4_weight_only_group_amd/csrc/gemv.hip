@@ -90,6 +90,50 @@ __device__ __forceinline__ uint4 pair_up(uint4 d) {
   return p;
 }
 
+// Codes of word w as exact f16 pairs through the fp8 converter: in the e4m3 encoding a byte
+// holding 0..15 is the number q * 2^-9 exactly (the subnormals and the first normal binade are
+// one evenly spaced range), so converting with the scale 2^9 yields q.  The low nibbles
+// (w & 0x0F0F0F0F) and high nibbles ((w >> 4) & 0x0F0F0F0F) give the pairs (q0,q2) (q4,q6)
+// and (q1,q3) (q5,q7): 7 instructions for 8 codes (the OR trick takes 9).  The symmetric
+// format subtracts 8 (exact).
+template <bool SYM>
+__device__ __forceinline__ void cvt_codes(uint32_t w, h2& q0, h2& q1, h2& q2, h2& q3) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  q0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, false);  // (q0, q2)
+  q1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, true);   // (q4, q6)
+  q2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, false);  // (q1, q3)
+  q3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, true);   // (q5, q7)
+  if constexpr (SYM) {
+    const h2 o8 = {(f16)8.0f, (f16)8.0f};
+    q0 -= o8;
+    q1 -= o8;
+    q2 -= o8;
+    q3 -= o8;
+  }
+}
+
+// (x0x1, x2x3, x4x5, x6x7) -> (x0x2, x4x6, x1x3, x5x7): the converter's code order
+__device__ __forceinline__ uint4 pair_up_cvt(uint4 d) {
+  uint4 p;
+  p.x = __builtin_amdgcn_perm(d.y, d.x, 0x05040100u);
+  p.y = __builtin_amdgcn_perm(d.w, d.z, 0x05040100u);
+  p.z = __builtin_amdgcn_perm(d.y, d.x, 0x07060302u);
+  p.w = __builtin_amdgcn_perm(d.w, d.z, 0x07060302u);
+  return p;
+}
+
+// One word's 8 weights (one FMA rounding each) dotted with x pairs in the converter's order.
+template <bool SYM>
+__device__ __forceinline__ float word_fma_cvt(uint32_t w, h2 s2, h2 b2, const uint4& xp, float acc) {
+  h2 q0, q1, q2, q3;
+  cvt_codes<SYM>(w, q0, q1, q2, q3);
+  acc = dot2(as_u32(__builtin_elementwise_fma(q0, s2, b2)), xp.x, acc);
+  acc = dot2(as_u32(__builtin_elementwise_fma(q1, s2, b2)), xp.y, acc);
+  acc = dot2(as_u32(__builtin_elementwise_fma(q2, s2, b2)), xp.z, acc);
+  acc = dot2(as_u32(__builtin_elementwise_fma(q3, s2, b2)), xp.w, acc);
+  return acc;
+}
+
 template <int MT, int R, int P, bool SYM>
 __global__ __launch_bounds__(kWG) void gemv_kernel(const uint32_t* __restrict__ qw,
                                                    const uint16_t* __restrict__ sc,
@@ -466,15 +510,16 @@ void launch_p(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const ui
 // top of the 13-operation dequant, so at M = 16 the arithmetic, not HBM, sets its speed.
 // Here the dequantized weights feed v_mfma_f32_16x16x32_f16 instead: D[n][m] += W[n][k] x[m][k]
 // over 16 weight rows n (A operand) and up to 16 activation rows m (B operand), so the only
-// per-row VALU work left is the dequant, shared by every m.
+// per-row VALU work left is the dequant (11 operations per word with the fp8 converter's
+// codes), shared by every m.
 //
 // Lane l = (i = l % 16, g = l / 16) of a wave holds A row i and B column i, k-group g.  At step
 // t it loads the 16-byte chunk c = 4t + g of weight row 16*rb + i (so a load instruction reads
 // 64 contiguous bytes of each of 16 rows) and the same 32 elements of x row min(i, M - 1).  Word
-// j of the chunk dequantizes into one A operand whose 8 f16 sit in the order the nibbles come
-// out of the word, (q0,q4) (q1,q5) (q2,q6) (q3,q7); the B operand holds the x pairs in that same
-// order, so every product pairs a weight with its own x whatever order the matrix core sums
-// the 32 products in.  D column i, rows 4g..4g+3 come back in the lane's 4 accumulators;
+// j of the chunk dequantizes into one A operand whose 8 f16 sit in the order the converter
+// yields the codes, (q0,q2) (q4,q6) (q1,q3) (q5,q7); the B operand holds the x pairs in that
+// same order, so every product pairs a weight with its own x whatever order the matrix core
+// sums the 32 products in.  D column i, rows 4g..4g+3 come back in the lane's 4 accumulators;
 // columns i >= M are computed on a duplicate x row and never stored.
 //
 // A wave streams RB row blocks (16 RB rows) over one K-range: the NW waves of a workgroup split
@@ -483,26 +528,12 @@ void launch_p(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const ui
 // past the row end read a valid address, their scale and bias are zeroed so their weights are
 // exactly 0) and run in two ping-pong blocks of V steps, as in the M = 1 kernel.
 
-// (x0x1, x2x3, x4x5, x6x7) -> (x0x4, x1x5, x2x6, x3x7) with byte permutes
-__device__ __forceinline__ uint4 pair_up_perm(uint4 d) {
-  uint4 p;
-  p.x = __builtin_amdgcn_perm(d.z, d.x, 0x05040100u);
-  p.y = __builtin_amdgcn_perm(d.z, d.x, 0x07060302u);
-  p.z = __builtin_amdgcn_perm(d.w, d.y, 0x05040100u);
-  p.w = __builtin_amdgcn_perm(d.w, d.y, 0x07060302u);
-  return p;
-}
-
-// The 8 weights of word w (f16, nibble order) as an MFMA operand.
+// The 8 weights of word w (f16, the converter's code order) as an MFMA operand.
 template <bool SYM>
-__device__ __forceinline__ f16x8 word_operand(uint32_t w, h2 s2, h2 b2, const Consts& k) {
-  const uint32_t w8 = w >> 8;
-  const h2 o1024 = {(f16)Fmt<SYM>::kLo, (f16)Fmt<SYM>::kLo}, o64 = {(f16)Fmt<SYM>::kHi, (f16)Fmt<SYM>::kHi};
-  const h2 q0 = as_h2(and_or(w, k.m_lo, k.mag_lo)) - o1024;   // exact
-  const h2 q1 = as_h2(and_or(w, k.m_hi, k.mag_hi)) - o64;
-  const h2 q2 = as_h2(and_or(w8, k.m_lo, k.mag_lo)) - o1024;
-  const h2 q3 = as_h2(and_or(w8, k.m_hi, k.mag_hi)) - o64;
-  const h2 r0 = __builtin_elementwise_fma(q0, s2, b2);         // one rounding each
+__device__ __forceinline__ f16x8 word_operand(uint32_t w, h2 s2, h2 b2) {
+  h2 q0, q1, q2, q3;
+  cvt_codes<SYM>(w, q0, q1, q2, q3);
+  const h2 r0 = __builtin_elementwise_fma(q0, s2, b2);  // one rounding each
   const h2 r1 = __builtin_elementwise_fma(q1, s2, b2);
   const h2 r2 = __builtin_elementwise_fma(q2, s2, b2);
   const h2 r3 = __builtin_elementwise_fma(q3, s2, b2);
@@ -566,12 +597,6 @@ __global__ __launch_bounds__(NW * 64) void gemv_mf_kernel(const uint32_t* __rest
     }
   };
 
-  Consts k;
-  k.m_lo = __builtin_amdgcn_readfirstlane(0x000F000Fu);
-  k.m_hi = __builtin_amdgcn_readfirstlane(0x00F000F0u);
-  k.mag_lo = __builtin_amdgcn_readfirstlane(0x64006400u);
-  k.mag_hi = __builtin_amdgcn_readfirstlane(0x54005400u);
-
   f32x4 acc[RB];
 #pragma unroll
   for (int r = 0; r < RB; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -582,7 +607,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_mf_kernel(const uint32_t* __rest
       const uint32_t sb_on = valid(t0 + blk * V + v) ? 0xFFFFu : 0u;
       uint4 xp[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) xp[j] = pair_up_perm(B.x[v][j]);
+      for (int j = 0; j < 4; ++j) xp[j] = pair_up_cvt(B.x[v][j]);
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
         const f16 sv = __builtin_bit_cast(f16, (uint16_t)(B.s[v][r] & sb_on));
@@ -592,7 +617,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_mf_kernel(const uint32_t* __rest
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              word_operand<SYM>(wd[j], s2, b2, k), as_operand(xp[j].x, xp[j].y, xp[j].z, xp[j].w),
+              word_operand<SYM>(wd[j], s2, b2), as_operand(xp[j].x, xp[j].y, xp[j].z, xp[j].w),
               acc[r], 0, 0, 0);
       }
     }
@@ -666,37 +691,6 @@ void launch_mf(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const u
 //    word with the FMA and the dot products.  The symmetric format subtracts 8 (exact) before
 //    its FMA, so both formats pair and sum their products in the same order and give the same
 //    bits where their weights agree (b = -8 s).
-template <bool SYM>
-__device__ __forceinline__ float word_fma_cvt(uint32_t w, h2 s2, h2 b2, const uint4& xp, float acc) {
-  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-  h2 q0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, false);  // (q0, q2), exact
-  h2 q1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, true);   // (q4, q6)
-  h2 q2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, false);  // (q1, q3)
-  h2 q3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, true);   // (q5, q7)
-  if constexpr (SYM) {  // q - 8, exact
-    const h2 o8 = {(f16)8.0f, (f16)8.0f};
-    q0 -= o8;
-    q1 -= o8;
-    q2 -= o8;
-    q3 -= o8;
-  }
-  acc = dot2(as_u32(__builtin_elementwise_fma(q0, s2, b2)), xp.x, acc);  // one rounding each
-  acc = dot2(as_u32(__builtin_elementwise_fma(q1, s2, b2)), xp.y, acc);
-  acc = dot2(as_u32(__builtin_elementwise_fma(q2, s2, b2)), xp.z, acc);
-  acc = dot2(as_u32(__builtin_elementwise_fma(q3, s2, b2)), xp.w, acc);
-  return acc;
-}
-
-// (x0x1, x2x3, x4x5, x6x7) -> (x0x2, x4x6, x1x3, x5x7): the converter's code order
-__device__ __forceinline__ uint4 pair_up_cvt(uint4 d) {
-  uint4 p;
-  p.x = __builtin_amdgcn_perm(d.y, d.x, 0x05040100u);
-  p.y = __builtin_amdgcn_perm(d.w, d.z, 0x05040100u);
-  p.z = __builtin_amdgcn_perm(d.y, d.x, 0x07060302u);
-  p.w = __builtin_amdgcn_perm(d.w, d.z, 0x07060302u);
-  return p;
-}
-
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* p) {
   // raw buffer (stride 0), the whole 31-bit offset range; callers keep offsets below 2^31
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, 0x7FFFFFFF, 0x00020000);
