@@ -67,6 +67,7 @@ struct GemmArgs {
   int64_t lda, ldb, ldc;
   int M, N, K;
   int tilesM, tilesN, ksplit, kslice;
+  int wide;  // C rows take 16-byte stores (C 16-byte aligned, ldc a multiple of 4)
 };
 
 __device__ __forceinline__ void tile_of(const GemmArgs& g, int bid, int& tm, int& tn, int& split) {
@@ -375,7 +376,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_dma_kernel(GemmArgs g) {
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int nj = 0; nj < NJ; ++nj)
-        acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[mi], f.b[nj], acc[mi][nj], 0, 0, 0);
+        acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[nj], f.a[mi], acc[mi][nj], 0, 0, 0);
   };
   // the MI + 2 * NJ LDS reads of the next fragments interleaved one-to-one with the first
   // of the MI * NJ MFMAs
@@ -419,31 +420,54 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_dma_kernel(GemmArgs g) {
   __builtin_amdgcn_sched_barrier(0);
   mma(f1);
 
+  // The MFMAs compute the transposed tile (A and B operands swapped): lane l holds C row
+  // m = l mod 32 of each 32 x 32 block and, for each group q of four accumulators, the
+  // four consecutive columns 8 q + 4 (l / 32) .. + 3 -- one 16-byte store instead of four.
+  // N is a multiple of 8, so a group is either wholly inside N or wholly past it.
   float* out = g.ksplit == 1 ? g.C : g.ws + (int64_t)split * g.M * g.N;
   const int64_t ldo = g.ksplit == 1 ? g.ldc : g.N;
+  const bool wide = g.ksplit > 1 || g.wide;
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int col = n0 + wn * WTN + j * 32 + (lane & 31);
+      const int row = m0 + wm * WTM + i * 32 + (lane & 31);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (row < g.M && col < g.N) out[(int64_t)row * ldo + col] = acc[i][j][r];
+      for (int q = 0; q < 4; ++q) {
+        const int col = n0 + wn * WTN + j * 32 + 8 * q + 4 * (lane >> 5);
+        if (row < g.M && col < g.N) {
+          float* dst = out + (int64_t)row * ldo + col;
+          if (wide) {
+            *reinterpret_cast<f32x4*>(dst) =
+                f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[e] = acc[i][j][4 * q + e];
+          }
+        }
       }
     }
 }
 
-// C[m][n] = sum over s (in order) of ws[s][m][n]
+// C[m][n] = sum over s (in order) of ws[s][m][n], four consecutive elements of a row per
+// thread (N is a multiple of 8); 16-byte stores when C allows them
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws,
                                                             float* __restrict__ C, int64_t ldc,
-                                                            int M, int N, int S) {
-  const int64_t MN = (int64_t)M * N;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < MN; e += (int64_t)gridDim.x * 256) {
-    float v = ws[e];
-    for (int s = 1; s < S; ++s) v += ws[s * MN + e];
-    const int64_t m = e / N, n = e - m * N;
-    C[m * ldc + n] = v;
+                                                            int M, int N, int S, int wide) {
+  const int64_t MN = (int64_t)M * N, MN4 = MN / 4;
+  for (int64_t e4 = (int64_t)blockIdx.x * 256 + threadIdx.x; e4 < MN4; e4 += (int64_t)gridDim.x * 256) {
+    f32x4 v = reinterpret_cast<const f32x4*>(ws)[e4];
+    for (int s = 1; s < S; ++s) v += reinterpret_cast<const f32x4*>(ws + s * MN)[e4];
+    const int64_t e = 4 * e4, m = e / N, n = e - m * N;
+    float* dst = C + m * ldc + n;
+    if (wide) {
+      *reinterpret_cast<f32x4*>(dst) = v;
+    } else {
+      dst[0] = v[0];
+      dst[1] = v[1];
+      dst[2] = v[2];
+      dst[3] = v[3];
+    }
   }
 }
 
@@ -459,8 +483,12 @@ GemmPlan plan_mfma(int64_t M, int64_t N, int64_t K, int bm) {
   const int tiles = p.tilesM * p.tilesN;
   const int kt = (int)((K + BK - 1) / BK);
   int s = 1;
-  // split K while fewer than half the CUs would have a tile, keeping >= 8 K-tiles per slice
-  while (tiles * s * 2 <= 256 && kt / (s * 2) >= 8) s *= 2;
+  // when fewer than half the CUs would have a tile, split K into as many slices as fill the
+  // CUs once, keeping >= 8 K-tiles per slice
+  if (tiles * 2 <= 256) {
+    s = 256 / tiles;
+    while (s > 1 && kt / s < 8) --s;
+  }
   p.ksplit = s;
   p.kslice = ((kt + s - 1) / s) * BK;
   p.ksplit = (int)((K + p.kslice - 1) / p.kslice);
@@ -691,8 +719,9 @@ void launch_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)dma_lds(32));
       });
       const GemmPlan p = choose_plan(M, N, K);
+      const int wide = aligned16(C) && ldc % 4 == 0;
       GemmArgs g{A, B, C, reinterpret_cast<float*>(ws), lda, ldb, ldc, M, N, K,
-                 p.tilesM, p.tilesN, p.ksplit, p.kslice};
+                 p.tilesM, p.tilesN, p.ksplit, p.kslice, wide};
       const dim3 grid((unsigned)(p.tilesM * p.tilesN * p.ksplit));
       if (K % DBK == 0 && p.bm == 32)
         hipLaunchKernelGGL((gemm_dma_kernel<kDmaWaves, 32, 1>), grid, dim3(64 * kDmaWaves), dma_lds(32), st, g);
@@ -703,11 +732,11 @@ void launch_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
       else
         hipLaunchKernelGGL(gemm_mfma_kernel, grid, dim3(256), kGemmLds, st, g);
       if (p.ksplit > 1) {
-        const int64_t MN = (int64_t)M * N;
-        int64_t blocks = (MN + 255) / 256;
+        const int64_t MN4 = (int64_t)M * N / 4;
+        int64_t blocks = (MN4 + 255) / 256;
         if (blocks > 4096) blocks = 4096;
         hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
-                           reinterpret_cast<const float*>(ws), C, ldc, M, N, p.ksplit);
+                           reinterpret_cast<const float*>(ws), C, ldc, M, N, p.ksplit, wide);
       }
       break;
     }
