@@ -747,6 +747,31 @@ def cpu_baseline(np, oracle, synth):
             "seconds": dt}
 
 
+def vendor_gemm(torch, wl, kt, reps=20):
+    """Context only: hipBLASLt (torch.matmul, f16 in and out) on the prefill GEMM shapes, the
+    best of 3 rounds of back-to-back launches, beside gemm_f16's per-launch time (which also
+    writes an f32 C, twice the output bytes)."""
+    res = []
+    stream = torch.cuda.current_stream()
+    for name, a, wt, c, (m, n, k), _, _ in wl.prefill_g:
+        ref = torch.matmul(a, wt)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        best = float("inf")
+        for _ in range(3):
+            e0.record(stream)
+            for _ in range(reps):
+                torch.matmul(a, wt, out=ref)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e3 / reps)
+        ours = kt[("gemm_f16", m, n, k)]["avg_us"]
+        res.append({"gemm": name, "shape_mnk": [m, n, k], "hipblaslt_f16_out_us": round(best, 2),
+                    "gemm_f16_f32_out_us": round(ours, 2), "hipblaslt_over_gemm_f16": round(best / ours, 3)})
+        del ref
+    return res
+
+
 def main():
     args = parse_args()
     if args.traffic_from:
@@ -854,8 +879,11 @@ def main():
         sm = small_m(torch, np, w4, synth, oracle)
         log(f"small-M GEMVs in {time.time() - t0:.1f}s: " + "; ".join(f"{c['workload']} {c['gbps']} GB/s" for c in sm))
 
-    qz = sv = ih = hs = sg = None
+    qz = sv = ih = hs = sg = vg = None
     if not args.no_small_m:
+        vg = vendor_gemm(torch, wl, kt)
+        log("hipBLASLt on the prefill shapes: " + "; ".join(
+            f"{v_['shape_mnk']} {v_['hipblaslt_f16_out_us']} us vs gemm_f16 {v_['gemm_f16_f32_out_us']} us" for v_ in vg))
         import oracle
         sv = spec_verify(torch, np, w4, synth, oracle, wl)
         ih = int4_head(torch, np, w4, synth, oracle, wl)
@@ -920,6 +948,7 @@ def main():
         "int4_head": ih,
         "heads": hs,
         "single_gemv": sg,
+        "vendor_gemm_context": vg,
     }
     if ((sm is not None and not all(c["parity_ok"] for c in sm)) or (qz is not None and not qz["parity_ok"])
             or (sv is not None and not sv["parity_ok"]) or (ih is not None and not ih["parity_ok"])

@@ -459,7 +459,11 @@ def test_gemm_mfma_path(w4, m, n, k):
     gemm_case(w4, m, n, k, seed=m + n + k)
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 8, 8), (3, 1032, 2048), (8, 4096, 256), (5, 520, 3840), (1, 4752, 2048)])
+# The small-M path gives each lane 8, 4 or 2 columns, whichever spreads the workgroups (64
+# lanes x columns each) most evenly over 256 CUs: 131064 columns take 8 (256 workgroups, the
+# last one ragged), 65528 take 4, the others 2.
+@pytest.mark.parametrize("m,n,k", [(1, 8, 8), (3, 1032, 2048), (8, 4096, 256), (5, 520, 3840), (1, 4752, 2048),
+                                   (1, 131064, 64), (4, 131072, 32), (2, 65528, 128), (1, 65536, 72)])
 def test_gemm_small_m_path(w4, m, n, k):
     gemm_case(w4, m, n, k, seed=m + n + k)
 
