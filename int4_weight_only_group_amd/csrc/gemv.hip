@@ -4,28 +4,27 @@
 // "What's inside the engine today": the multi-row decode GEMV whose weight stream is the
 // limit):  y[m][n] = sum_k (s[n][g] q[n][k] + b[n][g]) x[m][k],  g = k / 64.
 //
-// Design for CDNA4 (wave64, HBM-bound):
-//  * A "team" of P lanes (P = 64, or 32 for short rows) owns R output rows.  Lane l of a
-//    team streams 16-byte chunks (32 codes = half a group) c = l, l+P, l+2P, ... of each
-//    of its R rows, so every load instruction of a wave reads P*16 contiguous bytes of one
-//    row and R independent weight streams are in flight per lane.
-//  * x is staged once per workgroup in LDS (per K-tile when M*K is large), with each
-//    8-element block re-ordered into the f16 pairs (x0,x4) (x1,x5) (x2,x6) (x3,x7) that
-//    match the order in which codes come out of a word.
-//  * Codes become f16 without conversion instructions: OR-ing a nibble into the mantissa
-//    of 1024.0 (0x6400) gives exactly 1024 + q; a nibble sitting at bits 4..7 OR-ed into
-//    64.0 (0x5400) gives exactly 64 + q.  So one word w (codes q0..q7) yields
+// Design for CDNA4 (wave64, HBM-bound), three kernels by the number M of activation rows:
+//  * M = 1 with rows longer than 1024 (gemv1s_kernel, "row slices" below): a wave streams
+//    whole 1 KB slices of R rows with buffer loads at scalar row offsets, converts codes to
+//    f16 through the fp8 converter and splits long rows across the waves of a workgroup.
+//  * M = 1 with short rows (gemv1_kernel) and M = 2 (gemv_kernel): a "team" of P lanes
+//    (P = 64, or 32 for short rows) owns R output rows; lane l streams 16-byte chunks (32
+//    codes = half a group) c = l, l+P, ... of each row, so every load instruction reads P*16
+//    contiguous bytes of one row.  x is staged in LDS (or registers), re-ordered into the f16
+//    pairs (x0,x4) (x1,x5) (x2,x6) (x3,x7) that match the order codes come out of a word:
+//    OR-ing a nibble into the mantissa of 1024.0 (0x6400) gives exactly 1024 + q, a nibble at
+//    bits 4..7 OR-ed into 64.0 (0x5400) gives exactly 64 + q, so one word w yields
 //      (w & 0x000F000F) | 0x64006400 = (1024+q0, 1024+q4)
 //      (w & 0x00F000F0) | 0x54005400 = (  64+q1,   64+q5)
-//    and the same on w >> 8 for (q2,q6), (q3,q7).  A packed f16 subtract removes the
-//    offset exactly, a packed f16 FMA forms w = s q + b with one rounding (the same value
-//    the prefill scratch holds), and v_dot2_f32_f16 accumulates w*x in f32 (the f16
-//    products are exact in f32).  Every term's error is thus relative to |w x|, which keeps
-//    each output within 2e-3 * sum_k |w x| (and exactly 0 when every w x is 0), at 17 VALU
-//    operations per 8 weights, shared by all M activation rows except the 4 dot products.
-//  * Each team reduces its lanes with cross-lane shuffles; one lane stores y.
-//  * From M = 3 rows of x on, the dequantized words feed the matrix cores instead
-//    (gemv_mf_kernel below): the dequant is then the only VALU work per weight.
+//    and the same on w >> 8 for (q2,q6), (q3,q7); a packed f16 subtract removes the offset
+//    exactly.
+//  * 3 <= M <= 16 (gemv_mf_kernel): dequantized words feed the matrix cores.
+// In every kernel a packed f16 FMA forms w = s q + b with one rounding (the value the
+// prefill scratch holds) and the products w*x are exact in f32 and summed in f32, blockwise.
+// Every term's error is thus relative to |w x|, which keeps each output within
+// 2e-3 * sum_k |w x| (and exactly 0 when every w x is 0).  Rows reduce across lanes with DPP
+// moves; one lane stores y.
 #include "w4_internal.h"
 
 namespace w4 {
@@ -692,7 +691,7 @@ void launch_mf(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const u
 //    its FMA, so both formats pair and sum their products in the same order and give the same
 //    bits where their weights agree (b = -8 s).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* p) {
-  // raw buffer (stride 0), the whole 31-bit offset range; callers keep offsets below 2^31
+  // raw buffer (stride 0) over the 31-bit offset range from p; offsets stay far below it
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, 0x7FFFFFFF, 0x00020000);
 }
 
@@ -709,7 +708,6 @@ __global__ __launch_bounds__(KS == 1 ? kWG : KS * 64) void gemv1s_kernel(
   const int c = slice * 64 + lane;
   const int cc = min(c, C - 1);
   const uint32_t sb_on = c < C ? 0xFFFFu : 0u;  // past the row end: s = b = 0, every weight 0
-  const __amdgpu_buffer_rsrc_t rq = buffer_of(qw), rs = buffer_of(sc), rb = buffer_of(SYM ? sc : bi);
   const int voff_q = cc * 16, voff_s = (cc >> Fmt<SYM>::kChunkShift) * 2;
 
   // x first: loads complete in order, so the math can wait for x without the weights
@@ -719,15 +717,20 @@ __global__ __launch_bounds__(KS == 1 ? kWG : KS * 64) void gemv1s_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) xv[i] = xp[i];
   }
+  // the buffers start at this wave's first row, so the scalar offsets stay below R rows
   uint4 w[R];
   uint32_t sv[R], bv[R];
   const int b0 = min(blk, nblocks - 1);
+  const int64_t row0 = (int64_t)b0 * R;
+  const __amdgpu_buffer_rsrc_t rq = buffer_of(qw + row0 * (K / 8));
+  const __amdgpu_buffer_rsrc_t rs = buffer_of(sc + row0 * G);
+  const __amdgpu_buffer_rsrc_t rb = buffer_of((SYM ? sc : bi) + row0 * G);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int n = min(b0 * R + r, N - 1);  // tail rows reload the last row, never stored
-    w[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, voff_q, n * C * 16, 2));
-    sv[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, voff_s, n * G * 2, 0);
-    bv[r] = SYM ? 0u : __builtin_amdgcn_raw_buffer_load_b16(rb, voff_s, n * G * 2, 0);
+    const int dn = min(b0 * R + r, N - 1) - b0 * R;  // tail rows reload the last row, never stored
+    w[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, voff_q, dn * C * 16, 2));
+    sv[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, voff_s, dn * G * 2, 0);
+    bv[r] = SYM ? 0u : __builtin_amdgcn_raw_buffer_load_b16(rb, voff_s, dn * G * 2, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
   if (KS == 1 && blk >= nblocks) return;
@@ -790,13 +793,13 @@ void launch_m1s_r(int R, const uint32_t* qw, const uint16_t* s, const uint16_t* 
 // Row-slice policy, measured on MI355X (graph launches on distinct weights): rows per wave
 // from the number of (row, slice) units -- 4 from 30000 units, 3 from 16000 when rows are one
 // slice long, else 2.  Returns false when the shape is not covered (rows of at most 32 chunks,
-// more than 8 slices, or offsets past 2^31 bytes).
+// or more than 8 slices).
 template <bool SYM>
 bool launch_gemv_m1s(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
                      float* y, int N, int K, hipStream_t st) {
   const int C = K / 32;
   const int KS = (C + 63) / 64;
-  if (C <= 32 || KS > 8 || (int64_t)N * C * 16 >= ((int64_t)1 << 31)) return false;
+  if (C <= 32 || KS > 8) return false;
   const int64_t units = (int64_t)N * KS;
   const int R = units >= 30000 ? 4 : (units >= 16000 && KS == 1) ? 3 : 2;
   switch (KS) {
@@ -812,39 +815,18 @@ bool launch_gemv_m1s(const uint32_t* qw, const uint16_t* s, const uint16_t* b, c
   return true;
 }
 
-// M = 1 policy for the shapes the row-slice kernel does not cover (K / 32 = C chunks per
-// row), measured on MI355X with back-to-back graph launches on distinct weights: rows of
-// 2048 take one 64-lane wave per row, two rows per wave and two blocks per team once N is
-// large; rows up to 6144 keep x in registers; longer rows read x from LDS and very long
-// ones loop two blocks per team.
+// M = 1: rows of more than 32 chunks (K > 1024) and up to 8 slices (K <= 16384) on row
+// slices; shorter rows on 32-lane teams of the OR-trick kernel (one chunk per lane, x in
+// LDS); longer rows fall through to the general kernel.
 template <bool SYM>
 bool launch_gemv_m1(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
                     float* y, int N, int K, hipStream_t st) {
-  const int C = K / 32;
   if (launch_gemv_m1s<SYM>(qw, s, b, x, y, N, K, st)) return true;
-  if (C <= 32) {
+  if (K / 32 <= 32) {
     launch_m1<32, 1, 1, true, SYM>(qw, s, b, x, y, N, K, 1, st);
-  } else if (C <= 64) {
-    if (N >= 8192)
-      launch_m1<64, 1, 2, false, SYM>(qw, s, b, x, y, N, K, 2, st);
-    else if (N > 2048 || N <= 1024)
-      launch_m1<64, 1, 1, false, SYM>(qw, s, b, x, y, N, K, 1, st);
-    else
-      launch_m1<64, 1, 2, false, SYM>(qw, s, b, x, y, N, K, 1, st);
-  } else if (C <= 128) {
-    launch_m1<64, 2, 2, false, SYM>(qw, s, b, x, y, N, K, N >= 16384 ? 2 : 1, st);
-  } else if (C <= 192) {
-    launch_m1<64, 3, 2, false, SYM>(qw, s, b, x, y, N, K, 1, st);
-  } else if (C <= 256) {
-    launch_m1<64, 4, 1, true, SYM>(qw, s, b, x, y, N, K, 1, st);
-  } else if (C <= 384) {
-    launch_m1<64, 6, 1, true, SYM>(qw, s, b, x, y, N, K, 1, st);
-  } else if (C <= 512) {
-    launch_m1<64, 8, 1, true, SYM>(qw, s, b, x, y, N, K, 2, st);
-  } else {
-    return false;
+    return true;
   }
-  return true;
+  return false;
 }
 
 // 3 <= M <= 16 policy, measured on MI355X (back-to-back graph launches on distinct weights):
