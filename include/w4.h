@@ -137,9 +137,9 @@ int w4_dequant_f16_t_sym128(const uint32_t* qw, const uint16_t* scales, uint16_t
  *   A f16 [M][K] (row stride lda), B f16 [K][N] (row stride ldb, N contiguous),
  *   C f32 [M][N] (row stride ldc).
  * Requires M, N, K >= 1, lda >= K, ldb >= N, ldc >= N; A, B 2-byte aligned, C 4-byte
- * aligned.  M >= 9, and M >= 5 with K % 32 == 0, use matrix cores (needs K % 8 == 0, N % 8 == 0,
- * lda and ldb multiples of 8, A and B 16-byte aligned; M <= 32 in 32-row tiles that stream B
- * once); other M <= 8 with N % 8 == 0 and aligned B stream B once on the vector ALUs;
+ * aligned.  M >= 9 uses matrix cores (needs K % 8 == 0, N % 8 == 0, lda and ldb multiples
+ * of 8, A and B 16-byte aligned; M <= 32 in 32-row tiles that stream B once); M <= 8 with
+ * the same layout streams B once on the vector ALUs;
  * any other shape or alignment (e.g. one column of a head, B = H + id, ldb = V) takes a
  * plain path.  Per output within 2e-3 * sum_k |A[m][k] B[k][n]| of the exact sum; the result
  * is deterministic.  Workspace: shapes whose output tiles would leave most of the 256 CUs

@@ -7,18 +7,19 @@
 //    ("What's inside the engine today").
 //
 // Paths, chosen per call by shape and alignment:
-//  * MFMA (M > 8, or M >= 5 with K % 32 == 0; 16-byte aligned operands): 256- or 320-row x
+//  * MFMA (M > 8; 16-byte aligned operands): 256- or 320-row x
 //    256-column block tiles, operands moved HBM -> LDS by LDS DMA through a 4-stage ring,
 //    eight waves (two per SIMD) each owning a 128 (160) x 64 tile of v_mfma_f32_32x32x16_f16;
 //    up to 32 rows, 32-row tiles with every wave on 32 x 32 (a stream of B, e.g. a head read
-//    by 8 speculative rows).  B is read from its [K][N] layout with transposing LDS reads.  K % 32 != 0 takes a register-staged variant.  Tails: rows of A
+//    by 16 rows).  B is read from its [K][N] layout with transposing LDS reads.  K % 32 != 0
+//    takes a register-staged variant.  Tails: rows of A
 //    and column blocks of B are clamped on load (never stored) and the K tail is zero-filled,
 //    so the MFMA loop itself has no guards.  Too few tiles for the CUs: K is split and the
 //    slices summed in a fixed order by a second kernel.
-//  * small M (M <= 4, or M <= 8 with K % 32 != 0; the decode head): each lane owns 8
-//    contiguous columns and streams B rows
-//    with 16-byte loads; the four waves of a workgroup split K and reduce through LDS.  The
-//    A values of a k are wave-uniform scalar loads.
+//  * small M (M <= 8: the decode head, speculative-verify rows): each lane owns 8, 4 or 2
+//    contiguous columns and streams B rows with 16-, 8- or 4-byte loads; byte permutes pair
+//    the values of two k and v_dot2_f32_f16 multiplies them with the wave-uniform A pair; the
+//    four waves of a workgroup split K and reduce through LDS.
 //  * plain (any other shape or alignment, e.g. one strided column of a head): a workgroup
 //    per (column, 16 rows), threads split K.
 #include <cmath>
@@ -565,24 +566,34 @@ __global__ __launch_bounds__(256) void gemm_smallm_kernel(const uint16_t* __rest
 #pragma unroll
     for (int j = 0; j < CPL; ++j) acc[m][j] = 0.f;
 
+  // Eight k-rows per step.  Byte permutes pair each column's values of rows k and k + 1
+  // (one permute per two values), and v_dot2_f32_f16 multiplies such a pair with the pair
+  // (A[m][k], A[m][k + 1]), wave-uniform: one instruction per two products and row of A.
   const uint16_t* bcol = B + nn;
   for (int k = kb; k < ke; k += 8) {
     BRow<CPL> h[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) h[kk].load(bcol + (int64_t)(k + kk) * ldb);
+    uint32_t pr[4][CPL];  // pr[kp][j] = (B[k + 2 kp][j], B[k + 2 kp + 1][j])
+#pragma unroll
+    for (int kp = 0; kp < 4; ++kp)
+#pragma unroll
+      for (int j2 = 0; j2 < CPL / 2; ++j2) {
+        const uint32_t lo = h[2 * kp].dw(j2), hi = h[2 * kp + 1].dw(j2);
+        pr[kp][2 * j2] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+        pr[kp][2 * j2 + 1] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+      }
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       const int mm = m < M ? m : M - 1;
       const uint4 a8 = *reinterpret_cast<const uint4*>(A + (int64_t)mm * lda + k);
+      const uint32_t ap[4] = {a8.x, a8.y, a8.z, a8.w};  // (A[m][k + 2 kp], A[m][k + 2 kp + 1])
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const float a = h2f((uint16_t)half_of(a8, kk));
+      for (int kp = 0; kp < 4; ++kp)
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-          const uint32_t d = h[kk].dw(j >> 1);
-          acc[m][j] = __builtin_fmaf(h2f((uint16_t)((j & 1) ? (d >> 16) : (d & 0xFFFFu))), a, acc[m][j]);
-        }
-      }
+        for (int j = 0; j < CPL; ++j)
+          acc[m][j] = __builtin_amdgcn_fdot2(__builtin_bit_cast(hf16x2, pr[kp][j]),
+                                             __builtin_bit_cast(hf16x2, ap[kp]), acc[m][j], false);
     }
   }
 
@@ -697,9 +708,9 @@ GemmPath gemm_path(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ld
   const bool vec = K % 8 == 0 && N % 8 == 0 && lda % 8 == 0 && ldb % 8 == 0 && aligned16(A) &&
                    aligned16(B);
   if (!vec) return kGemmPlain;
-  // 5 <= M <= 8 with K % 32 == 0 streams B faster through 32-row MFMA tiles than through the
-  // VALU small-M kernel (measured on the 2048 x 151936 head); M <= 4 stays on the latter
-  if (M > 8 || (M >= 5 && K % DBK == 0)) return kGemmMfma;
+  // up to 8 rows the VALU kernel (dot2 over pairs of k) streams B faster than 32-row MFMA tiles
+  // (measured at M = 8: 2048 x 151936 head 100 vs 114 us, 3840 x 262144 head 295 vs 346 us)
+  if (M > 8) return kGemmMfma;
   return kGemmSmallM;
 }
 
