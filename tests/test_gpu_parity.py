@@ -305,7 +305,7 @@ WORKLOAD_SHAPES = sorted({(n, k) for _, n, k in synth.QWEN25_3B_LAYER}
 
 
 @pytest.mark.parametrize("n,k", WORKLOAD_SHAPES)
-@pytest.mark.parametrize("m", [1, 8, 16])
+@pytest.mark.parametrize("m", [1, 2, 8, 16])
 def test_gemv_workload_shapes_full(w4, m, n, k):
     gemv_case(w4, m, n, k, seed=n * 7 + k + m)
 
