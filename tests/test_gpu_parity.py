@@ -231,6 +231,14 @@ def test_gemv_small_shapes(w4, m, n, k):
     gemv_case(w4, m, n, k, seed=1000 * m + n + k)
 
 
+@pytest.mark.parametrize("m", [1, 2, 3])
+@pytest.mark.parametrize("n,k", [(37, 16448), (9, 20480)])
+def test_gemv_rows_past_16384(w4, m, n, k):
+    # rows of more than 8 slices of 2048 take the general team kernel (M <= 2) or the matrix
+    # cores (M >= 3)
+    gemv_case(w4, m, n, k, seed=7 * n + k + m, ldx_pad=8 * (m % 2), ldy_pad=m % 3)
+
+
 def test_gemv_strided_x_and_y(w4):
     gemv_case(w4, 3, 129, 384, seed=5, ldx_pad=24, ldy_pad=5)
     gemv_case(w4, 1, 64, 1024, seed=6, ldx_pad=8, ldy_pad=1)
