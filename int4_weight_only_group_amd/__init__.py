@@ -51,6 +51,10 @@ def _dev(t: torch.Tensor, name: str, dtype: torch.dtype) -> None:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be on the GPU")
+    if t.device.index != torch.cuda.current_device():
+        # the library launches on the current device; a pointer of another one would fault
+        raise ValueError(f"{name} is on {t.device}, but the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
 
 
 def _rowmajor(t: torch.Tensor, name: str) -> int:

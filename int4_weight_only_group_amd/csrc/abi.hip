@@ -14,11 +14,11 @@ inline bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline bool al4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 inline bool al2(const void* p) { return ((uintptr_t)p & 1u) == 0; }
 
-std::atomic<int> g_device_ok[64];  // 0 unknown, 1 gfx950, -1 other
+std::atomic<int> g_device_ok[w4::kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
 
 int check_device() {
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= w4::kMaxDevices) {
     (void)hipGetLastError();
     return W4_ERR_DEVICE;
   }

@@ -718,8 +718,8 @@ void launch_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                  int64_t ldc, int M, int N, int K, void* ws, hipStream_t st) {
   switch (gemm_path(A, lda, B, ldb, M, N, K)) {
     case kGemmMfma: {
-      static std::once_flag lds_attr;
-      std::call_once(lds_attr, [] {
+      static std::once_flag lds_attr[kMaxDevices];
+      once_per_device(lds_attr, [] {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_mfma_kernel),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_dma_kernel<kDmaWaves, 256, 2>),

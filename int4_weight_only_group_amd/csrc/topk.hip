@@ -474,8 +474,8 @@ size_t topk_ws_bytes(int64_t M, int64_t V, int k) {
 
 void launch_topk(const float* logits, int64_t ldl, int M, int V, int k, int32_t* idx, float* val,
                  void* ws, hipStream_t st) {
-  static std::once_flag lds_attr;  // the E = 32 wave kernels use more than 64 KB of LDS
-  std::call_once(lds_attr, [] {
+  static std::once_flag lds_attr[kMaxDevices];  // the E = 32 wave kernels use more than 64 KB of LDS
+  once_per_device(lds_attr, [] {
     for (const void* f : {reinterpret_cast<const void*>(wtopk_chunk_kernel<32, false>),
                           reinterpret_cast<const void*>(wtopk_chunk_kernel<32, true>),
                           reinterpret_cast<const void*>(wtopk_final_kernel<32, false>),

@@ -6,6 +6,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <utility>
+
 namespace w4 {
 
 typedef _Float16 f16;
@@ -77,5 +80,18 @@ int topk_chunk(int64_t V, int k);        // 0 when the shape is unsupported
 size_t topk_ws_bytes(int64_t M, int64_t V, int k);
 void launch_topk(const float* logits, int64_t ldl, int M, int V, int k, int32_t* idx, float* val,
                  void* ws, hipStream_t st);
+
+// Runs f once for the current device.  Function attributes such as the dynamic LDS limit are
+// set per device, so a process that launches on several GPUs sets them on each.
+constexpr int kMaxDevices = 64;
+template <class F>
+void once_per_device(std::once_flag (&flags)[kMaxDevices], F&& f) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    dev = 0;
+  }
+  std::call_once(flags[dev], std::forward<F>(f));
+}
 
 }  // namespace w4
