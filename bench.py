@@ -17,8 +17,11 @@ N*K/2 codes + N*K/16 scales/biases + 2*M*K x + 4*M*N y per GEMV) and, beside it,
 prefill's dequant+GEMM TFLOP/s (2*M*N*K per GEMM over the phase's wall time), each as a
 fraction of MI355X's 8 TB/s HBM and 2.5 PFLOP/s dense f16.  `roofline` is the dominant
 GEMV kernel's own rate from per-launch HIP events; `cpu_baseline` times the CPU oracle on a
-bounded sample of the same workload.  Outputs of the timed steps are re-checked against the
-oracle on sampled rows before anything is printed.
+bounded sample of the same workload.  `stats` gives, per phase, the median of the timed
+steps and its 95 % bootstrap interval (2000 resamples, as in the timing method of
+"ENGINEERING_10X_RESEARCH", "Controls"); `context` a 1 GiB device copy's bandwidth and the
+clocks rocm-smi reports after timing (context, not denominators).  Outputs of the timed
+steps are re-checked against the oracle on sampled rows before anything is printed.
 """
 
 from __future__ import annotations
@@ -43,7 +46,7 @@ def parse_args():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--eager", action="store_true", help="launch every kernel from Python instead of replaying graphs")
     p.add_argument("--unfused", action="store_true", help="run q,k,v and gate,up as separate GEMVs (7 per layer)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -184,6 +187,49 @@ def capture(torch, fn):
         fn()
     torch.cuda.synchronize()
     return g
+
+
+def median_ci(np, samples, reps=2000, seed=0):
+    """Median of per-round samples and its 95 % bootstrap interval (reps resamples with
+    replacement, percentile method, fixed seed)."""
+    a = np.asarray(samples, dtype=np.float64)
+    rng = np.random.default_rng(seed)
+    med = np.median(rng.choice(a, size=(reps, a.size), replace=True), axis=1)
+    lo, hi = np.percentile(med, [2.5, 97.5])
+    return {"median": round(float(np.median(a)), 3), "ci95": [round(float(lo), 3), round(float(hi), 3)],
+            "rounds": int(a.size)}
+
+
+def context(torch):
+    """Context for the figures (not denominators): a plain device copy's bandwidth and the
+    clocks rocm-smi reports once the timed loops are done."""
+    n = 1 << 29  # 1 GiB of f16
+    src = torch.empty(n, dtype=torch.float16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for _ in range(5):
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del src, dst
+    ctx = {"copy_1gib_read_plus_write_gbps": round(2 * 2 * n / best / 1e6, 1)}
+    try:
+        import subprocess
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        if r.returncode == 0:
+            d = json.loads(r.stdout[r.stdout.index("{"):])
+            card = d.get("card0") or next(iter(d.values()))
+            ctx["clocks_after_timing"] = {k: v for k, v in card.items() if "clk" in k.lower()}
+    except Exception as e:  # context only: a missing or failing tool leaves it out
+        ctx["clocks_after_timing"] = f"unavailable ({type(e).__name__})"
+    return ctx
 
 
 def kernel_groups(wl):
@@ -820,6 +866,11 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ph = [sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)) / 1e3 for j in range(3)]
+    per_step = [[ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 for i in range(args.steps)] for j in range(3)]  # us
+    stats = {"gemv_gbps": median_ci(np, [wl.gemv_bytes / t / 1e3 for t in per_step[0]]),
+             "prefill_tflops": median_ci(np, [wl.prefill_flops / t / 1e6 for t in per_step[2]]),
+             "gemv_us": median_ci(np, per_step[0]), "head_topk_us": median_ci(np, per_step[1]),
+             "prefill_us": median_ci(np, per_step[2])}
     log(f"timed {args.steps} steps in {wall * 1e3:.1f} ms: gemv {ph[0] / args.steps * 1e6:.1f} us, "
         f"head+top-k {ph[1] / args.steps * 1e6:.1f} us, prefill {ph[2] / args.steps * 1e6:.1f} us per step")
 
@@ -839,6 +890,8 @@ def main():
         torch.cuda.synchronize()
         dg = sum(evd[i][0].elapsed_time(evd[i][1]) for i in range(args.steps)) / args.steps * 1e3
         dh = sum(evd[i][1].elapsed_time(evd[i][2]) for i in range(args.steps)) / args.steps * 1e3
+        stats["decode_only_gemv_gbps"] = median_ci(
+            np, [wl.gemv_bytes / (evd[i][0].elapsed_time(evd[i][1]) * 1e3) / 1e3 for i in range(args.steps)])
         dec = {"gemv_us": round(dg, 1), "head_topk_us": round(dh, 1),
                "gemv_gbps": round(wl.gemv_bytes / dg / 1e3, 1),
                "decode_step_gbps": round((wl.gemv_bytes + wl.head_bytes) / (dg + dh) / 1e3, 1)}
@@ -897,6 +950,9 @@ def main():
         qz = quantize_bench(torch, np, w4, synth, oracle)
         log(f"quantizer: {qz['avg_us']} us, {qz['gbps']} GB/s, parity {'ok' if qz['parity_ok'] else 'FAILED'}")
 
+    ctx = context(torch)
+    log(f"context: device copy {ctx['copy_1gib_read_plus_write_gbps']} GB/s; clocks {ctx.get('clocks_after_timing')}")
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -936,6 +992,8 @@ def main():
                               "prefill": ph[2] / args.steps * 1e6},
         "decode_step_gbps": decode_bytes * args.steps / (ph[0] + ph[1]) / 1e9,
         "decode_only_loop": dec,
+        "stats": stats,
+        "context": ctx,
         "roofline": roofline,
         "roofline_prefill": roofline_prefill,
         "kernels": {"/".join(map(str, k)): {kk: round(vv, 3) if isinstance(vv, float) else vv for kk, vv in v.items()}

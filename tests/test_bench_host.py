@@ -1,5 +1,6 @@
 """Host logic of bench.py that runs without a GPU: the counter-CSV reduction behind
-profiles/traffic.json and the multi-GPU refusal."""
+profiles/traffic.json, the median and bootstrap interval of the timed rounds, and the
+multi-GPU refusal."""
 
 import csv
 import json
@@ -69,3 +70,18 @@ def test_multi_gpu_request_exits_with_a_message():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_median_ci_bootstrap_interval():
+    import numpy as np
+    const = bench.median_ci(np, [5.0] * 20)
+    assert const == {"median": 5.0, "ci95": [5.0, 5.0], "rounds": 20}
+    x = list(np.random.default_rng(3).normal(100.0, 2.0, 20))
+    r = bench.median_ci(np, x)
+    assert r["median"] == round(float(np.median(x)), 3)
+    assert r["ci95"][0] <= r["median"] <= r["ci95"][1]
+    assert r["ci95"][1] - r["ci95"][0] < 4.0  # the median of 20 N(100, 2) draws is tight
+    assert bench.median_ci(np, x) == r  # fixed seed: the same interval every time
+    # one slow outlier round moves neither the median nor the interval much
+    y = x[:-1] + [1000.0]
+    assert abs(bench.median_ci(np, y)["median"] - r["median"]) < 1.0
