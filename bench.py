@@ -56,6 +56,8 @@ def parse_args():
                    help="counter-collection pass: launch each kernel shape of the step 3 times (eagerly, between "
                         "marker kernels) plus a copy of known size, write the launch plan to MANIFEST and exit; "
                         "run under rocprofv3 --pmc")
+    p.add_argument("--util-from", nargs=2, metavar=("MANIFEST", "UTIL_CSV"),
+                   help="reduce a `rocprofv3 --pmc VALUBusy MfmaUtil` run of --counters into profiles/utilization.json")
     p.add_argument("--traffic-from", nargs=3, metavar=("MANIFEST", "FETCH_CSV", "WRITE_CSV"),
                    help="(no GPU) turn the FETCH_SIZE and WRITE_SIZE counter CSVs of two --counters passes into "
                         "profiles/traffic.json and print a table of them")
@@ -290,11 +292,41 @@ COUNTER_REPS = 3
 COPY_ELEMS = 128 << 20  # f16 elements of the calibration copy (256 MiB read, 256 MiB written)
 
 
+def small_m_groups(torch, np, w4, synth):
+    """The batched GEMV shapes of the side sections (affine format: Qwen3-1.7B classify at
+    M = 16, the Gemma-12B-shaped layer at M = 8 and 1) as counter-plan groups: key -> bytes
+    and COUNTER_REPS launches, each on its own copy of the weights."""
+    groups = {}
+    for cfg, (label, m, layer_name, wname, grps, copies, fmt) in enumerate(SMALL_M):
+        if fmt != "affine64":
+            continue
+        m = getattr(synth, m) if isinstance(m, str) else m
+        wk = getattr(synth, wname)
+        shapes = {name: (j, n, k) for j, (name, n, k) in enumerate(getattr(synth, layer_name))}
+        for grp in grps:
+            parts = [synth.w4_weights(shapes[g][1], shapes[g][2], seed=0, workload=wk,
+                                      layer=100 * cfg + shapes[g][0]) for g in grp]
+            q, sc, b = (np.concatenate([p_[i] for p_ in parts]) for i in range(3))
+            n, k = q.shape
+            x = torch.from_numpy(synth.activations(m, k, seed=0, workload=wk,
+                                                   layer=100 * cfg + 50 + shapes[grp[0]][0])).cuda()
+            y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+            qw0, s0, b0 = w4.w4_pack(torch.from_numpy(q).cuda()), torch.from_numpy(sc).cuda(), torch.from_numpy(b).cuda()
+            mats = [(qw0, s0, b0)] + [(qw0.clone(), s0.clone(), b0.clone()) for _ in range(COUNTER_REPS - 1)]
+            groups[("w4_gemv", m, n, k)] = {"bytes": gemv_bytes(m, n, k), "flops": 0,
+                                            "fns": [lambda t=t, x=x, y=y: w4.w4_gemv(t[0], t[1], t[2], x, out=y)
+                                                    for t in mats]}
+    return groups
+
+
 def counters_pass(torch, wl, manifest_path):
     """Launch plan for the counter runs: a marker kernel (an int16 fill, a kernel nothing
     else here launches), then a copy of known size COUNTER_REPS times, then for each kernel
     shape COUNTER_REPS launches on different weights, each group followed by a marker.
     The plan and the algorithmic bytes of each group go to manifest_path."""
+    # every buffer (and the packing launches that build them) before the first marker
+    groups = dict(kernel_groups(wl))
+    groups.update(small_m_groups(torch, wl.np, wl.w4, wl.synth))
     marker = torch.empty(4097, dtype=torch.int16, device="cuda")
     src = torch.ones(COPY_ELEMS, dtype=torch.float16, device="cuda")
     dst = torch.empty_like(src)
@@ -304,7 +336,7 @@ def counters_pass(torch, wl, manifest_path):
     for _ in range(COUNTER_REPS):
         torch.neg(src, out=dst)
     marker.fill_(1)
-    for key, g in kernel_groups(wl).items():
+    for key, g in groups.items():
         fns = g["fns"]
         for r in range(COUNTER_REPS):
             fns[r % len(fns)]()
@@ -338,6 +370,61 @@ def _counter_segments(csv_path, counter):
             cur["v"] += d["v"]
             cur["names"].append(d["name"].replace("(anonymous namespace)::", "").split("(")[0][:80])
     return segs
+
+
+def _counter_dispatches(csv_path, counters):
+    """Per marker-delimited segment (after the first marker): each dispatch's kernel name and
+    the values of the named counters (derived metrics such as VALUBusy are per dispatch)."""
+    import csv
+    disp = {}
+    with open(csv_path, newline="") as f:
+        for r in csv.DictReader(f):
+            d = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "v": {}})
+            if r["Counter_Name"] in counters:
+                d["v"][r["Counter_Name"]] = d["v"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    segs, cur, started = [], None, False
+    for i in sorted(disp):
+        d = disp[i]
+        if "FillFunctor<short>" in d["name"]:
+            if started:
+                segs.append(cur)
+            started, cur = True, []
+        elif started:
+            cur.append((d["name"].replace("(anonymous namespace)::", "").split("(")[0][:80], d["v"]))
+    return segs
+
+
+UTIL_COUNTERS = ("VALUBusy", "MfmaUtil")
+
+
+def util_from(manifest_path, csv_path, out_path=None):
+    """profiles/utilization.json from one `rocprofv3 --pmc VALUBusy MfmaUtil` run of the
+    --counters pass: per kernel shape and dispatched kernel, the mean of each metric (percent
+    of the kernel's busy time) over its launches."""
+    with open(manifest_path) as f:
+        man = json.load(f)
+    groups = man["groups"]
+    segs = _counter_dispatches(csv_path, UTIL_COUNTERS)
+    if len(segs) != len(groups):
+        raise SystemExit(f"segments {len(segs)} do not match the plan's {len(groups)} groups")
+    out = {"method": "rocprofv3 --pmc VALUBusy MfmaUtil over bench.py --counters; per dispatch, averaged "
+                     "over the launches of each kernel in a shape's group", "kernels": {}}
+    print("| kernel shape | dispatched kernel | launches | VALUBusy % | MfmaUtil % |")
+    print("|---|---|---|---|---|")
+    for g, seg in zip(groups[1:], segs[1:]):
+        per = {}
+        for name, v in seg:
+            per.setdefault(name, []).append(v)
+        out["kernels"][g["key"]] = {"source_sha": g["source_sha"], "by_kernel": {}}
+        for name, vs in per.items():
+            row = {c: sum(v.get(c, 0.0) for v in vs) / len(vs) for c in UTIL_COUNTERS}
+            row["launches"] = len(vs)
+            out["kernels"][g["key"]]["by_kernel"][name] = row
+            print(f"| {g['key']} | {name} | {len(vs)} | {row['VALUBusy']:.1f} | {row['MfmaUtil']:.1f} |")
+    path = out_path or os.path.join(ROOT, "profiles", "utilization.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(f"wrote {path}")
 
 
 def traffic_from(manifest_path, fetch_csv, write_csv, out_path=None):
@@ -822,6 +909,9 @@ def main():
     args = parse_args()
     if args.traffic_from:
         traffic_from(*args.traffic_from)
+        return
+    if args.util_from:
+        util_from(*args.util_from)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",

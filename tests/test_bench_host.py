@@ -65,6 +65,31 @@ def test_traffic_from_rejects_a_plan_mismatch(tmp_path):
                            str(tmp_path / "t.json"))
 
 
+def test_util_from_averages_each_kernel_per_dispatch(tmp_path):
+    mark = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<short>>(int)"
+    copy = "void at::native::vectorized_elementwise_kernel<4, neg>(int)"
+    gemm, red = "void w4::gemm_dma_kernel(GemmArgs)", "void w4::splitk_reduce_kernel(float*)"
+    man = {"reps": 2, "groups": [
+        {"key": "copy", "read_bytes": 1, "write_bytes": 1, "source": None},
+        {"key": "gemm_f16_1570_2048_11008", "bytes": 1000, "flops": 1, "source": "gemm.hip", "source_sha": "x"}]}
+    seq = [("void setup()", 50.0, 50.0), (mark, 0, 0), (copy, 1.0, 0), (copy, 1.0, 0), (mark, 0, 0),
+           (gemm, 10.0, 40.0), (red, 6.0, 0.0), (gemm, 12.0, 36.0), (red, 4.0, 0.0), (mark, 0, 0)]
+    with open(tmp_path / "u.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for i, (name, valu, mfma) in enumerate(seq, start=1):
+            w.writerow({"Dispatch_Id": i, "Kernel_Name": name, "Counter_Name": "VALUBusy", "Counter_Value": valu})
+            w.writerow({"Dispatch_Id": i, "Kernel_Name": name, "Counter_Name": "MfmaUtil", "Counter_Value": mfma})
+    (tmp_path / "m.json").write_text(json.dumps(man))
+    out = tmp_path / "u.json"
+    bench.util_from(str(tmp_path / "m.json"), str(tmp_path / "u.csv"), str(out))
+    k = json.loads(out.read_text())["kernels"]["gemm_f16_1570_2048_11008"]
+    assert k["source_sha"] == "x"
+    g, r = k["by_kernel"]["void w4::gemm_dma_kernel"], k["by_kernel"]["void w4::splitk_reduce_kernel"]
+    assert (g["VALUBusy"], g["MfmaUtil"], g["launches"]) == (pytest.approx(11.0), pytest.approx(38.0), 2)
+    assert (r["VALUBusy"], r["MfmaUtil"], r["launches"]) == (pytest.approx(5.0), pytest.approx(0.0), 2)
+
+
 def test_multi_gpu_request_exits_with_a_message():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
