@@ -18,10 +18,11 @@ prefill's dequant+GEMM TFLOP/s (2*M*N*K per GEMM over the phase's wall time), ea
 fraction of MI355X's 8 TB/s HBM and 2.5 PFLOP/s dense f16.  `roofline` is the dominant
 GEMV kernel's own rate from per-launch HIP events; `cpu_baseline` times the CPU oracle on a
 bounded sample of the same workload.  `stats` gives, per phase, the median of the timed
-steps and its 95 % bootstrap interval (2000 resamples, as in the timing method of
-"ENGINEERING_10X_RESEARCH", "Controls"); `context` a 1 GiB device copy's bandwidth and the
-clocks rocm-smi reports after timing (context, not denominators).  Outputs of the timed
-steps are re-checked against the oracle on sampled rows before anything is printed.
+steps and its 95 % bootstrap interval (2000 resamples, as in "Engineering investigation: can
+this MLX port become another 10x faster?", "Experimental controls and limits"); `context` a
+1 GiB device copy's bandwidth and the clocks rocm-smi reports after timing (context, not
+denominators).  Outputs of the timed steps are re-checked against the oracle on sampled rows
+before anything is printed.
 """
 
 from __future__ import annotations

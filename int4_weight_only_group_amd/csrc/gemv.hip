@@ -506,9 +506,9 @@ void launch_p(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const ui
     launch_r<MT, 64, SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
 }
 
-// ------------------------------------------------------------------ 2 <= M <= 16 on MFMA
-// With several activation rows the VALU kernel spends 4 dot products per word and row on
-// top of the 13-operation dequant, so at M = 16 the arithmetic, not HBM, sets its speed.
+// ------------------------------------------------------------------ 3 <= M <= 16 on MFMA
+// With several activation rows the VALU kernels spend 4 dot products per word and row on
+// top of the dequant, so at M = 16 the arithmetic, not HBM, would set their speed.
 // Here the dequantized weights feed v_mfma_f32_16x16x32_f16 instead: D[n][m] += W[n][k] x[m][k]
 // over 16 weight rows n (A operand) and up to 16 activation rows m (B operand), so the only
 // per-row VALU work left is the dequant (11 operations per word with the fp8 converter's
