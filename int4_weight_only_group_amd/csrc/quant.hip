@@ -9,7 +9,8 @@
 //   q = clamp(rint_even(f32(f32(w - b) / s)), 0, 15),   or q = 0 for the group when s == 0.
 // Every step that decides a code is a correctly rounded f32 operation written with the
 // explicit _rn intrinsics (no contraction, no reciprocal rewrite), so the codes are a pure
-// function of the inputs.
+// function of the inputs; the quotient's division is replaced by a reciprocal product wherever
+// that provably gives the same code (see the kernel).
 //
 // Design (HBM-bound: 2 bytes read, 0.5625 written per weight): eight lanes per group, each
 // lane one 16-byte load (8 weights) and one packed word; the group's min and max are
@@ -71,13 +72,25 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__
     const float t = __fdiv_rn(__fsub_rn(hi, lo), 15.0f);
     const f16 s16 = (f16)t;  // round to nearest even, subnormals kept
     const float s = (float)s16;
+    // Codes: only the nearest integer of the correctly rounded quotient RN(d / s) matters.  The
+    // quotients stay below 22.5 (s = RN16((hi - lo) / 15) is at least 2/3 of (hi - lo) / 15, the
+    // worst case being a subnormal s), so a = RN(d * rcp(s)) is within 1.1e-5 of RN(d / s)
+    // (v_rcp_f32 within 2^-22 relative, the product's rounding 2^-24, the quotient's own rounding
+    // 2^-20) and rint(a) is the code unless a half-integer lies that close.  Those quotients
+    // (about 1 in 12000 on random weights; exact ties always) take the correctly rounded
+    // division.  d >= 0 (lo is the group's minimum), so only the upper clamp can act; s == 0
+    // (a NaN or infinite a, never within reach of a half-integer) zeroes the word at the end.
+    const float rs = __builtin_amdgcn_rcpf(s);
     uint32_t word = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float r = __builtin_rintf(__fdiv_rn(__fsub_rn(v[i], lo), s));
-      const uint32_t q = s == 0.0f ? 0u : (uint32_t)fminf(fmaxf(r, 0.0f), 15.0f);
-      word |= q << (4 * i);
+      const float d = __fsub_rn(v[i], lo);
+      const float a = __fmul_rn(d, rs);
+      float r = __builtin_rintf(a);
+      if (fabsf(__builtin_amdgcn_fractf(a) - 0.5f) <= 4e-5f) r = __builtin_rintf(__fdiv_rn(d, s));
+      word |= (uint32_t)fminf(r, 15.0f) << (4 * i);
     }
+    if (s == 0.0f) word = 0u;
     if (gid < ngroups) {
       qw[n * ((int64_t)G * 8) + (int64_t)g * 8 + lane8] = word;
       if (lane8 == 0) {

@@ -112,6 +112,32 @@ def test_quantize_edge_values_and_stride(w4):
     quantize_case(w4, w, ldw_pad=24)
 
 
+def test_quantize_quotients_at_and_near_half_integers(w4):
+    # Codes whose f32 quotient (w - b) / s is an exact half-integer (ties to even) or within
+    # 4e-5 of one: where a reciprocal product cannot decide the code, the division must.
+    rows = []
+    for e in (-20, -10, -4, 0, 3):  # s = 2^e exactly: every quotient below is k + 1/2
+        sc = 2.0 ** e
+        w = np.array([0.0, 15 * sc] + [((i % 15) + 0.5) * sc for i in range(62)])
+        rows.append(w.astype(np.float16))
+    rng = np.random.default_rng(91)
+    cand = (rng.standard_normal((40000, 64)) * 0.02).astype(np.float16)
+    wf = cand.astype(np.float32)
+    lo, hi = wf.min(1), wf.max(1)
+    lo[lo == 0] = 0.0
+    hi[hi == 0] = 0.0
+    sq = ((hi - lo).astype(np.float32) / np.float32(15)).astype(np.float16).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        qt = ((wf - lo[:, None]).astype(np.float32) / sq[:, None]).astype(np.float32)
+    dist = np.abs(qt - np.floor(qt) - np.float32(0.5))
+    near = np.nonzero(((dist <= 4e-5) & (sq[:, None] > 0)).any(1))[0]
+    assert len(near) >= 20, len(near)
+    w = np.concatenate([np.stack(rows), cand[near]])
+    qw, _, _ = quantize_case(w4, w)
+    codes = oracle.unpack(to_np(qw).view(np.uint32))
+    assert codes[0, 2:17].tolist() == [0, 2, 2, 4, 4, 6, 6, 8, 8, 10, 10, 12, 12, 14, 14]  # ties to even
+
+
 def test_quantize_full_matrix_and_roundtrip(w4):
     # a gate-sized matrix of N(0, 0.02) weights, every code; then dequant of the result
     n, k = 11008, 2048
