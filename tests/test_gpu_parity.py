@@ -566,6 +566,21 @@ def test_gemm_prefill_sampled_rows(w4):
     assert ok, worst
 
 
+@pytest.mark.parametrize("m,n,k,seed", [(1570, 22016, 2048, 7), (1570, 2048, 11008, 9)])
+def test_gemm_prefill_full(w4, m, n, k, seed):
+    # Every output of a prefill GEMM at the step's sizes (so the step's launch configuration:
+    # 320-row tiles, and split-K with its reduce for the 11008-long K) against fp64, on the
+    # dequantized scratch of synthetic int4 weights (the oracle's own dequant as B).
+    a = synth.activations(m, k, seed=seed)
+    q, sc, b = synth.w4_weights(n, k, seed=seed + 1)
+    wt = w4.w4_dequant_f16_t(w4.w4_pack(dev(q)), dev(sc), dev(b))
+    c = to_np(w4.gemm_f16(dev(a), wt))
+    wt_ref = oracle.dequant_f16_t(oracle.pack(q), sc, b)
+    c_ref, bound = oracle.gemm_ref(a, wt_ref.view(np.float16))
+    ok, worst = oracle.check_bound(c, c_ref, bound, RTOL)
+    assert ok, worst
+
+
 @pytest.mark.parametrize("m,n,k,sampled", [
     (600, 25608, 64, False),    # 320-row tiles (2 row tiles instead of 3), ragged M and N
     (600, 11000, 2048, True),   # 320-row tiles with K split in two, ragged N
