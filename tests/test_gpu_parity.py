@@ -553,6 +553,22 @@ def test_gemm_head_column_slice(w4):
     assert oracle.check_bound(c, c_ref, bound, RTOL)[0]
 
 
+@pytest.mark.parametrize("m,k,v", [(1, 2048, 151936), (8, 2048, 151936), (1, 3840, 262144), (8, 3840, 262144)])
+def test_gemm_head_full(w4, m, k, v):
+    # Every logit of the f16 LM heads at their real shapes (the decode head, speculative
+    # verify's 8 rows, the Gemma-shaped head at M = 1 and 8: the small-M kernel with 2 and 8
+    # columns per lane) against fp64, checked in column blocks.
+    x = synth.activations(m, k, seed=m + v)
+    head = synth.head_f16(k, v, seed=k + v)
+    logits = to_np(w4.gemm_f16(dev(x), dev(head)))
+    worst = 0.0
+    for c0 in range(0, v, 16384):
+        c_ref, bound = oracle.gemm_ref(x, head[:, c0:c0 + 16384])
+        ok, wr = oracle.check_bound(logits[:, c0:c0 + 16384], c_ref, bound, RTOL)
+        assert ok, (c0, wr)
+        worst = max(worst, wr)
+
+
 def test_gemm_prefill_sampled_rows(w4):
     # (M, N, K) = (1570, 11008, 2048): 128 sampled rows incl. the M tail 1536..1569
     m, n, k = 1570, 11008, 2048
