@@ -4,13 +4,14 @@
 // "What's inside the engine today": the multi-row decode GEMV whose weight stream is the
 // limit):  y[m][n] = sum_k (s[n][g] q[n][k] + b[n][g]) x[m][k],  g = k / 64.
 //
-// Design for CDNA4 (wave64, HBM-bound), four kernels by the number M of activation rows:
+// Design for CDNA4 (wave64, HBM-bound), kernels by the number M of activation rows:
 //  * M = 1 with rows longer than 1024 (gemv1s_kernel, "row slices" below): a wave streams
 //    whole 1 KB slices of R rows with buffer loads at scalar row offsets, converts codes to
 //    f16 through the fp8 converter and splits long rows across the waves of a workgroup.
-//  * M = 2 (gemvm_kernel): the row slices with both rows of x, each word dequantized once.
+//  * M = 2 (the same kernel with both rows of x in registers): each word dequantized once and
+//    dotted with both rows.
 //  * M = 1 with short rows (gemv1_kernel), and what the above do not cover (gemv_kernel:
-//    rows beyond 16384, or 2 GB of codes at M = 2): a "team" of P lanes
+//    rows beyond 16384): a "team" of P lanes
 //    (P = 64, or 32 for short rows) owns R output rows; lane l streams 16-byte chunks (32
 //    codes = half a group) c = l, l+P, ... of each row, so every load instruction reads P*16
 //    contiguous bytes of one row.  x is staged in LDS (or registers), re-ordered into the f16
@@ -700,12 +701,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* p) {
 // BIG: 2 GB of codes or more -- the buffers then start at each wave's own rows (64-bit base,
 // offsets below R rows); otherwise one buffer per array and the row offset in the scalar
 // register (measured 1-2 % faster).
-template <int R, int KS, bool SYM, bool BIG>
+template <int R, int KS, bool SYM, bool BIG, int MT>
 __global__ __launch_bounds__(KS == 1 ? kWG : KS * 64) void gemv1s_kernel(
     const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc, const uint16_t* __restrict__ bi,
-    const uint16_t* __restrict__ x, float* __restrict__ y, int N, int K, int nblocks,
-    uint32_t qblk, uint32_t sblk) {  // bytes of codes / of scales per block of R rows
-  __shared__ float red[KS][R];
+    const uint16_t* __restrict__ x, int64_t ldx, float* __restrict__ y, int64_t ldy, int N, int K,
+    int nblocks, uint32_t qblk, uint32_t sblk) {  // bytes of codes / of scales per block of R rows
+  __shared__ float red[KS][R * MT];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int slice = KS == 1 ? 0 : wave;
@@ -717,11 +718,12 @@ __global__ __launch_bounds__(KS == 1 ? kWG : KS * 64) void gemv1s_kernel(
   const int voff_q = cc * 16, voff_s = (cc >> Fmt<SYM>::kChunkShift) * 2;
 
   // x first: loads complete in order, so the math can wait for x without the weights
-  uint4 xv[4];
-  {
-    const uint4* xp = reinterpret_cast<const uint4*>(x + cc * 32);
+  uint4 xv[MT][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xv[i] = xp[i];
+  for (int m = 0; m < MT; ++m) {
+    const uint4* xp = reinterpret_cast<const uint4*>(x + m * ldx + cc * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xv[m][i] = xp[i];
   }
   uint4 w[R];
   uint32_t sv[R], bv[R];
@@ -741,89 +743,138 @@ __global__ __launch_bounds__(KS == 1 ? kWG : KS * 64) void gemv1s_kernel(
   __builtin_amdgcn_sched_barrier(0);
   if (KS == 1 && blk >= nblocks) return;
 
-  uint4 xp[4];
+  uint4 xp[MT][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) xp[i] = pair_up_cvt(xv[i]);
-  float acc[R];
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xp[m][i] = pair_up_cvt(xv[m][i]);
+  float acc[R][MT];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const h2 s2 = __builtin_bit_cast(h2, (sv[r] & sb_on) * 0x10001u);
     const h2 b2 = __builtin_bit_cast(h2, (bv[r] & sb_on) * 0x10001u);
-    float a0 = word_fma_cvt<SYM>(w[r].x, s2, b2, xp[0], 0.f);
-    float a1 = word_fma_cvt<SYM>(w[r].y, s2, b2, xp[1], 0.f);
-    a0 = word_fma_cvt<SYM>(w[r].z, s2, b2, xp[2], a0);
-    a1 = word_fma_cvt<SYM>(w[r].w, s2, b2, xp[3], a1);
-    acc[r] = group_sum<64>(a0 + a1);
+    if constexpr (MT == 1) {
+      float a0 = word_fma_cvt<SYM>(w[r].x, s2, b2, xp[0][0], 0.f);
+      float a1 = word_fma_cvt<SYM>(w[r].y, s2, b2, xp[0][1], 0.f);
+      a0 = word_fma_cvt<SYM>(w[r].z, s2, b2, xp[0][2], a0);
+      a1 = word_fma_cvt<SYM>(w[r].w, s2, b2, xp[0][3], a1);
+      acc[r][0] = group_sum<64>(a0 + a1);
+    } else {
+      // each word dequantized once, its weight pairs dotted with every row of x (the same
+      // pairing and chaining per row as at M = 1)
+      float a[MT][2];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) a[m][0] = a[m][1] = 0.f;
+      const uint32_t wd[4] = {w[r].x, w[r].y, w[r].z, w[r].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        h2 q0, q1, q2, q3;
+        cvt_codes<SYM>(wd[j], q0, q1, q2, q3);
+        const uint32_t p0 = as_u32(__builtin_elementwise_fma(q0, s2, b2));
+        const uint32_t p1 = as_u32(__builtin_elementwise_fma(q1, s2, b2));
+        const uint32_t p2 = as_u32(__builtin_elementwise_fma(q2, s2, b2));
+        const uint32_t p3 = as_u32(__builtin_elementwise_fma(q3, s2, b2));
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          float t = a[m][j & 1];
+          t = dot2(p0, xp[m][j].x, t);
+          t = dot2(p1, xp[m][j].y, t);
+          t = dot2(p2, xp[m][j].z, t);
+          t = dot2(p3, xp[m][j].w, t);
+          a[m][j & 1] = t;
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[r][m] = group_sum<64>(a[m][0] + a[m][1]);
+    }
   }
   if constexpr (KS == 1) {
     if (lane == 63) {
 #pragma unroll
       for (int r = 0; r < R; ++r)
-        if (blk * R + r < N) y[blk * R + r] = acc[r];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          if (blk * R + r < N) y[m * ldy + blk * R + r] = acc[r][m];
     }
   } else {
     if (lane == 63) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) red[slice][r] = acc[r];
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) red[slice][r * MT + m] = acc[r][m];
     }
     __syncthreads();
-    if (wave == 0 && lane < R && blk * R + lane < N) {
+    if (wave == 0 && lane < R * MT && blk * R + lane / MT < N) {
       float v = red[0][lane];
 #pragma unroll
       for (int j = 1; j < KS; ++j) v += red[j][lane];
-      y[blk * R + lane] = v;
+      y[(lane % MT) * ldy + blk * R + lane / MT] = v;
     }
   }
 }
 
-template <int R, int KS, bool SYM>
-void launch_m1s(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
-                float* y, int N, int K, hipStream_t st) {
+template <int R, int KS, bool SYM, int MT>
+void launch_rs(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
+               int64_t ldx, float* y, int64_t ldy, int N, int K, hipStream_t st) {
   const int nblocks = (N + R - 1) / R;
   const int grid = KS == 1 ? (nblocks + kWG / 64 - 1) / (kWG / 64) : nblocks;
   const uint32_t qblk = (uint32_t)R * (uint32_t)(K / 2);
   const uint32_t sblk = (uint32_t)R * (uint32_t)(K / Fmt<SYM>::kGroupSize) * 2;
   const dim3 block(KS == 1 ? kWG : KS * 64);
   if ((int64_t)N * (K / 2) >= ((int64_t)1 << 31))
-    hipLaunchKernelGGL((gemv1s_kernel<R, KS, SYM, true>), dim3(grid), block, 0, st, qw, s, b, x, y, N,
-                       K, nblocks, qblk, sblk);
+    hipLaunchKernelGGL((gemv1s_kernel<R, KS, SYM, true, MT>), dim3(grid), block, 0, st, qw, s, b, x, ldx,
+                       y, ldy, N, K, nblocks, qblk, sblk);
   else
-    hipLaunchKernelGGL((gemv1s_kernel<R, KS, SYM, false>), dim3(grid), block, 0, st, qw, s, b, x, y, N,
-                       K, nblocks, qblk, sblk);
+    hipLaunchKernelGGL((gemv1s_kernel<R, KS, SYM, false, MT>), dim3(grid), block, 0, st, qw, s, b, x, ldx,
+                       y, ldy, N, K, nblocks, qblk, sblk);
 }
 
-template <int KS, bool SYM>
-void launch_m1s_r(int R, const uint32_t* qw, const uint16_t* s, const uint16_t* b,
-                  const uint16_t* x, float* y, int N, int K, hipStream_t st) {
+template <int KS, bool SYM, int MT>
+void launch_rs_r(int R, const uint32_t* qw, const uint16_t* s, const uint16_t* b,
+                 const uint16_t* x, int64_t ldx, float* y, int64_t ldy, int N, int K, hipStream_t st) {
   if (R >= 4)
-    launch_m1s<4, KS, SYM>(qw, s, b, x, y, N, K, st);
+    launch_rs<4, KS, SYM, MT>(qw, s, b, x, ldx, y, ldy, N, K, st);
   else if (KS == 1 && R == 3)
-    launch_m1s<3, KS, SYM>(qw, s, b, x, y, N, K, st);
+    launch_rs<3, KS, SYM, MT>(qw, s, b, x, ldx, y, ldy, N, K, st);
   else
-    launch_m1s<2, KS, SYM>(qw, s, b, x, y, N, K, st);
+    launch_rs<2, KS, SYM, MT>(qw, s, b, x, ldx, y, ldy, N, K, st);
 }
 
-// Row-slice policy, measured on MI355X (graph launches on distinct weights): rows per wave
-// from the number of (row, slice) units -- 4 from 30000 units, 3 from 16000 when rows are one
-// slice long, else 2.  Returns false when the shape is not covered (rows of at most 32 chunks,
-// or more than 8 slices).
+template <bool SYM, int MT>
+void launch_rs_ks(int KS, int R, const uint32_t* qw, const uint16_t* s, const uint16_t* b,
+                  const uint16_t* x, int64_t ldx, float* y, int64_t ldy, int N, int K, hipStream_t st) {
+  switch (KS) {
+    case 1: launch_rs_r<1, SYM, MT>(R, qw, s, b, x, ldx, y, ldy, N, K, st); break;
+    case 2: launch_rs_r<2, SYM, MT>(R, qw, s, b, x, ldx, y, ldy, N, K, st); break;
+    case 3: launch_rs_r<3, SYM, MT>(R, qw, s, b, x, ldx, y, ldy, N, K, st); break;
+    case 4: launch_rs_r<4, SYM, MT>(R, qw, s, b, x, ldx, y, ldy, N, K, st); break;
+    case 5: launch_rs_r<5, SYM, MT>(R, qw, s, b, x, ldx, y, ldy, N, K, st); break;
+    case 6: launch_rs_r<6, SYM, MT>(R, qw, s, b, x, ldx, y, ldy, N, K, st); break;
+    case 7: launch_rs_r<7, SYM, MT>(R, qw, s, b, x, ldx, y, ldy, N, K, st); break;
+    default: launch_rs_r<8, SYM, MT>(R, qw, s, b, x, ldx, y, ldy, N, K, st); break;
+  }
+}
+
+// Row-slice policy, measured on MI355X (graph launches on distinct weights), rows per wave
+// from the number of (row, slice) units: at M = 1, 4 from 30000 units, 3 from 16000 when rows
+// are one slice long, else 2; at M = 2, 4 from 12000, 3 from 2304 for one-slice rows, else 2
+// (22016 x 2048: 8.3 us; 2560 x 2048: 3.05; 2048 x 2048: 2.76; 2048 x 11008: 6.25).  Returns
+// false when the shape is not covered: more than 8 slices, or at M = 1 rows of at most 32
+// chunks (a half-empty slice; the 32-lane team kernel is faster there).
 template <bool SYM>
-bool launch_gemv_m1s(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
-                     float* y, int N, int K, hipStream_t st) {
+bool launch_gemv_rs(int M, const uint32_t* qw, const uint16_t* s, const uint16_t* b,
+                    const uint16_t* x, int64_t ldx, float* y, int64_t ldy, int N, int K,
+                    hipStream_t st) {
   const int C = K / 32;
   const int KS = (C + 63) / 64;
-  if (C <= 32 || KS > 8) return false;
+  if (KS > 8 || M < 1 || M > 2 || (M == 1 && C <= 32)) return false;
   const int64_t units = (int64_t)N * KS;
-  const int R = units >= 30000 ? 4 : (units >= 16000 && KS == 1) ? 3 : 2;
-  switch (KS) {
-    case 1: launch_m1s_r<1, SYM>(R, qw, s, b, x, y, N, K, st); break;
-    case 2: launch_m1s_r<2, SYM>(R, qw, s, b, x, y, N, K, st); break;
-    case 3: launch_m1s_r<3, SYM>(R, qw, s, b, x, y, N, K, st); break;
-    case 4: launch_m1s_r<4, SYM>(R, qw, s, b, x, y, N, K, st); break;
-    case 5: launch_m1s_r<5, SYM>(R, qw, s, b, x, y, N, K, st); break;
-    case 6: launch_m1s_r<6, SYM>(R, qw, s, b, x, y, N, K, st); break;
-    case 7: launch_m1s_r<7, SYM>(R, qw, s, b, x, y, N, K, st); break;
-    default: launch_m1s_r<8, SYM>(R, qw, s, b, x, y, N, K, st); break;
+  if (M == 1) {
+    const int R = units >= 30000 ? 4 : (units >= 16000 && KS == 1) ? 3 : 2;
+    launch_rs_ks<SYM, 1>(KS, R, qw, s, b, x, ldx, y, ldy, N, K, st);
+  } else {
+    const int R = units >= 12000 ? 4 : (units >= 2304 && KS == 1) ? 3 : 2;
+    launch_rs_ks<SYM, 2>(KS, R, qw, s, b, x, ldx, y, ldy, N, K, st);
   }
   return true;
 }
@@ -834,7 +885,7 @@ bool launch_gemv_m1s(const uint32_t* qw, const uint16_t* s, const uint16_t* b, c
 template <bool SYM>
 bool launch_gemv_m1(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
                     float* y, int N, int K, hipStream_t st) {
-  if (launch_gemv_m1s<SYM>(qw, s, b, x, y, N, K, st)) return true;
+  if (launch_gemv_rs<SYM>(1, qw, s, b, x, K, y, N, N, K, st)) return true;
   if (K / 32 <= 32) {
     launch_m1<32, 1, 1, true, SYM>(qw, s, b, x, y, N, K, 1, st);
     return true;
@@ -859,185 +910,11 @@ void launch_gemv_mf(const uint32_t* qw, const uint16_t* s, const uint16_t* b, co
     launch_mf<4, 1, 1, SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
 }
 
-// ------------------------------------------------------------------ M = 2 on row slices
-// The row-slice layout of the M = 1 kernel with MT rows of x (MT = 2 is the one launched): a lane keeps the 32 x values of
-// its chunk for every row (as f16 pairs in the converter's order, 16 registers per row), each
-// word is dequantized once (11 VALU operations) and dotted with every row of x (4 dot
-// products per row).  With up to 128 registers of x a SIMD holds two waves, so a wave walks
-// `per` blocks of R rows and loads the next block while it computes the current one (two
-// register sets, as in the M = 1 team kernel); every wave walks the same number of blocks, the
-// surplus ones on clamped loads, never stored.  Slices of long rows run as the waves of one
-// workgroup and add through LDS, double-buffered, one barrier per block.
-template <int MT, int R, int KS, bool SYM>
-__global__ __launch_bounds__(KS == 1 ? kWG : KS * 64) void gemvm_kernel(
-    const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc, const uint16_t* __restrict__ bi,
-    const uint16_t* __restrict__ x, int64_t ldx, float* __restrict__ y, int64_t ldy, int M, int N,
-    int K, int nblocks, int per) {
-  __shared__ float red[2][KS][R * MT];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int slice = KS == 1 ? 0 : wave;
-  const int team = KS == 1 ? (int)blockIdx.x * (kWG / 64) + wave : (int)blockIdx.x;
-  const int T = KS == 1 ? (int)gridDim.x * (kWG / 64) : (int)gridDim.x;
-  const int C = K / 32, G = K / Fmt<SYM>::kGroupSize;
-  const int c = slice * 64 + lane;
-  const int cc = min(c, C - 1);
-  const uint32_t sb_on = c < C ? 0xFFFFu : 0u;  // past the row end: s = b = 0, every weight 0
-  const __amdgpu_buffer_rsrc_t rq = buffer_of(qw), rs = buffer_of(sc), rb = buffer_of(SYM ? sc : bi);
-  const int voff_q = cc * 16, voff_s = (cc >> Fmt<SYM>::kChunkShift) * 2;
-
-  struct Blk {
-    uint4 w[R];
-    uint32_t s[R], b[R];
-  };
-  auto load = [&](int i, Blk& B) {
-    const int blk = min(team + i * T, nblocks - 1);
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int n = min(blk * R + r, N - 1);  // tail rows reload the last row, never stored
-      B.w[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, voff_q, n * C * 16, 2));
-      B.s[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, voff_s, n * G * 2, 0);
-      B.b[r] = SYM ? 0u : __builtin_amdgcn_raw_buffer_load_b16(rb, voff_s, n * G * 2, 0);
-    }
-  };
-
-  // x first (rows past M repeat the last row and are never stored)
-  uint4 xv[MT][4];
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    const uint4* xr = reinterpret_cast<const uint4*>(x + (int64_t)min(m, M - 1) * ldx + cc * 32);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) xv[m][i] = xr[i];
-  }
-  Blk A, B;
-  load(0, A);
-  __builtin_amdgcn_sched_barrier(0);
-  if (KS == 1 && team >= nblocks) return;  // no block at all (no barrier when KS == 1)
-  uint4 xp[MT][4];
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) xp[m][i] = pair_up_cvt(xv[m][i]);
-
-  auto compute = [&](int i, const Blk& Bk) {
-    const int blk = team + i * T;  // past nblocks: computed on clamped loads, not stored
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const h2 s2 = __builtin_bit_cast(h2, (Bk.s[r] & sb_on) * 0x10001u);
-      const h2 b2 = __builtin_bit_cast(h2, (Bk.b[r] & sb_on) * 0x10001u);
-      const uint32_t wd[4] = {Bk.w[r].x, Bk.w[r].y, Bk.w[r].z, Bk.w[r].w};
-      float a[MT];
-#pragma unroll
-      for (int m = 0; m < MT; ++m) a[m] = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        h2 q0, q1, q2, q3;
-        cvt_codes<SYM>(wd[j], q0, q1, q2, q3);
-        const uint32_t w0 = as_u32(__builtin_elementwise_fma(q0, s2, b2));  // one rounding each
-        const uint32_t w1 = as_u32(__builtin_elementwise_fma(q1, s2, b2));
-        const uint32_t w2 = as_u32(__builtin_elementwise_fma(q2, s2, b2));
-        const uint32_t w3 = as_u32(__builtin_elementwise_fma(q3, s2, b2));
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          a[m] = dot2(w0, xp[m][j].x, a[m]);
-          a[m] = dot2(w1, xp[m][j].y, a[m]);
-          a[m] = dot2(w2, xp[m][j].z, a[m]);
-          a[m] = dot2(w3, xp[m][j].w, a[m]);
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < MT; ++m) a[m] = group_sum<64>(a[m]);
-      const int row = blk * R + r;
-      if constexpr (KS == 1) {
-        if (lane == 63 && blk < nblocks && row < N) {
-#pragma unroll
-          for (int m = 0; m < MT; ++m)
-            if (m < M) y[(int64_t)m * ldy + row] = a[m];
-        }
-      } else if (lane == 63) {
-#pragma unroll
-        for (int m = 0; m < MT; ++m) red[i & 1][slice][r * MT + m] = a[m];
-      }
-    }
-    if constexpr (KS > 1) {
-      __syncthreads();
-      if (wave == 0 && lane < R * MT) {
-        const int r = lane / MT, m = lane - (lane / MT) * MT;
-        const int row = blk * R + r;
-        if (m < M && blk < nblocks && row < N) {
-          float v = red[i & 1][0][lane];
-#pragma unroll
-          for (int sl = 1; sl < KS; ++sl) v += red[i & 1][sl][lane];
-          y[(int64_t)m * ldy + row] = v;
-        }
-      }
-    }
-  };
-
-  int i = 0;
-  for (; i + 2 < per; i += 2) {
-    load(i + 1, B);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(i, A);
-    load(i + 2, A);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(i + 1, B);
-  }
-  if (per - i == 2) {
-    load(i + 1, B);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(i, A);
-    compute(i + 1, B);
-  } else {
-    compute(i, A);
-  }
-}
-
-// Waves in flight: two per SIMD with 8 rows of x (128 registers of x), four with up to 4.
-template <int MT, int R, int KS, bool SYM>
-void launch_mr(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
-               int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
-  const int nblocks = (N + R - 1) / R;
-  const int wpc = MT > 4 ? 8 : 16;  // resident waves per CU
-  const int wpb = KS == 1 ? kWG / 64 : KS;
-  const int slots = 256 * (wpc / wpb);   // workgroups resident at once
-  const int teams = KS == 1 ? slots * (kWG / 64) : slots;
-  const int per = std::max(1, (nblocks + teams - 1) / teams);
-  const int need = (nblocks + per - 1) / per;  // teams that cover every block
-  const int grid = KS == 1 ? (need + kWG / 64 - 1) / (kWG / 64) : need;
-  hipLaunchKernelGGL((gemvm_kernel<MT, R, KS, SYM>), dim3(grid), dim3(KS == 1 ? kWG : KS * 64), 0, st, qw,
-                     s, b, x, ldx, y, ldy, M, N, K, nblocks, per);
-}
-
-// M = 2 on row slices, measured on MI355X (graph launches on distinct weights): 22016 x 2048
-// 9.3 us against 11.1 us for the LDS-x team kernel; at M = 3..4 the row slices are within
-// 6 % of the matrix cores and at M = 8 well behind them (38.8 vs 28.4 us on 30720 x 3840), so
-// from M = 3 on the matrix cores stay.  Returns false for rows of more than 8 slices.
-template <bool SYM>
-bool launch_gemv_m2(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
-                    int64_t ldx, float* y, int64_t ldy, int N, int K, hipStream_t st) {
-  const int KS = (K / 32 + 63) / 64;
-  switch (KS) {
-    case 1: launch_mr<2, 2, 1, SYM>(qw, s, b, x, ldx, y, ldy, 2, N, K, st); break;
-    case 2: launch_mr<2, 2, 2, SYM>(qw, s, b, x, ldx, y, ldy, 2, N, K, st); break;
-    case 3: launch_mr<2, 2, 3, SYM>(qw, s, b, x, ldx, y, ldy, 2, N, K, st); break;
-    case 4: launch_mr<2, 2, 4, SYM>(qw, s, b, x, ldx, y, ldy, 2, N, K, st); break;
-    case 5: launch_mr<2, 2, 5, SYM>(qw, s, b, x, ldx, y, ldy, 2, N, K, st); break;
-    case 6: launch_mr<2, 2, 6, SYM>(qw, s, b, x, ldx, y, ldy, 2, N, K, st); break;
-    case 7: launch_mr<2, 2, 7, SYM>(qw, s, b, x, ldx, y, ldy, 2, N, K, st); break;
-    case 8: launch_mr<2, 2, 8, SYM>(qw, s, b, x, ldx, y, ldy, 2, N, K, st); break;
-    default: return false;
-  }
-  return true;
-}
-
 template <bool SYM>
 void launch_gemv_fmt(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
                      int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
   if (M <= 1 && launch_gemv_m1<SYM>(qw, s, b, x, y, N, K, st)) return;
-  if (M == 2 && (int64_t)N * (K / 2) < ((int64_t)1 << 31) &&
-      launch_gemv_m2<SYM>(qw, s, b, x, ldx, y, ldy, N, K, st))
-    return;
+  if (M == 2 && launch_gemv_rs<SYM>(2, qw, s, b, x, ldx, y, ldy, N, K, st)) return;
   if (M >= 3) {
     launch_gemv_mf<SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
     return;
