@@ -8,8 +8,8 @@
 //  * M = 1 with rows longer than 1024 (gemv1s_kernel, "row slices" below): a wave streams
 //    whole 1 KB slices of R rows with buffer loads at scalar row offsets, converts codes to
 //    f16 through the fp8 converter and splits long rows across the waves of a workgroup.
-//  * M = 2 (the same kernel with both rows of x in registers): each word dequantized once and
-//    dotted with both rows.
+//  * M = 2..4 (the same kernel with every row of x in registers): each word dequantized once
+//    and dotted with each row.
 //  * M = 1 with short rows (gemv1_kernel), and what the above do not cover (gemv_kernel:
 //    rows beyond 16384): a "team" of P lanes
 //    (P = 64, or 32 for short rows) owns R output rows; lane l streams 16-byte chunks (32
@@ -22,7 +22,8 @@
 //      (w & 0x00F000F0) | 0x54005400 = (  64+q1,   64+q5)
 //    and the same on w >> 8 for (q2,q6), (q3,q7); a packed f16 subtract removes the offset
 //    exactly.
-//  * 3 <= M <= 16 (gemv_mf_kernel): dequantized words feed the matrix cores.
+//  * 5 <= M <= 16, and 3..4 with rows beyond 16384 (gemv_mf_kernel): dequantized words feed
+//    the matrix cores.
 // In every kernel a packed f16 FMA forms w = s q + b with one rounding (the value the
 // prefill scratch holds) and the products w*x are exact in f32 and summed in f32, blockwise.
 // Every term's error is thus relative to |w x|, which keeps each output within
@@ -507,7 +508,7 @@ void launch_p(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const ui
     launch_r<MT, 64, SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
 }
 
-// ------------------------------------------------------------------ 3 <= M <= 16 on MFMA
+// ------------------------------------------------------------------ up to 16 rows on MFMA
 // With several activation rows the VALU kernels spend 4 dot products per word and row on
 // top of the dequant, so at M = 16 the arithmetic, not HBM, would set their speed.
 // Here the dequantized weights feed v_mfma_f32_16x16x32_f16 instead: D[n][m] += W[n][k] x[m][k]
@@ -855,26 +856,49 @@ void launch_rs_ks(int KS, int R, const uint32_t* qw, const uint16_t* s, const ui
   }
 }
 
+// three or four rows of x: 4 rows per wave on every shape measured
+template <bool SYM, int MT>
+void launch_rs_ks4(int KS, const uint32_t* qw, const uint16_t* s, const uint16_t* b,
+                   const uint16_t* x, int64_t ldx, float* y, int64_t ldy, int N, int K, hipStream_t st) {
+  switch (KS) {
+    case 1: launch_rs<4, 1, SYM, MT>(qw, s, b, x, ldx, y, ldy, N, K, st); break;
+    case 2: launch_rs<4, 2, SYM, MT>(qw, s, b, x, ldx, y, ldy, N, K, st); break;
+    case 3: launch_rs<4, 3, SYM, MT>(qw, s, b, x, ldx, y, ldy, N, K, st); break;
+    case 4: launch_rs<4, 4, SYM, MT>(qw, s, b, x, ldx, y, ldy, N, K, st); break;
+    case 5: launch_rs<4, 5, SYM, MT>(qw, s, b, x, ldx, y, ldy, N, K, st); break;
+    case 6: launch_rs<4, 6, SYM, MT>(qw, s, b, x, ldx, y, ldy, N, K, st); break;
+    case 7: launch_rs<4, 7, SYM, MT>(qw, s, b, x, ldx, y, ldy, N, K, st); break;
+    default: launch_rs<4, 8, SYM, MT>(qw, s, b, x, ldx, y, ldy, N, K, st); break;
+  }
+}
+
 // Row-slice policy, measured on MI355X (graph launches on distinct weights), rows per wave
 // from the number of (row, slice) units: at M = 1, 4 from 30000 units, 3 from 16000 when rows
 // are one slice long, else 2; at M = 2, 4 from 12000, 3 from 2304 for one-slice rows, else 2
-// (22016 x 2048: 8.3 us; 2560 x 2048: 3.05; 2048 x 2048: 2.76; 2048 x 11008: 6.25).  Returns
-// false when the shape is not covered: more than 8 slices, or at M = 1 rows of at most 32
-// chunks (a half-empty slice; the 32-lane team kernel is faster there).
+// (22016 x 2048: 8.3 us; 2560 x 2048: 3.05; 2048 x 2048: 2.76; 2048 x 11008: 6.25); at M = 3
+// and 4, 4 (faster than the matrix cores on every decode, classify and Gemma-shaped matrix:
+// 22016 x 2048 10.0 vs 15.8 us at M = 3, 11.3 vs 16.0 at M = 4; from M = 6 the matrix cores
+// win on most).  Returns false when the shape is not covered: M outside 1..4, more than 8
+// slices, or at M = 1 rows of at most 32 chunks (a half-empty slice; the 32-lane team kernel
+// is faster there).
 template <bool SYM>
 bool launch_gemv_rs(int M, const uint32_t* qw, const uint16_t* s, const uint16_t* b,
                     const uint16_t* x, int64_t ldx, float* y, int64_t ldy, int N, int K,
                     hipStream_t st) {
   const int C = K / 32;
   const int KS = (C + 63) / 64;
-  if (KS > 8 || M < 1 || M > 2 || (M == 1 && C <= 32)) return false;
+  if (KS > 8 || M < 1 || M > 4 || (M == 1 && C <= 32)) return false;
   const int64_t units = (int64_t)N * KS;
   if (M == 1) {
     const int R = units >= 30000 ? 4 : (units >= 16000 && KS == 1) ? 3 : 2;
     launch_rs_ks<SYM, 1>(KS, R, qw, s, b, x, ldx, y, ldy, N, K, st);
-  } else {
+  } else if (M == 2) {
     const int R = units >= 12000 ? 4 : (units >= 2304 && KS == 1) ? 3 : 2;
     launch_rs_ks<SYM, 2>(KS, R, qw, s, b, x, ldx, y, ldy, N, K, st);
+  } else if (M == 3) {
+    launch_rs_ks4<SYM, 3>(KS, qw, s, b, x, ldx, y, ldy, N, K, st);
+  } else {
+    launch_rs_ks4<SYM, 4>(KS, qw, s, b, x, ldx, y, ldy, N, K, st);
   }
   return true;
 }
@@ -893,9 +917,10 @@ bool launch_gemv_m1(const uint32_t* qw, const uint16_t* s, const uint16_t* b, co
   return false;
 }
 
-// 3 <= M <= 16 policy, measured on MI355X (back-to-back graph launches on distinct weights):
+// Matrix-core policy (5 <= M <= 16, and M = 3..4 past 16384 elements), measured on MI355X
+// (back-to-back graph launches on distinct weights):
 // four row blocks per wave once there are >= 768 of them, two from 384, otherwise one with
-// eight waves splitting K when rows are long.  At M = 2 the VALU kernel is still ahead.
+// eight waves splitting K when rows are long.  Up to 4 rows of x the row slices are ahead.
 template <bool SYM>
 void launch_gemv_mf(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
                     int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
@@ -914,7 +939,7 @@ template <bool SYM>
 void launch_gemv_fmt(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
                      int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
   if (M <= 1 && launch_gemv_m1<SYM>(qw, s, b, x, y, N, K, st)) return;
-  if (M == 2 && launch_gemv_rs<SYM>(2, qw, s, b, x, ldx, y, ldy, N, K, st)) return;
+  if (M >= 2 && M <= 4 && launch_gemv_rs<SYM>(M, qw, s, b, x, ldx, y, ldy, N, K, st)) return;
   if (M >= 3) {
     launch_gemv_mf<SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
     return;

@@ -173,7 +173,7 @@ def test_sym128_gemv(w4, m, n, k):
     sym_case(w4, m, n, k, seed=500 * m + n + k, ldx_pad=8 * (m % 2), ldy_pad=m % 3)
 
 
-@pytest.mark.parametrize("m", [1, 2, 16])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 16])
 @pytest.mark.parametrize("n,k", [(2560, 2048), (22016, 2048), (2048, 11008)])
 def test_sym128_gemv_equals_affine_kernel_with_bias_minus_8s(w4, m, n, k):
     # w = s (q - 8) is the affine weight with b = -8 s (exact), so with each scale repeated over
@@ -251,13 +251,13 @@ def gemv_case(w4, m, n, k, seed, x_override=None, ldx_pad=0, ldy_pad=0):
     return worst
 
 
-@pytest.mark.parametrize("m", [1, 2, 3, 5, 8, 11, 16])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 11, 16])
 @pytest.mark.parametrize("n,k", [(1, 64), (3, 128), (257, 960), (70, 2048), (33, 2112), (5, 11008)])
 def test_gemv_small_shapes(w4, m, n, k):
     gemv_case(w4, m, n, k, seed=1000 * m + n + k)
 
 
-@pytest.mark.parametrize("m", [1, 2, 3])
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
 @pytest.mark.parametrize("n,k", [(37, 16448), (9, 20480)])
 def test_gemv_rows_past_16384(w4, m, n, k):
     # rows of more than 8 slices of 2048 take the general team kernel (M <= 2) or the matrix
@@ -339,17 +339,18 @@ WORKLOAD_SHAPES = sorted({(n, k) for _, n, k in synth.QWEN25_3B_LAYER}
 
 
 @pytest.mark.parametrize("n,k", WORKLOAD_SHAPES)
-@pytest.mark.parametrize("m", [1, 2, 8, 16])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 8, 16])
 def test_gemv_workload_shapes_full(w4, m, n, k):
     gemv_case(w4, m, n, k, seed=n * 7 + k + m)
 
 
-@pytest.mark.parametrize("m", [3, 16])
+@pytest.mark.parametrize("m", [3, 5, 16])
 @pytest.mark.parametrize("n,k", [(12290, 320), (6150, 448), (100, 8256), (17, 64), (383 * 16 + 1, 192)])
 def test_gemv_matrix_core_edges(w4, m, n, k):
-    # from three rows of x on, the GEMV runs on matrix cores in 16-row blocks grouped by 1, 2 or
+    # from five rows of x on, the GEMV runs on matrix cores in 16-row blocks grouped by 1, 2 or
     # 4 per wave; these shapes leave the last group partly filled in each grouping, end rows on
-    # a half step (K % 128 == 64) and give some waves of the K split no step at all
+    # a half step (K % 128 == 64) and give some waves of the K split no step at all (at M = 3
+    # the same shapes run on row slices of 4 rows with three rows of x)
     gemv_case(w4, m, n, k, seed=31 * n + k + m, ldx_pad=8 * (m % 2), ldy_pad=m % 5)
 
 
