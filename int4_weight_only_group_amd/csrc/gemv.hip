@@ -874,7 +874,9 @@ void launch_rs_ks4(int KS, const uint32_t* qw, const uint16_t* s, const uint16_t
 
 // Row-slice policy, measured on MI355X (graph launches on distinct weights), rows per wave
 // from the number of (row, slice) units: at M = 1, 4 from 30000 units, 3 from 16000 when rows
-// are one slice long, else 2; at M = 2, 4 from 12000, 3 from 2304 for one-slice rows, else 2
+// are one slice long, else 2, except that one-slice rows that fit one wave per SIMD at 3 rows
+// per wave but not at 2 take 3, so no SIMD carries 4 rows (2560 x 2048: 2.83 vs 3.00 us); at
+// M = 2, 4 from 12000, 3 from 2304 for one-slice rows, else 2
 // (22016 x 2048: 8.3 us; 2560 x 2048: 3.05; 2048 x 2048: 2.76; 2048 x 11008: 6.25); at M = 3
 // and 4, 4 (faster than the matrix cores on every decode, classify and Gemma-shaped matrix:
 // 22016 x 2048 10.0 vs 15.8 us at M = 3, 11.3 vs 16.0 at M = 4; from M = 6 the matrix cores
@@ -890,7 +892,9 @@ bool launch_gemv_rs(int M, const uint32_t* qw, const uint16_t* s, const uint16_t
   if (KS > 8 || M < 1 || M > 4 || (M == 1 && C <= 32)) return false;
   const int64_t units = (int64_t)N * KS;
   if (M == 1) {
-    const int R = units >= 30000 ? 4 : (units >= 16000 && KS == 1) ? 3 : 2;
+    constexpr int kSimds = 256 * 4;  // MI355X: 256 CUs of 4 SIMDs
+    const bool fits3 = KS == 1 && N > 2 * kSimds && N <= 3 * kSimds;
+    const int R = units >= 30000 ? 4 : ((units >= 16000 && KS == 1) || fits3) ? 3 : 2;
     launch_rs_ks<SYM, 1>(KS, R, qw, s, b, x, ldx, y, ldy, N, K, st);
   } else if (M == 2) {
     const int R = units >= 12000 ? 4 : (units >= 2304 && KS == 1) ? 3 : 2;

@@ -257,6 +257,13 @@ def test_gemv_small_shapes(w4, m, n, k):
     gemv_case(w4, m, n, k, seed=1000 * m + n + k)
 
 
+@pytest.mark.parametrize("n", [2048, 2049, 2050, 3071, 3072, 3073])
+def test_gemv_rows_per_wave_edges(w4, n):
+    # one-slice rows at M = 1 take 3 rows per wave from 2049 to 3072 rows, 2 on either side;
+    # 2050, 3071 and 3073 end in a partial block of rows
+    gemv_case(w4, 1, n, 2048, seed=n)
+
+
 @pytest.mark.parametrize("m", [1, 2, 3, 4])
 @pytest.mark.parametrize("n,k", [(37, 16448), (9, 20480)])
 def test_gemv_rows_past_16384(w4, m, n, k):
