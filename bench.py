@@ -52,7 +52,7 @@ def parse_args():
     p.add_argument("--unfused", action="store_true", help="run q,k,v and gate,up as separate GEMVs (7 per layer)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-check", action="store_true", help="skip the parity re-check of the timed outputs")
-    p.add_argument("--no-small-m", action="store_true", help="skip the side sections: batched (M = 16, 8), Gemma-shaped and symmetric group-128 GEMVs, speculative verify, the quantizer")
+    p.add_argument("--no-small-m", action="store_true", help="skip the side sections: batched (M = 16, 8), Gemma-shaped and symmetric group-128 GEMVs, speculative verify, the quantizer and the packer")
     p.add_argument("--counters", metavar="MANIFEST",
                    help="counter-collection pass: launch each kernel shape of the step 3 times (eagerly, between "
                         "marker kernels) plus a copy of known size, write the launch plan to MANIFEST and exit; "
@@ -854,6 +854,33 @@ def quantize_bench(torch, np, w4, synth, oracle, copies=4, reps=5):
             "bytes_per_launch": nb, "parity_ok": bool(ok), "copies": copies}
 
 
+def pack_bench(torch, np, w4, synth, oracle, copies=8, reps=5):
+    """The load-time packer on the decode step's gate|up codes ([22016][2048] uint8 codes):
+    graph-timed over `copies` distinct input buffers (together larger than the MALL), GB/s of
+    NK bytes read + NK/2 written, and a bit-exact check of every word against the oracle."""
+    n = sum(nn for name, nn, _ in synth.QWEN25_3B_LAYER if name in ("gate", "up"))
+    k = synth.QWEN25_3B_HIDDEN
+    q_host, _, _ = synth.w4_weights(n, k, seed=0, workload=synth.W_DECODE, layer=901)
+    q0 = torch.from_numpy(q_host).cuda()
+    ins = [q0] + [q0.clone() for _ in range(copies - 1)]
+    out = torch.empty((n, k // 8), dtype=torch.int32, device="cuda")
+    graph = capture(torch, lambda: [w4.w4_pack(t, out=out) for t in ins])
+    graph.replay()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+    nb = n * k + n * k // 2
+    ok = np.array_equal(out.cpu().numpy().view(np.uint32), oracle.pack(q_host))
+    return {"workload": f"w4_pack of [{n}][{k}] uint8 codes (gate|up)", "avg_us": round(us, 3),
+            "gbps": round(nb / us / 1e3, 1), "frac_hbm": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
+            "bytes_per_launch": nb, "parity_ok": bool(ok), "copies": copies}
+
+
 def cpu_baseline(np, oracle, synth):
     """The oracle's GEMV (unpack + exact dequant + fp64 product) over the seven matrices of as
     many decoder layers as take about 10 s, at M = 1, on this host's cores."""
@@ -1023,7 +1050,7 @@ def main():
         sm = small_m(torch, np, w4, synth, oracle)
         log(f"small-M GEMVs in {time.time() - t0:.1f}s: " + "; ".join(f"{c['workload']} {c['gbps']} GB/s" for c in sm))
 
-    qz = sv = ih = hs = sg = vg = None
+    qz = pk = sv = ih = hs = sg = vg = None
     if not args.no_small_m:
         vg = vendor_gemm(torch, wl, kt)
         log("hipBLASLt on the prefill shapes: " + "; ".join(
@@ -1040,6 +1067,8 @@ def main():
         log(f"speculative verify: {sv['us']} us, parity {'ok' if sv['parity_ok'] else 'FAILED'}")
         qz = quantize_bench(torch, np, w4, synth, oracle)
         log(f"quantizer: {qz['avg_us']} us, {qz['gbps']} GB/s, parity {'ok' if qz['parity_ok'] else 'FAILED'}")
+        pk = pack_bench(torch, np, w4, synth, oracle)
+        log(f"packer: {pk['avg_us']} us, {pk['gbps']} GB/s, parity {'ok' if pk['parity_ok'] else 'FAILED'}")
 
     ctx = context(torch)
     log(f"context: device copy {ctx['copy_1gib_read_plus_write_gbps']} GB/s; clocks {ctx.get('clocks_after_timing')}")
@@ -1093,13 +1122,14 @@ def main():
         "parity": check,
         "small_m": sm,
         "quantize": qz,
+        "pack": pk,
         "spec_verify": sv,
         "int4_head": ih,
         "heads": hs,
         "single_gemv": sg,
         "vendor_gemm_context": vg,
     }
-    if ((sm is not None and not all(c["parity_ok"] for c in sm)) or (qz is not None and not qz["parity_ok"])
+    if ((sm is not None and not all(c["parity_ok"] for c in sm)) or (qz is not None and not qz["parity_ok"]) or (pk is not None and not pk["parity_ok"])
             or (sv is not None and not sv["parity_ok"]) or (ih is not None and not ih["parity_ok"])
             or (hs is not None and not all(v_["parity_ok"] for v_ in hs.values()))
             or (sg is not None and not sg["parity_ok"])):
