@@ -43,7 +43,7 @@ def upload_layer(w4, q, s, b):
 # ----------------------------------------------------------------------------- pack
 
 
-@pytest.mark.parametrize("n,k", [(1, 64), (3, 128), (37, 960), (4864, 896), (257, 2048)])
+@pytest.mark.parametrize("n,k", [(1, 64), (3, 128), (37, 960), (4864, 896), (257, 2048), (5, 11008), (22016, 2048), (2048, 11008)])
 def test_pack_bit_exact(w4, n, k):
     q = synth.codes(n, k, seed=n + k)
     got = to_np(w4.w4_pack(dev(q))).view(np.uint32)
