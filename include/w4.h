@@ -162,6 +162,21 @@ int gemm_f16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, flo
 int logits_argmax_topk(const float* logits, int64_t ldl, int64_t M, int64_t V, int64_t k,
                        int32_t* idx, float* val, void* ws, size_t* ws_bytes, w4_stream_t stream);
 
+/*
+ * logits_argmax_topk_noalloc -- logits_argmax_topk for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, requirements, results and errors as logits_argmax_topk, minus
+ * the workspace: the pass-1 candidates (M * ceil(V / chunk) * k * 8 bytes, the size
+ * logits_argmax_topk would ask for) go to a 4 MiB array that the library holds on each device
+ * until the process ends.  Needing more than 4 MiB returns W4_ERR_WORKSPACE without launching
+ * (e.g. top-64 of 262144 logits needs 32 KiB per row, so up to 128 such rows per call).  The
+ * call allocates nothing.  Calls that overlap on one device (concurrent streams, or host
+ * threads) share that array and race: serialise them.  Nothing in the array has to start at
+ * zero; every call overwrites what it reads.
+ */
+int logits_argmax_topk_noalloc(const float* logits, int64_t ldl, int64_t M, int64_t V, int64_t k,
+                               int32_t* idx, float* val, w4_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

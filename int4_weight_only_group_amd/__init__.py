@@ -19,6 +19,7 @@ from ._lib import lib, LIB_PATH  # noqa: F401
 
 __all__ = [
     "W4Error", "w4_pack", "w4_quantize", "w4_gemv", "w4_gemv_sym128", "w4_dequant_f16_t_sym128", "w4_dequant_f16_t", "gemm_f16", "logits_argmax_topk",
+    "logits_argmax_topk_noalloc",
     "topk_workspace_bytes", "gemm_workspace_bytes", "status_string",
 ]
 
@@ -285,4 +286,27 @@ def logits_argmax_topk(logits: torch.Tensor, k: int, idx: torch.Tensor | None = 
     _check("logits_argmax_topk", lib().logits_argmax_topk(
         logits.data_ptr(), ldl, m, v, k, idx.data_ptr(), val.data_ptr(), ws_ptr,
         ctypes.byref(cap) if need.value else None, _stream()))
+    return idx, val
+
+
+def logits_argmax_topk_noalloc(logits: torch.Tensor, k: int, idx: torch.Tensor | None = None,
+                               val: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """logits_argmax_topk without a workspace: the library's own per-device scratch array holds
+    the candidates (so the call allocates nothing when idx and val are given).  Calls that
+    overlap on one device share that array."""
+    _dev(logits, "logits", torch.float32)
+    ldl = _rowmajor(logits, "logits")
+    m, v = logits.shape
+    if idx is None:
+        idx = torch.empty((m, k), dtype=torch.int32, device=logits.device)
+    if val is None:
+        val = torch.empty((m, k), dtype=torch.float32, device=logits.device)
+    _dev(idx, "idx", torch.int32)
+    _dev(val, "val", torch.float32)
+    _contig(idx, "idx")
+    _contig(val, "val")
+    if tuple(idx.shape) != (m, k) or tuple(val.shape) != (m, k):
+        raise ValueError("idx and val must be [M][k]")
+    _check("logits_argmax_topk_noalloc", lib().logits_argmax_topk_noalloc(
+        logits.data_ptr(), ldl, m, v, k, idx.data_ptr(), val.data_ptr(), _stream()))
     return idx, val

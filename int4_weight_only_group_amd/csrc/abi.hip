@@ -219,4 +219,25 @@ int logits_argmax_topk(const float* logits, int64_t ldl, int64_t M, int64_t V, i
   }
 }
 
+int logits_argmax_topk_noalloc(const float* logits, int64_t ldl, int64_t M, int64_t V, int64_t k,
+                               int32_t* idx, float* val, w4_stream_t stream) {
+  try {
+    if (!logits || !idx || !val) return W4_ERR_NULL;
+    if (M < 1 || M > 65535 || V < 1 || V >= ((int64_t)1 << 31) || k < 1 || k > 256 || k > V ||
+        ldl < V)
+      return W4_ERR_SHAPE;
+    if (w4::topk_chunk(V, (int)k) == 0) return W4_ERR_SHAPE;
+    if (!al4(logits) || !al4(idx) || !al4(val)) return W4_ERR_ALIGN;
+    if (w4::topk_ws_bytes(M, V, (int)k) > w4::kTopkScratchBytes) return W4_ERR_WORKSPACE;
+    if (int e = check_device()) return e;
+    void* scratch = w4::topk_scratch();  // this device's copy of the library's array
+    if (scratch == nullptr) return W4_ERR_INTERNAL;
+    (void)hipGetLastError();
+    w4::launch_topk(logits, ldl, (int)M, (int)V, (int)k, idx, val, scratch, (hipStream_t)stream);
+    return launched();
+  } catch (...) {
+    return W4_ERR_INTERNAL;
+  }
+}
+
 }  // extern "C"

@@ -519,4 +519,39 @@ void launch_topk(const float* logits, int64_t ldl, int M, int V, int k, int32_t*
   final_pass(logits, ldl, M, V, k, cand, nchunks * k, idx, val, st);
 }
 
+// ------------------------------------------------------------ allocation-free variant
+// Callers that cannot allocate device memory (code under graph capture, tight serving loops)
+// get the pass-1 candidates in a file-scope device array instead of a workspace.  Host code
+// never passes the array's name to a kernel: on the host that name is only a stand-in, so
+// the device address is fetched once per device with hipGetSymbolAddress and kept.
+namespace {
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+}  // namespace w4
+
+// One array per device, held until the process ends; calls on one device share it.
+static __device__ __align__(256) uint64_t scratch[w4::kTopkScratchBytes / sizeof(uint64_t)];
+
+namespace w4 {
+
+void* topk_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess) {
+      g_scratch_ptr[dev] = p;
+    } else {
+      (void)hipGetLastError();
+      g_scratch_ptr[dev] = nullptr;
+    }
+  });
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace w4

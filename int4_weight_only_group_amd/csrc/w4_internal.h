@@ -80,6 +80,10 @@ int topk_chunk(int64_t V, int k);        // 0 when the shape is unsupported
 size_t topk_ws_bytes(int64_t M, int64_t V, int k);
 void launch_topk(const float* logits, int64_t ldl, int M, int V, int k, int32_t* idx, float* val,
                  void* ws, hipStream_t st);
+// The allocation-free top-k's file-scope device array: its size, and its device address on
+// the current device (fetched once per device; nullptr if the runtime cannot give it).
+constexpr size_t kTopkScratchBytes = (size_t)4 << 20;
+void* topk_scratch();
 
 // Runs f once for the current device.  Function attributes such as the dynamic LDS limit are
 // set per device, so a process that launches on several GPUs sets them on each.
