@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
+ROTATE_BYTES = 1 << 30  # distinct bytes a timed loop cycles through (4x the 256 MB last-level cache)
 METRIC = "W4 GEMV GB/s (% of HBM peak); prefill dequant+GEMM TFLOP/s (% MFMA peak)"
 TOPK = 40
 
@@ -59,14 +60,26 @@ def parse_args():
                         "run under rocprofv3 --pmc")
     p.add_argument("--util-from", nargs=2, metavar=("MANIFEST", "UTIL_CSV"),
                    help="reduce a `rocprofv3 --pmc VALUBusy MfmaUtil` run of --counters into profiles/utilization.json")
-    p.add_argument("--traffic-from", nargs=3, metavar=("MANIFEST", "FETCH_CSV", "WRITE_CSV"),
-                   help="(no GPU) turn the FETCH_SIZE and WRITE_SIZE counter CSVs of two --counters passes into "
-                        "profiles/traffic.json and print a table of them")
+    p.add_argument("--trace-from", nargs="+", metavar="FILE",
+                   help="(no GPU) PROFILED_JSON TRACE_CSV [UNPROFILED_JSON]: reduce a rocprofv3 --kernel-trace run "
+                        "of bench.py (its JSON line and its kernel_trace.csv) into profiles/kernel_trace.json, "
+                        "rocprof durations per kernel shape beside the unprofiled run's per-launch times")
+    p.add_argument("--traffic-from", nargs=3, metavar=("MANIFEST", "READ_CSV", "WRITE_CSV"),
+                   help="(no GPU) turn the counter CSVs of two --counters passes (read requests by size, then "
+                        "write requests) into profiles/traffic.json and print a table of them")
     return p.parse_args()
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def sha256_of(*arrays):
+    """SHA-256 of host buffers' bytes, in order (C order, native little-endian)."""
+    h = hashlib.sha256()
+    for a in arrays:
+        h.update(memoryview(a).cast("B") if a.flags.c_contiguous else a.tobytes())
+    return h.hexdigest()
 
 
 def gemv_bytes(m, n, k):
@@ -83,6 +96,10 @@ class Workload:
         t0 = time.time()
         self.layers = []  # per layer: list of (names, qw, s, b, x, y, (M, N, K))
         self.gemv_bytes = 0
+        # SHA-256 of every input buffer as drawn on the host; a decode layer's buffers are
+        # summarised by one digest over their own digests, in launch order (codes, scales,
+        # biases of each GEMV, then each activation vector the first time it is read)
+        self.sha = {"decode_layers": []}
         # q, k, v read one activation and gate, up another (as in the model); by default each
         # group is stored row-concatenated so it runs as one GEMV (identical outputs).
         groups = ([["q"], ["k"], ["v"], ["o"], ["gate"], ["up"], ["down"]] if unfused
@@ -92,6 +109,7 @@ class Workload:
         for l in range(synth.QWEN25_3B_LAYERS):
             xs = {}
             mats = []
+            digests = []
             for grp in groups:
                 qs, ss, bs = [], [], []
                 for name in grp:
@@ -99,18 +117,21 @@ class Workload:
                     q, s, b = synth.w4_weights(n, k, seed=0, workload=synth.W_DECODE, layer=l * 16 + j)
                     qs.append(q); ss.append(s); bs.append(b)
                 q, s, b = np.concatenate(qs), np.concatenate(ss), np.concatenate(bs)
+                digests += [sha256_of(q), sha256_of(s), sha256_of(b)]
                 n, k = q.shape
                 qw = w4.w4_pack(torch.from_numpy(q).to(dev))
                 src = src_of[grp[0]]
                 if src not in xs:
                     slot = ["attn", "o", "mlp", "down"].index(src)
-                    xs[src] = torch.from_numpy(synth.activations(1, k, seed=0, workload=synth.W_DECODE,
-                                                                 layer=l * 16 + 8 + slot)).to(dev)
+                    xh = synth.activations(1, k, seed=0, workload=synth.W_DECODE, layer=l * 16 + 8 + slot)
+                    digests.append(sha256_of(xh))
+                    xs[src] = torch.from_numpy(xh).to(dev)
                 y = torch.empty((1, n), dtype=torch.float32, device=dev)
                 mats.append(("+".join(grp), qw, torch.from_numpy(s).to(dev), torch.from_numpy(b).to(dev), xs[src], y,
                              (1, n, k)))
                 self.gemv_bytes += gemv_bytes(1, n, k)
             self.layers.append(mats)
+            self.sha["decode_layers"].append(hashlib.sha256("".join(digests).encode()).hexdigest())
         log(f"decode weights packed on the GPU in {time.time() - t0:.1f}s ({self.gemv_bytes / 1e9:.3f} GB per step)")
 
         t0 = time.time()
@@ -118,6 +139,8 @@ class Workload:
         self.head_host = synth.head_f16(self.H, self.V, seed=0, workload=synth.W_DECODE, layer=999)
         self.head = torch.from_numpy(self.head_host).to(dev)
         self.x_head_host = synth.activations(1, self.H, seed=0, workload=synth.W_DECODE, layer=998)
+        self.sha["head"] = sha256_of(self.head_host)
+        self.sha["x_head"] = sha256_of(self.x_head_host)
         self.x_head = torch.from_numpy(self.x_head_host).to(dev)
         self.logits = torch.empty((1, self.V), dtype=torch.float32, device=dev)
         self.idx = torch.empty((1, TOPK), dtype=torch.int32, device=dev)
@@ -139,12 +162,15 @@ class Workload:
             ntot = sum(mats[nm][1] for nm in names)
             if k not in a_host:
                 a_host[k] = synth.activations(self.M, k, seed=0, workload=synth.W_PREFILL, layer=100 + k)
+                self.sha[f"prefill_A_{self.M}x{k}"] = sha256_of(a_host[k])
             wt = torch.empty((k, ntot), dtype=torch.float16, device=dev)
             col = 0
             parts = []
             for nm in names:
                 j, n, _ = mats[nm]
                 q, s, b = synth.w4_weights(n, k, seed=0, workload=synth.W_PREFILL, layer=j)
+                self.sha[f"prefill_{nm}_q"], self.sha[f"prefill_{nm}_s"], self.sha[f"prefill_{nm}_b"] = (
+                    sha256_of(q), sha256_of(s), sha256_of(b))
                 qw = w4.w4_pack(torch.from_numpy(q).to(dev))
                 self.prefill_w.append((nm, qw, torch.from_numpy(s).to(dev), torch.from_numpy(b).to(dev),
                                        wt[:, col:col + n], (n, k), (q, s, b)))
@@ -249,9 +275,22 @@ def kernel_groups(wl):
         for name, qw, s, b, x, y, (m, n, k) in mats:
             add(("w4_gemv", m, n, k), gemv_bytes(m, n, k), 0,
                 lambda qw=qw, s=s, b=b, x=x, y=y: wl.w4.w4_gemv(qw, s, b, x, out=y))
-    for name, qw, s, b, view, (n, k), _ in wl.prefill_w:
-        add(("w4_dequant_f16_t", 0, n, k), n * k // 2 + n * k // 16 + 2 * n * k, 0,
-            lambda qw=qw, s=s, b=b, view=view: wl.w4.w4_dequant_f16_t(qw, s, b, out=view))
+    # the dequant shapes rotate through distinct copies of their inputs and outputs, together at
+    # least ROTATE_BYTES per shape, so no launch finds its operands in the last-level cache
+    torch = wl.torch
+    per_shape = {}
+    for w in wl.prefill_w:
+        per_shape.setdefault(w[5], []).append(w)
+    for (n, k), ws_ in per_shape.items():
+        nb = n * k // 2 + n * k // 16 + 2 * n * k
+        copies = -(-ROTATE_BYTES // nb)
+        for c in range(copies):
+            _, qw, s, b, _, _, _ = ws_[c % len(ws_)]
+            if c >= len(ws_):
+                qw, s, b = qw.clone(), s.clone(), b.clone()
+            view = torch.empty((k, n), dtype=torch.float16, device="cuda")
+            add(("w4_dequant_f16_t", 0, n, k), nb, 0,
+                lambda qw=qw, s=s, b=b, view=view: wl.w4.w4_dequant_f16_t(qw, s, b, out=view))
     for name, a, wt, c, (m, n, k), _, _ in wl.prefill_g:
         add(("gemm_f16", m, n, k), 2 * (m * k + k * n) + 4 * m * n, 2 * m * n * k,
             lambda a=a, wt=wt, c=c: wl.w4.gemm_f16(a, wt, out=c, workspace=wl.gemm_ws))
@@ -270,16 +309,23 @@ def kernel_timings(torch, wl, reps=5, min_launches=36):
     duration including the in-graph dispatch gap (a conservative figure)."""
     groups = kernel_groups(wl)
     stream = torch.cuda.current_stream()
+    # an int16 fill before each shape's timed replays and a uint8 fill after them (kernels
+    # nothing else here launches): in a kernel trace of this run the dispatches between the two
+    # are exactly one shape's timed launches (see --trace-from)
+    marker = torch.empty(4097, dtype=torch.int16, device="cuda")
+    end_marker = torch.empty(4097, dtype=torch.uint8, device="cuda")
     out = {}
     for key, g in groups.items():
         fns = g["fns"] * ((min_launches + len(g["fns"]) - 1) // len(g["fns"]))
         graph = capture(torch, lambda fns=fns: [f() for f in fns])
         graph.replay()
+        marker.fill_(1)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(reps):
             graph.replay()
         e1.record(stream)
+        end_marker.fill_(1)
         torch.cuda.synchronize()
         avg = e0.elapsed_time(e1) * 1e3 / (reps * len(fns))
         out[key] = {"launches": reps * len(fns), "avg_us": avg, "bytes": g["bytes"], "flops": g["flops"],
@@ -287,10 +333,88 @@ def kernel_timings(torch, wl, reps=5, min_launches=36):
     return out
 
 
+def _short_name(kernel_name):
+    return (kernel_name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+            .replace("w4::", ""))
+
+
+def _bench_line(path):
+    with open(path) as f:
+        return json.loads([l for l in f if l.lstrip().startswith("{")][-1])
+
+
+def trace_from(bench_json, trace_csv, unprofiled_json=None, out_path=None):
+    """profiles/kernel_trace.json from a rocprofv3 --kernel-trace run of bench.py: per kernel shape
+    of the per-shape timing section (the dispatches between the start and end markers, in the
+    order of the run's own `kernels` field), rocprof's kernel durations (End - Start) beside the
+    HIP-event time per launch of the same command run without the profiler (unprofiled_json;
+    the profiled run's own event times include the profiler's wait between dispatches)."""
+    import csv
+    import statistics
+    ker = _bench_line(bench_json)["kernels"]
+    live = _bench_line(unprofiled_json)["kernels"] if unprofiled_json else ker
+    rows = sorted(csv.DictReader(open(trace_csv, newline="")), key=lambda r: int(r["Dispatch_Id"]))
+    # a segment opens at an int16 fill and closes at the next uint8 fill (or, in traces taken
+    # without end markers, at the next int16 fill: its timed launches are then its first ones)
+    segs, cur = [], None
+    for r in rows:
+        name = r["Kernel_Name"]
+        if "FillFunctor<short>" in name or "FillFunctor<unsigned char>" in name:
+            if cur is not None:
+                segs.append(cur)
+            cur = [] if "FillFunctor<short>" in name else None
+        elif cur is not None:
+            cur.append(r)
+    if len(segs) != len(ker):
+        raise SystemExit(f"{len(segs)} marker segments, but the run timed {len(ker)} kernel shapes")
+    out = {"method": "rocprofv3 --kernel-trace --stats of bench.py; per kernel shape, the dispatches of bench.py's "
+                     "per-shape timing section (between int16-fill markers); duration = End - Start per dispatch",
+           "kernels": {}}
+    print("| kernel shape | dispatches | kernels (grid) | rocprof mean us | median us | min us | bench us per launch | mean / bench |")
+    print("|---|---|---|---|---|---|---|---|")
+    for (key, k), seg in zip(ker.items(), segs):
+        # one shape's launch may be several kernels (the split-K GEMM and its reduce): the launch
+        # repeats once the first dispatch's kernel and grid come round again
+        sig = [(r["Kernel_Name"], r["Grid_Size_X"]) for r in seg]
+        per = next((i for i in range(1, len(sig)) if sig[i] == sig[0]), len(sig))
+        if len(seg) < per * k["launches"]:
+            raise SystemExit(f"{key}: {len(seg)} dispatches for {k['launches']} launches of {per} kernels")
+        seg = seg[:per * k["launches"]]
+        durs = [sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in seg[i * per:(i + 1) * per]) / 1e3
+                for i in range(k["launches"])]
+        names = sorted({_short_name(r["Kernel_Name"]) + f"[{int(r['Grid_Size_X']) // int(r['Workgroup_Size_X'])}]"
+                        for r in seg})
+        src = SOURCE_OF[key.split("/")[0]]
+        ent = {"source_sha": source_hash(src), "dispatches": len(seg), "kernels_per_launch": per,
+               "kernels": names, "mean_us": statistics.mean(durs), "median_us": statistics.median(durs),
+               "min_us": min(durs), "bench_avg_launch_us": live[key]["avg_us"],
+               "mean_over_bench": statistics.mean(durs) / live[key]["avg_us"]}
+        out["kernels"][key] = ent
+        print(f"| {key} | {len(seg)} | {', '.join(names)} | {ent['mean_us']:.2f} | {ent['median_us']:.2f} | "
+              f"{ent['min_us']:.2f} | {live[key]['avg_us']:.2f} | {ent['mean_over_bench']:.3f} |")
+    path = out_path or os.path.join(ROOT, "profiles", "kernel_trace.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(f"wrote {path}")
+
+
+def trace_for(key):
+    """rocprof's per-dispatch duration of a kernel shape from the committed trace summary, if it
+    was taken on the current kernel source; else None."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "kernel_trace.json")) as f:
+            ent = json.load(f)["kernels"][key]
+        if ent.get("source_sha") != source_hash(SOURCE_OF[key.split("/")[0]]):
+            return None
+        return ent
+    except Exception:
+        return None
+
+
 SOURCE_OF = {"w4_gemv": "gemv.hip", "w4_dequant_f16_t": "dequant.hip", "gemm_f16": "gemm.hip",
              "logits_argmax_topk": "topk.hip"}
 COUNTER_REPS = 3
-COPY_ELEMS = 128 << 20  # f16 elements of the calibration copy (256 MiB read, 256 MiB written)
+COPY_ELEMS = 128 << 20  # f16 elements of the validation copy (256 MiB read, 256 MiB written)
 
 
 def small_m_groups(torch, np, w4, synth):
@@ -320,9 +444,15 @@ def small_m_groups(torch, np, w4, synth):
     return groups
 
 
+# Kernels of known bytes that validate the byte counts: a plain copy (whole 128-byte lines) and
+# copies that read 64 or 32 bytes of every 128 (rows of 32 or 16 f16 out of 64).  Each reads
+# exactly the bytes it touches if the L2 fetches at request granularity.
+VALIDATION = (("copy", 64), ("copy_64B_of_each_128B", 32), ("copy_32B_of_each_128B", 16))
+
+
 def counters_pass(torch, wl, manifest_path):
     """Launch plan for the counter runs: a marker kernel (an int16 fill, a kernel nothing
-    else here launches), then a copy of known size COUNTER_REPS times, then for each kernel
+    else here launches), then each validation copy COUNTER_REPS times, then for each kernel
     shape COUNTER_REPS launches on different weights, each group followed by a marker.
     The plan and the algorithmic bytes of each group go to manifest_path."""
     # every buffer (and the packing launches that build them) before the first marker
@@ -330,13 +460,18 @@ def counters_pass(torch, wl, manifest_path):
     groups.update(small_m_groups(torch, wl.np, wl.w4, wl.synth))
     marker = torch.empty(4097, dtype=torch.int16, device="cuda")
     src = torch.ones(COPY_ELEMS, dtype=torch.float16, device="cuda")
-    dst = torch.empty_like(src)
-    plan = [{"key": "copy", "read_bytes": 2 * COPY_ELEMS, "write_bytes": 2 * COPY_ELEMS, "source": None}]
+    views = []
+    for key, cols in VALIDATION:
+        sv = src.view(-1, 64)[:, :cols]
+        views.append((key, sv, torch.empty(sv.shape, dtype=torch.float16, device="cuda")))
+    plan = [{"key": key, "kind": "validation", "read_bytes": 2 * sv.numel(), "write_bytes": 2 * sv.numel(),
+             "source": None} for key, sv, _ in views]
     torch.cuda.synchronize()
     marker.fill_(1)
-    for _ in range(COUNTER_REPS):
-        torch.neg(src, out=dst)
-    marker.fill_(1)
+    for _, sv, dv in views:
+        for _ in range(COUNTER_REPS):
+            torch.neg(sv, out=dv)
+        marker.fill_(1)
     for key, g in groups.items():
         fns = g["fns"]
         for r in range(COUNTER_REPS):
@@ -350,32 +485,9 @@ def counters_pass(torch, wl, manifest_path):
     log(f"counter pass: {len(plan)} groups of {COUNTER_REPS} launches; plan in {manifest_path}")
 
 
-def _counter_segments(csv_path, counter):
-    """Per marker-delimited segment (after the first marker): the summed counter of every
-    dispatch in it and the dispatched kernels' names."""
-    import csv
-    disp = {}
-    with open(csv_path, newline="") as f:
-        for r in csv.DictReader(f):
-            d = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "v": 0.0})
-            if r["Counter_Name"] == counter:
-                d["v"] += float(r["Counter_Value"])
-    segs, cur, started = [], None, False
-    for i in sorted(disp):
-        d = disp[i]
-        if "FillFunctor<short>" in d["name"]:
-            if started:
-                segs.append(cur)
-            started, cur = True, {"v": 0.0, "names": []}
-        elif started:
-            cur["v"] += d["v"]
-            cur["names"].append(d["name"].replace("(anonymous namespace)::", "").split("(")[0][:80])
-    return segs
-
-
 def _counter_dispatches(csv_path, counters):
     """Per marker-delimited segment (after the first marker): each dispatch's kernel name and
-    the values of the named counters (derived metrics such as VALUBusy are per dispatch)."""
+    the values of the named counters (summed over the rows rocprofv3 writes per dispatch)."""
     import csv
     disp = {}
     with open(csv_path, newline="") as f:
@@ -395,6 +507,15 @@ def _counter_dispatches(csv_path, counters):
     return segs
 
 
+def _segment_sums(csv_path, counters):
+    """Per segment: the sum over its dispatches of each counter, and the kernel names."""
+    out = []
+    for seg in _counter_dispatches(csv_path, counters):
+        tot = {c: sum(v.get(c, 0.0) for _, v in seg) for c in counters}
+        out.append({"v": tot, "names": [n for n, _ in seg]})
+    return out
+
+
 UTIL_COUNTERS = ("VALUBusy", "MfmaUtil")
 
 
@@ -412,7 +533,9 @@ def util_from(manifest_path, csv_path, out_path=None):
                      "over the launches of each kernel in a shape's group", "kernels": {}}
     print("| kernel shape | dispatched kernel | launches | VALUBusy % | MfmaUtil % |")
     print("|---|---|---|---|---|")
-    for g, seg in zip(groups[1:], segs[1:]):
+    for g, seg in zip(groups, segs):
+        if g.get("kind") == "validation":
+            continue
         per = {}
         for name, v in seg:
             per.setdefault(name, []).append(v)
@@ -428,36 +551,59 @@ def util_from(manifest_path, csv_path, out_path=None):
     print(f"wrote {path}")
 
 
-def traffic_from(manifest_path, fetch_csv, write_csv, out_path=None):
-    """profiles/traffic.json from two counter runs of the --counters pass.  FETCH_SIZE and
-    WRITE_SIZE (KiB per dispatch, read at the L2's memory side) are scaled by the factor that
-    makes the calibration copy read and write exactly its known bytes."""
+# HBM traffic from the L2's requests to the memory side, by request size.  FETCH_SIZE, the
+# derived counter, takes every read that is not 32 bytes as 64 unless TCC_BUBBLE fires, so it
+# undercounts 128-byte reads by half; here every size has its own counter.
+READ_COUNTERS = ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum")
+WRITE_COUNTERS = ("TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum", "TCC_EA0_RDREQ_DRAM_sum", "TCC_EA0_WRREQ_DRAM_sum")
+
+
+def read_bytes_of(v):
+    return 32 * v["TCC_EA0_RDREQ_32B_sum"] + 64 * v["TCC_EA0_RDREQ_64B_sum"] + 128 * v["TCC_EA0_RDREQ_128B_sum"]
+
+
+def write_bytes_of(v):
+    # write requests are 32 or 64 bytes
+    return 32 * (v["TCC_EA0_WRREQ_sum"] - v["TCC_EA0_WRREQ_64B_sum"]) + 64 * v["TCC_EA0_WRREQ_64B_sum"]
+
+
+def traffic_from(manifest_path, read_csv, write_csv, out_path=None):
+    """profiles/traffic.json from two counter runs of the --counters pass: the read requests by
+    size (READ_COUNTERS), then the write requests (WRITE_COUNTERS).  Bytes per launch are the
+    requests times their sizes, with no calibration factor; the validation copies show how
+    close that comes to the bytes they touch."""
     with open(manifest_path) as f:
         man = json.load(f)
     reps = man["reps"]
-    fs, ws = _counter_segments(fetch_csv, "FETCH_SIZE"), _counter_segments(write_csv, "WRITE_SIZE")
+    rs, ws = _segment_sums(read_csv, READ_COUNTERS), _segment_sums(write_csv, WRITE_COUNTERS)
     groups = man["groups"]
-    if len(fs) != len(groups) or len(ws) != len(groups):
-        raise SystemExit(f"segments {len(fs)}/{len(ws)} do not match the plan's {len(groups)} groups")
-    copy = groups[0]
-    f_fac = copy["read_bytes"] / (fs[0]["v"] / reps * 1024)
-    w_fac = copy["write_bytes"] / (ws[0]["v"] / reps * 1024)
-    out = {"method": "rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, over bench.py --counters; KiB per "
-                     "dispatch summed over each call's dispatches, averaged over the calls, scaled by the copy factors",
-           "copy_calibration": {"bytes_read": copy["read_bytes"], "bytes_written": copy["write_bytes"],
-                                "fetch_kib_per_launch": fs[0]["v"] / reps, "write_kib_per_launch": ws[0]["v"] / reps,
-                                "fetch_factor": f_fac, "write_factor": w_fac},
-           "kernels": {}}
-    rows = []
-    for g, fseg, wseg in zip(groups[1:], fs[1:], ws[1:]):
-        rd = fseg["v"] / reps * 1024 * f_fac
-        wr = wseg["v"] / reps * 1024 * w_fac
-        out["kernels"][g["key"]] = {"source_sha": g["source_sha"], "dispatches": sorted(set(fseg["names"])),
-                                    "fetch_kib_raw": fseg["v"] / reps, "write_kib_raw": wseg["v"] / reps,
-                                    "hbm_read_bytes": rd, "hbm_write_bytes": wr, "hbm_bytes_per_launch": rd + wr,
-                                    "algorithmic_bytes": g["bytes"], "traffic_over_algorithmic": (rd + wr) / g["bytes"]}
+    if len(rs) != len(groups) or len(ws) != len(groups):
+        raise SystemExit(f"segments {len(rs)}/{len(ws)} do not match the plan's {len(groups)} groups")
+    out = {"method": "rocprofv3 --pmc " + " ".join(READ_COUNTERS) + ", then --pmc " + " ".join(WRITE_COUNTERS)
+                     + ", over bench.py --counters; read bytes = 32*RDREQ_32B + 64*RDREQ_64B + 128*RDREQ_128B, "
+                     "write bytes = 32*(WRREQ - WRREQ_64B) + 64*WRREQ_64B, summed over each call's dispatches and "
+                     "averaged over the calls",
+           "validation": {}, "kernels": {}}
+    rows, vrows = [], []
+    for g, rseg, wseg in zip(groups, rs, ws):
+        rv = {c: x / reps for c, x in rseg["v"].items()}
+        wv = {c: x / reps for c, x in wseg["v"].items()}
+        rd, wr = read_bytes_of(rv), write_bytes_of(wv)
+        sizes_sum = rv["TCC_EA0_RDREQ_32B_sum"] + rv["TCC_EA0_RDREQ_64B_sum"] + rv["TCC_EA0_RDREQ_128B_sum"]
+        ent = {"read_requests": rv, "write_requests": wv, "read_bytes": rd, "write_bytes": wr,
+               "read_requests_by_size_over_all": sizes_sum / rv["TCC_EA0_RDREQ_sum"] if rv["TCC_EA0_RDREQ_sum"] else None}
+        if g.get("kind") == "validation":
+            ent.update(touched_read_bytes=g["read_bytes"], touched_write_bytes=g["write_bytes"],
+                       read_over_touched=rd / g["read_bytes"], write_over_touched=wr / g["write_bytes"])
+            out["validation"][g["key"]] = ent
+            vrows.append((g["key"], g["read_bytes"], rd, g["write_bytes"], wr))
+            continue
+        ent.update(source_sha=g["source_sha"], dispatches=sorted(set(rseg["names"])), hbm_read_bytes=rd,
+                   hbm_write_bytes=wr, hbm_bytes_per_launch=rd + wr, algorithmic_bytes=g["bytes"],
+                   traffic_over_algorithmic=(rd + wr) / g["bytes"])
+        out["kernels"][g["key"]] = ent
         rows.append((g["key"], g["bytes"], rd, wr, (rd + wr) / g["bytes"]))
-    # the three prefill GEMMs together, per launch
+    # the prefill GEMMs together, per launch
     pre = [k for k in out["kernels"] if k.startswith("gemm_f16_1570_")]
     if pre:
         ks = [out["kernels"][k] for k in pre]
@@ -468,7 +614,11 @@ def traffic_from(manifest_path, fetch_csv, write_csv, out_path=None):
     path = out_path or os.path.join(ROOT, "profiles", "traffic.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
-    print(f"copy factors: fetch {f_fac:.3f}, write {w_fac:.3f}")
+    print("| validation kernel | bytes read (touched) | counted read | bytes written | counted write |")
+    print("|---|---|---|---|---|")
+    for key, tr, rd, tw, wr in vrows:
+        print(f"| {key} | {tr} | {rd:.0f} ({rd / tr:.3f}x) | {tw} | {wr:.0f} ({wr / tw:.3f}x) |")
+    print()
     print("| kernel shape | algorithmic B | HBM read B | HBM write B | traffic / algorithmic |")
     print("|---|---|---|---|---|")
     for key, b, rd, wr, ratio in rows:
@@ -820,20 +970,22 @@ def spec_verify(torch, np, w4, synth, oracle, wl, reps=20):
             "parity_ok": bool(ok), "rows_in_near_tie": int(loose)}
 
 
-def quantize_bench(torch, np, w4, synth, oracle, copies=4, reps=5):
+def quantize_bench(torch, np, w4, synth, oracle, reps=5):
     """The load-time quantizer on the decode step's gate|up matrix ([22016][2048] f16
-    weights, N(0, 0.02)): graph-timed over `copies` distinct input buffers (together larger
-    than the MALL), GB/s of 2NK bytes read + NK/2 + NK/16 written, and a bit-exact re-check
-    of 64 sampled rows against the oracle."""
+    weights, N(0, 0.02)): graph-timed over distinct input and output buffers that together
+    hold at least 1 GiB, GB/s of 2NK bytes read + NK/2 + NK/16 written, and a bit-exact
+    re-check of 64 sampled rows of the first and last copy against the oracle."""
     n = sum(nn for name, nn, _ in synth.QWEN25_3B_LAYER if name in ("gate", "up"))
     k = synth.QWEN25_3B_HIDDEN
+    nb = 2 * n * k + n * k // 2 + n * k // 16
+    copies = -(-ROTATE_BYTES // nb)
     w_host = synth.float_weights(n, k, seed=0, workload=synth.W_DECODE, layer=900)
     w0 = torch.from_numpy(w_host).cuda()
     ins = [w0] + [w0.clone() for _ in range(copies - 1)]
-    out = (torch.empty((n, k // 8), dtype=torch.int32, device="cuda"),
-           torch.empty((n, k // 64), dtype=torch.float16, device="cuda"),
-           torch.empty((n, k // 64), dtype=torch.float16, device="cuda"))
-    graph = capture(torch, lambda: [w4.w4_quantize(t, out=out) for t in ins])
+    outs = [(torch.empty((n, k // 8), dtype=torch.int32, device="cuda"),
+             torch.empty((n, k // 64), dtype=torch.float16, device="cuda"),
+             torch.empty((n, k // 64), dtype=torch.float16, device="cuda")) for _ in range(copies)]
+    graph = capture(torch, lambda: [w4.w4_quantize(t, out=o) for t, o in zip(ins, outs)])
     graph.replay()
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -843,28 +995,32 @@ def quantize_bench(torch, np, w4, synth, oracle, copies=4, reps=5):
     e1.record(stream)
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
-    nb = 2 * n * k + n * k // 2 + n * k // 16
     rows = np.sort(np.random.default_rng(9).choice(n, 64, replace=False))
     qw_ref, s_ref, b_ref = oracle.quantize(w_host[rows])
-    ok = (np.array_equal(out[0].cpu().numpy().view(np.uint32)[rows], qw_ref)
-          and np.array_equal(out[1].cpu().numpy().view(np.uint16)[rows], s_ref.view(np.uint16))
-          and np.array_equal(out[2].cpu().numpy().view(np.uint16)[rows], b_ref.view(np.uint16)))
+    ok = all(np.array_equal(out[0].cpu().numpy().view(np.uint32)[rows], qw_ref)
+             and np.array_equal(out[1].cpu().numpy().view(np.uint16)[rows], s_ref.view(np.uint16))
+             and np.array_equal(out[2].cpu().numpy().view(np.uint16)[rows], b_ref.view(np.uint16))
+             for out in (outs[0], outs[-1]))
     return {"workload": f"w4_quantize of a [{n}][{k}] f16 matrix (gate|up), N(0, 0.02)", "avg_us": round(us, 3),
             "gbps": round(nb / us / 1e3, 1), "frac_hbm": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
-            "bytes_per_launch": nb, "parity_ok": bool(ok), "copies": copies}
+            "bytes_per_launch": nb, "parity_ok": bool(ok), "copies": copies,
+            "rotated_bytes": copies * nb}
 
 
-def pack_bench(torch, np, w4, synth, oracle, copies=8, reps=5):
+def pack_bench(torch, np, w4, synth, oracle, reps=5):
     """The load-time packer on the decode step's gate|up codes ([22016][2048] uint8 codes):
-    graph-timed over `copies` distinct input buffers (together larger than the MALL), GB/s of
-    NK bytes read + NK/2 written, and a bit-exact check of every word against the oracle."""
+    graph-timed over distinct input and output buffers that together hold at least 1 GiB,
+    GB/s of NK bytes read + NK/2 written, and a bit-exact check of every word of the first
+    and last copy against the oracle."""
     n = sum(nn for name, nn, _ in synth.QWEN25_3B_LAYER if name in ("gate", "up"))
     k = synth.QWEN25_3B_HIDDEN
+    nb = n * k + n * k // 2
+    copies = -(-ROTATE_BYTES // nb)
     q_host, _, _ = synth.w4_weights(n, k, seed=0, workload=synth.W_DECODE, layer=901)
     q0 = torch.from_numpy(q_host).cuda()
     ins = [q0] + [q0.clone() for _ in range(copies - 1)]
-    out = torch.empty((n, k // 8), dtype=torch.int32, device="cuda")
-    graph = capture(torch, lambda: [w4.w4_pack(t, out=out) for t in ins])
+    outs = [torch.empty((n, k // 8), dtype=torch.int32, device="cuda") for _ in range(copies)]
+    graph = capture(torch, lambda: [w4.w4_pack(t, out=o) for t, o in zip(ins, outs)])
     graph.replay()
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -874,38 +1030,111 @@ def pack_bench(torch, np, w4, synth, oracle, copies=8, reps=5):
     e1.record(stream)
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
-    nb = n * k + n * k // 2
-    ok = np.array_equal(out.cpu().numpy().view(np.uint32), oracle.pack(q_host))
+    ref = oracle.pack(q_host)
+    ok = all(np.array_equal(out.cpu().numpy().view(np.uint32), ref) for out in (outs[0], outs[-1]))
     return {"workload": f"w4_pack of [{n}][{k}] uint8 codes (gate|up)", "avg_us": round(us, 3),
             "gbps": round(nb / us / 1e3, 1), "frac_hbm": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
-            "bytes_per_launch": nb, "parity_ok": bool(ok), "copies": copies}
+            "bytes_per_launch": nb, "parity_ok": bool(ok), "copies": copies, "rotated_bytes": copies * nb}
+
+
+def host_metadata(np):
+    """The host the CPU figures were taken on: cores, CPU model, NumPy and its BLAS."""
+    meta = {"nproc": os.cpu_count(), "affinity_cores": len(os.sched_getaffinity(0)),
+            "numpy": np.__version__, "python": sys.version.split()[0]}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    meta["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        meta["cpu_model"] = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        meta["blas"] = [{k: i.get(k) for k in ("internal_api", "version", "num_threads", "threading_layer",
+                                               "architecture")} for i in threadpool_info()]
+    except Exception as e:  # metadata only
+        meta["blas"] = f"unavailable ({type(e).__name__})"
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        meta[var] = os.environ.get(var)
+    return meta
+
+
+def _median_of(np, fn, reps=5):
+    """Median wall time of reps calls after one warm-up call."""
+    fn()
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts)), [round(t, 4) for t in ts]
 
 
 def cpu_baseline(np, oracle, synth):
-    """The oracle's GEMV (unpack + exact dequant + fp64 product) over the seven matrices of as
-    many decoder layers as take about 10 s, at M = 1, on this host's cores."""
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    """The CPU oracle on this host, stage by stage, each the median of 5 timed calls after one
+    warm-up:
+      (a) unpack + exact dequant (NumPy elementwise, one thread) of the gate matrix;
+      (b) the fp64 products through BLAS on all cores and on one thread: the decode GEMV of
+          the gate matrix (with its error-bound product) and a 32-row slice of the prefill
+          GEMM on the gate|up scratch;
+      (c) top-40 selection over the 151936 logits;
+    and, as `value`, the oracle's whole GEMV (unpack, dequant, fp64 product and bound) over
+    the seven int4 matrices of one decoder layer at M = 1, on all cores, in GB/s of the
+    layer's algorithmic bytes (the unit of the GPU figure)."""
+    from threadpoolctl import threadpool_limits, threadpool_info
+    meta = host_metadata(np)
+    all_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    t_start = time.perf_counter()
+    stages = {}
+
+    # (a) unpack + dequant of the 11008 x 2048 gate matrix (NumPy, no BLAS)
+    n, k = 11008, 2048
+    q, s, b = synth.w4_weights(n, k, seed=0, workload=synth.W_DECODE, layer=4)
+    qw = oracle.pack(q)
+    t, ts = _median_of(np, lambda: oracle.dequant_exact(qw, s, b))
+    stages["a_unpack_dequant_1thread"] = {"shape_nk": [n, k], "median_s": t, "samples_s": ts, "threads": 1,
+                                          "gweights_per_s": n * k / t / 1e9, "packed_gbps": (n * k // 2 + n * k // 16) / t / 1e9}
+
+    # (b) fp64 products through BLAS, all cores and one thread
+    w = oracle.dequant_exact(qw, s, b)
+    x = synth.activations(1, k, seed=0, workload=synth.W_DECODE, layer=12).astype(np.float64)
+    wabs = np.abs(w)
+    a_rows = synth.activations(32, k, seed=0, workload=synth.W_PREFILL, layer=100 + k).astype(np.float64)
+    wt = np.ascontiguousarray(w.T)
+    for label, lim in (("all_cores", all_threads), ("1thread", 1)):
+        with threadpool_limits(limits=lim, user_api="blas"):
+            used = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+            t, ts = _median_of(np, lambda: (x @ w.T, np.abs(x) @ wabs.T))
+            stages[f"b_gemv_fp64_{label}"] = {"shape_mnk": [1, n, k], "median_s": t, "samples_s": ts, "threads": used,
+                                              "gflops": 2 * 2 * n * k / t / 1e9}
+            t, ts = _median_of(np, lambda: a_rows @ wt)
+            stages[f"b_gemm_fp64_{label}"] = {"shape_mnk": [32, n, k], "median_s": t, "samples_s": ts,
+                                              "threads": used, "gflops": 2 * 32 * n * k / t / 1e9}
+    del w, wabs, wt
+
+    # (c) top-40 of 151936 logits (f32 values of the head's output scale)
+    v = synth.QWEN25_3B_VOCAB
+    lg = (synth.rng(0, synth.W_DECODE, 997, synth.T_X).standard_normal((1, v)) * 0.905).astype(np.float32)
+    t, ts = _median_of(np, lambda: oracle.topk_ref(lg, TOPK))
+    stages["c_topk40_of_151936"] = {"median_s": t, "samples_s": ts, "threads": 1, "mlogits_per_s": v / t / 1e6}
+
+    # the oracle's whole GEMV over one decoder layer's seven matrices, all cores
+    mats = []
     nbytes = 0
-    dt = 0.0
-    layers = 0
-    while dt < 10.0 and layers < synth.QWEN25_3B_LAYERS:  # about 10 s of host work
-        for j, (name, n, k) in enumerate(synth.QWEN25_3B_LAYER):
-            q, s, b = synth.w4_weights(n, k, seed=0, workload=synth.W_DECODE, layer=layers * 16 + j)
-            x = synth.activations(1, k, seed=0, workload=synth.W_DECODE, layer=layers * 16 + 8 + j)
-            qw = oracle.pack(q)
-            t0 = time.perf_counter()
-            oracle.gemv_ref(qw, s, b, x)
-            dt += time.perf_counter() - t0
-            nbytes += gemv_bytes(1, n, k)
-        layers += 1
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"oracle.gemv_ref over the 7 int4 matrices of {layers} decoder layer(s) at M=1 "
-                      f"({nbytes / 1e6:.1f} MB of algorithmic bytes, {dt:.1f} s; NumPy fp64, BLAS threads={threads})",
-            "seconds": dt}
+    for j, (name, n_, k_) in enumerate(synth.QWEN25_3B_LAYER):
+        q_, s_, b_ = synth.w4_weights(n_, k_, seed=0, workload=synth.W_DECODE, layer=j)
+        x_ = synth.activations(1, k_, seed=0, workload=synth.W_DECODE, layer=8 + j)
+        mats.append((oracle.pack(q_), s_, b_, x_))
+        nbytes += gemv_bytes(1, n_, k_)
+    with threadpool_limits(limits=all_threads, user_api="blas"):
+        t, ts = _median_of(np, lambda: [oracle.gemv_ref(*m_) for m_ in mats])
+    total = time.perf_counter() - t_start
+    return {"value": nbytes / t / 1e9, "unit": "GB/s", "cores": all_threads, "kind": "oracle",
+            "sample": f"oracle.gemv_ref over the 7 int4 matrices of one Qwen2.5-3B decoder layer at M=1 "
+                      f"({nbytes / 1e6:.1f} MB of algorithmic bytes), median of 5 after 1 warm-up, NumPy fp64 "
+                      f"with BLAS on {all_threads} thread(s); stages (a)-(c) beside it",
+            "median_s": t, "samples_s": ts, "stages": stages, "host": meta, "seconds": total}
 
 
 def vendor_gemm(torch, wl, kt, reps=20):
@@ -937,6 +1166,9 @@ def main():
     args = parse_args()
     if args.traffic_from:
         traffic_from(*args.traffic_from)
+        return
+    if args.trace_from:
+        trace_from(*args.trace_from)
         return
     if args.util_from:
         util_from(*args.util_from)
@@ -1015,6 +1247,31 @@ def main():
                "decode_step_gbps": round((wl.gemv_bytes + wl.head_bytes) / (dg + dh) / 1e3, 1)}
         log(f"decode-only loop: gemv {dg:.1f} us ({dec['gemv_gbps']} GB/s), head+top-k {dh:.1f} us")
 
+    # The same step launched kernel by kernel on the stream (each launch from Python through the
+    # C ABI, no graph), timed the same way: the per-launch host cost is what graphs remove.
+    eager = None
+    if not args.eager:
+        for f in phases:
+            f()
+        torch.cuda.synchronize()
+        eve = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        te0 = time.perf_counter()
+        for i in range(args.steps):
+            eve[i][0].record(stream)
+            for j, f in enumerate(phases):
+                f()
+                eve[i][j + 1].record(stream)
+        torch.cuda.synchronize()
+        ewall = time.perf_counter() - te0
+        eph = [sum(eve[i][j].elapsed_time(eve[i][j + 1]) for i in range(args.steps)) / args.steps * 1e3
+               for j in range(3)]
+        eager = {"launch": "stream (eager, one ctypes call per kernel)", "ms_per_step": round(ewall / args.steps * 1e3, 4),
+                 "gemv_us": round(eph[0], 1), "head_topk_us": round(eph[1], 1), "prefill_us": round(eph[2], 1),
+                 "gemv_gbps": round(wl.gemv_bytes / eph[0] / 1e3, 1),
+                 "prefill_tflops": round(wl.prefill_flops / eph[2] / 1e6, 1)}
+        log(f"stream-launched step: {eager['ms_per_step']} ms per step; gemv {eph[0]:.1f} us "
+            f"({eager['gemv_gbps']} GB/s), head+top-k {eph[1]:.1f} us, prefill {eph[2]:.1f} us")
+
     check = None
     if not args.no_check:
         import oracle
@@ -1035,6 +1292,12 @@ def main():
                 "achieved": d["gbps"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": d["gbps"] / HBM_PEAK_GBS,
                 "traffic": traffic_for("gemv.hip", f"w4_gemv_{dom[1]}_{dom[2]}_{dom[3]}"),
                 "bytes_per_launch": d["bytes"], "avg_launch_us": d["avg_us"], "launches_timed": d["launches"]}
+    tr = trace_for("/".join(map(str, dom)))
+    if tr is not None:  # the committed rocprof trace of this kernel shape, beside the live figure
+        roofline["rocprof"] = {"mean_us": round(tr["mean_us"], 3), "median_us": round(tr["median_us"], 3),
+                               "frac_from_mean": d["bytes"] / tr["mean_us"] / 1e3 / HBM_PEAK_GBS,
+                               "live_over_rocprof_mean": round(tr["mean_us"] / d["avg_us"], 3),
+                               "source": "profiles/kernel_trace.json"}
     gk = [v for k_, v in kt.items() if k_[0] == "gemm_f16" and k_[1] == synth.PREFILL_TOKENS]
     g_us = sum(v["avg_us"] for v in gk)
     g_fl = sum(v["flops"] for v in gk)
@@ -1078,7 +1341,8 @@ def main():
         import oracle
         log("timing the CPU oracle on a bounded sample ...")
         cpu = cpu_baseline(np, oracle, synth)
-        log(f"cpu baseline {cpu['value']:.4f} GB/s in {cpu['seconds']:.1f}s")
+        log(f"cpu baseline {cpu['value']:.4f} GB/s ({cpu['cores']} BLAS threads) in {cpu['seconds']:.1f}s; "
+            + "; ".join(f"{k_} {v_['median_s'] * 1e3:.1f} ms" for k_, v_ in cpu["stages"].items()))
 
     gemv_gbps = wl.gemv_bytes * args.steps / ph[0] / 1e9
     prefill_tflops = wl.prefill_flops * args.steps / ph[2] / 1e12
@@ -1112,6 +1376,7 @@ def main():
                               "prefill": ph[2] / args.steps * 1e6},
         "decode_step_gbps": decode_bytes * args.steps / (ph[0] + ph[1]) / 1e9,
         "decode_only_loop": dec,
+        "stream_launched_step": eager,
         "stats": stats,
         "context": ctx,
         "roofline": roofline,
@@ -1119,6 +1384,10 @@ def main():
         "kernels": {"/".join(map(str, k)): {kk: round(vv, 3) if isinstance(vv, float) else vv for kk, vv in v.items()}
                     for k, v in kt.items()},
         "cpu_baseline": cpu,
+        "inputs_sha256": dict(wl.sha, method="SHA-256 of each host buffer's bytes as drawn (uint8 codes before "
+                                              "packing, f16 scales/biases/activations/head); each decode layer is one "
+                                              "SHA-256 over the hex digests of its buffers in launch order"),
+        "host": (cpu or {}).get("host") or host_metadata(np),
         "parity": check,
         "small_m": sm,
         "quantize": qz,
