@@ -779,41 +779,63 @@ def small_m(torch, np, w4, synth, oracle, reps=5):
     return out
 
 
-def int4_head(torch, np, w4, synth, oracle, wl, reps=20):
+def int4_head(torch, np, w4, synth, oracle, wl, reps=10):
     """The LM head stored in the int4 format (group-64 affine, [vocab][hidden] = 151936 x 2048,
-    the pages' 622 MB f16 head at 175 MB) at M = 1: w4_gemv to f32 logits, then the top-40
-    selection, as one graph.  Parity: 64 sampled logits against the fp64 oracle, and the
-    selection bit-exact on the GPU's own logits."""
+    the pages' 622 MB f16 head at 175 MB) at M = 1 with top-40: fused (w4_gemv_topk, the
+    selection in the GEMV's epilogue plus one final launch) and unfused (w4_gemv to f32 logits,
+    then logits_argmax_topk), each graph-timed over distinct copies of the head that together
+    hold at least 1 GiB.  Parity: 64 sampled logits against the fp64 oracle, the selection
+    bit-exact on the GPU's own logits, and the two paths' indices and values equal."""
     V, K = wl.V, wl.H
     q, s, b = synth.w4_weights(V, K, seed=0, workload=synth.W_DECODE, layer=990)
     qw = w4.w4_pack(torch.from_numpy(q).cuda())
     sd, bd = torch.from_numpy(s).cuda(), torch.from_numpy(b).cuda()
+    nb = gemv_bytes(1, V, K) + 4 * V
+    copies = -(-ROTATE_BYTES // nb)
+    heads = [(qw, sd, bd)] + [(qw.clone(), sd.clone(), bd.clone()) for _ in range(copies - 1)]
     logits = torch.empty((1, V), dtype=torch.float32, device="cuda")
     idx = torch.empty((1, TOPK), dtype=torch.int32, device="cuda")
     val = torch.empty((1, TOPK), dtype=torch.float32, device="cuda")
+    flog = torch.empty(V, dtype=torch.float32, device="cuda")
+    fidx = torch.empty(TOPK, dtype=torch.int32, device="cuda")
+    fval = torch.empty(TOPK, dtype=torch.float32, device="cuda")
+    fws = torch.empty(w4.gemv_topk_workspace_bytes(V, K, TOPK), dtype=torch.uint8, device="cuda")
 
-    def step():
-        w4.w4_gemv(qw, sd, bd, wl.x_head, out=logits)
-        w4.logits_argmax_topk(logits, TOPK, idx=idx, val=val, workspace=wl.topk_ws)
-    graph = capture(torch, step)
-    graph.replay()
+    def unfused():
+        for h in heads:
+            w4.w4_gemv(*h, wl.x_head, out=logits)
+            w4.logits_argmax_topk(logits, TOPK, idx=idx, val=val, workspace=wl.topk_ws)
+
+    def fused():
+        for h in heads:
+            w4.w4_gemv_topk(*h, wl.x_head, TOPK, logits=flog, idx=fidx, val=fval, workspace=fws)
+
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
+    res = {}
+    for name, fn in (("unfused", unfused), ("fused", fused)):
+        graph = capture(torch, fn)
         graph.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / reps
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) * 1e3 / (reps * copies)
     lg = logits.cpu().numpy()
     rows = np.sort(np.random.default_rng(11).choice(V, 64, replace=False))
     y_ref, bound = oracle.gemv_ref(oracle.pack(q[rows]), s[rows], b[rows], wl.x_head_host)
     ok = oracle.check_bound(lg[:, rows], y_ref, bound)[0]
     ok &= oracle.check_topk_selection(lg, idx.cpu().numpy(), val.cpu().numpy(), TOPK)
-    nb = gemv_bytes(1, V, K) + 4 * V
+    fl = flog.cpu().numpy()[None]
+    ok &= oracle.check_bound(fl[:, rows], y_ref, bound)[0]
+    ok &= oracle.check_topk_selection(fl, fidx.cpu().numpy()[None], fval.cpu().numpy()[None], TOPK)
+    ok &= bool(np.array_equal(fidx.cpu().numpy(), idx.cpu().numpy()[0]))
+    us = res["fused"]
     return {"workload": f"int4 LM head [{V}][{K}] (affine group 64) at M=1 + top-{TOPK}", "us": round(us, 3),
             "gbps": round(nb / us / 1e3, 1), "frac_hbm": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
-            "head_bytes": gemv_bytes(1, V, K), "parity_ok": bool(ok)}
+            "launch": "w4_gemv_topk (fused)", "unfused_us": round(res["unfused"], 3),
+            "head_bytes": gemv_bytes(1, V, K), "copies": copies, "parity_ok": bool(ok)}
 
 
 def single_gemv(torch, np, w4, synth, oracle, copies=512, reps=5):
@@ -1326,7 +1348,8 @@ def main():
         log(f"single GEMV: lone launch {sg['lone_launch_us_median']} us, steady state {sg['steady_state_us']} us "
             f"({sg['steady_state_gbps']} GB/s)")
         log("heads: " + "; ".join(f"{k_} {v_['us']} us" for k_, v_ in hs.items()))
-        log(f"int4 head + top-{TOPK}: {ih['us']} us ({ih['gbps']} GB/s), parity {'ok' if ih['parity_ok'] else 'FAILED'}")
+        log(f"int4 head + top-{TOPK}: fused {ih['us']} us ({ih['gbps']} GB/s), unfused {ih['unfused_us']} us, "
+            f"parity {'ok' if ih['parity_ok'] else 'FAILED'}")
         log(f"speculative verify: {sv['us']} us, parity {'ok' if sv['parity_ok'] else 'FAILED'}")
         qz = quantize_bench(torch, np, w4, synth, oracle)
         log(f"quantizer: {qz['avg_us']} us, {qz['gbps']} GB/s, parity {'ok' if qz['parity_ok'] else 'FAILED'}")

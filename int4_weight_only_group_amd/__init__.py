@@ -19,7 +19,7 @@ from ._lib import lib, LIB_PATH  # noqa: F401
 
 __all__ = [
     "W4Error", "w4_pack", "w4_quantize", "w4_gemv", "w4_gemv_sym128", "w4_dequant_f16_t_sym128", "w4_dequant_f16_t", "gemm_f16", "logits_argmax_topk",
-    "logits_argmax_topk_noalloc",
+    "logits_argmax_topk_noalloc", "w4_gemv_topk", "gemv_topk_workspace_bytes",
     "topk_workspace_bytes", "gemm_workspace_bytes", "status_string",
 ]
 
@@ -310,3 +310,43 @@ def logits_argmax_topk_noalloc(logits: torch.Tensor, k: int, idx: torch.Tensor |
     _check("logits_argmax_topk_noalloc", lib().logits_argmax_topk_noalloc(
         logits.data_ptr(), ldl, m, v, k, idx.data_ptr(), val.data_ptr(), _stream()))
     return idx, val
+
+
+def gemv_topk_workspace_bytes(v: int, k_dim: int, k: int) -> int:
+    """Workspace bytes w4_gemv_topk needs for a [v][k_dim] head and top-k."""
+    n = ctypes.c_size_t(0)
+    p = ctypes.c_void_p(16)
+    _check("w4_gemv_topk", lib().w4_gemv_topk(p, p, p, p, v, k_dim, k, p, p, p, None, ctypes.byref(n), None))
+    return int(n.value)
+
+
+def w4_gemv_topk(qw: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, x: torch.Tensor, k: int,
+                 logits: torch.Tensor | None = None, idx: torch.Tensor | None = None,
+                 val: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """The int4 LM head with fused top-k: x float16 [K] (or [1][K]) -> (logits float32 [V],
+    idx int32 [k], val float32 [k]), the k largest logits, value descending, ties to the lower
+    index.  One is allocated for each of the outputs and the workspace not given."""
+    v, kdim = _w4_args(qw, scales, biases)
+    _dev(x, "x", torch.float16)
+    _contig(x, "x")
+    if x.numel() != kdim or (x.dim() == 2 and x.shape[0] != 1):
+        raise ValueError("x must be [K] or [1][K]")
+    outs = []
+    for t, name, shape, dt in ((logits, "logits", (v,), torch.float32), (idx, "idx", (k,), torch.int32),
+                               (val, "val", (k,), torch.float32)):
+        if t is None:
+            t = torch.empty(shape, dtype=dt, device=x.device)
+        _dev(t, name, dt)
+        _contig(t, name)
+        if t.numel() != shape[0]:
+            raise ValueError(f"{name} must hold {shape[0]} elements")
+        outs.append(t)
+    logits, idx, val = outs
+    need = gemv_topk_workspace_bytes(v, kdim, k)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    cap = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    _check("w4_gemv_topk", lib().w4_gemv_topk(qw.data_ptr(), scales.data_ptr(), biases.data_ptr(), x.data_ptr(),
+                                              v, kdim, k, logits.data_ptr(), idx.data_ptr(), val.data_ptr(),
+                                              workspace.data_ptr(), ctypes.byref(cap), _stream()))
+    return logits, idx, val

@@ -219,6 +219,27 @@ int logits_argmax_topk(const float* logits, int64_t ldl, int64_t M, int64_t V, i
   }
 }
 
+int w4_gemv_topk(const uint32_t* qw, const uint16_t* scales, const uint16_t* biases, const uint16_t* x,
+                 int64_t V, int64_t K, int64_t k, float* logits, int32_t* idx, float* val, void* ws,
+                 size_t* ws_bytes, w4_stream_t stream) {
+  try {
+    if (!qw || !scales || !biases || !x || !logits || !idx || !val) return W4_ERR_NULL;
+    if (int e = check_w4_shape(V, K)) return e;
+    if (k < 1 || k > 64 || !w4::head_topk_supported(V, K, (int)k)) return W4_ERR_SHAPE;
+    if (!al16(qw) || !al16(scales) || !al16(biases) || !al16(x) || !al4(logits) || !al4(idx) || !al4(val))
+      return W4_ERR_ALIGN;
+    const int w = workspace(ws, ws_bytes, w4::head_topk_ws_bytes(V, K, (int)k));
+    if (w < 0) return w;
+    if (w == 1) return W4_OK;
+    if (int e = check_device()) return e;
+    (void)hipGetLastError();
+    w4::launch_head_topk(qw, scales, biases, x, logits, idx, val, (int)V, (int)K, (int)k, ws, (hipStream_t)stream);
+    return launched();
+  } catch (...) {
+    return W4_ERR_INTERNAL;
+  }
+}
+
 int logits_argmax_topk_noalloc(const float* logits, int64_t ldl, int64_t M, int64_t V, int64_t k,
                                int32_t* idx, float* val, w4_stream_t stream) {
   try {

@@ -29,7 +29,9 @@
 // Every term's error is thus relative to |w x|, which keeps each output within
 // 2e-3 * sum_k |w x| (and exactly 0 when every w x is 0).  Rows reduce across lanes with DPP
 // moves; one lane stores y.
+#include "w4_dequant.h"
 #include "w4_internal.h"
+#include "w4_select.h"
 
 namespace w4 {
 
@@ -37,26 +39,6 @@ namespace {
 
 constexpr int kWG = 256;
 constexpr int kLdsBudget = 64 * 1024;
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(hf16x2, a), __builtin_bit_cast(hf16x2, b), c,
-                                false);
-}
-
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
-__device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
-
-// Weight formats: the affine group-64 format (w = s q + b) and the symmetric group-128 one
-// (w = s (q - 8), no bias).  For the latter the OR trick's offsets grow by 8, so the exact
-// f16 it yields is q - 8, and the FMA's addend is +0 (w = RN(s (q - 8)), an exact zero +0).
-template <bool SYM>
-struct Fmt {
-  static constexpr int kGroupSize = SYM ? 128 : 64;
-  static constexpr int kChunkShift = SYM ? 2 : 1;  // 16-byte chunk index -> group index
-  static constexpr float kLo = SYM ? 1032.0f : 1024.0f, kHi = SYM ? 72.0f : 64.0f;
-};
 
 // The 8 weights of word w as f16 pairs matching the x pair order (see file comment).
 template <bool SYM>
@@ -91,50 +73,6 @@ __device__ __forceinline__ uint4 pair_up(uint4 d) {
   p.z = (d.y & 0xFFFFu) | (d.w << 16);
   p.w = (d.y >> 16) | (d.w & 0xFFFF0000u);
   return p;
-}
-
-// Codes of word w as exact f16 pairs through the fp8 converter: in the e4m3 encoding a byte
-// holding 0..15 is the number q * 2^-9 exactly (the subnormals and the first normal binade are
-// one evenly spaced range), so converting with the scale 2^9 yields q.  The low nibbles
-// (w & 0x0F0F0F0F) and high nibbles ((w >> 4) & 0x0F0F0F0F) give the pairs (q0,q2) (q4,q6)
-// and (q1,q3) (q5,q7): 7 instructions for 8 codes (the OR trick takes 9).  The symmetric
-// format subtracts 8 (exact).
-template <bool SYM>
-__device__ __forceinline__ void cvt_codes(uint32_t w, h2& q0, h2& q1, h2& q2, h2& q3) {
-  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-  q0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, false);  // (q0, q2)
-  q1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, true);   // (q4, q6)
-  q2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, false);  // (q1, q3)
-  q3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, true);   // (q5, q7)
-  if constexpr (SYM) {
-    const h2 o8 = {(f16)8.0f, (f16)8.0f};
-    q0 -= o8;
-    q1 -= o8;
-    q2 -= o8;
-    q3 -= o8;
-  }
-}
-
-// (x0x1, x2x3, x4x5, x6x7) -> (x0x2, x4x6, x1x3, x5x7): the converter's code order
-__device__ __forceinline__ uint4 pair_up_cvt(uint4 d) {
-  uint4 p;
-  p.x = __builtin_amdgcn_perm(d.y, d.x, 0x05040100u);
-  p.y = __builtin_amdgcn_perm(d.w, d.z, 0x05040100u);
-  p.z = __builtin_amdgcn_perm(d.y, d.x, 0x07060302u);
-  p.w = __builtin_amdgcn_perm(d.w, d.z, 0x07060302u);
-  return p;
-}
-
-// One word's 8 weights (one FMA rounding each) dotted with x pairs in the converter's order.
-template <bool SYM>
-__device__ __forceinline__ float word_fma_cvt(uint32_t w, h2 s2, h2 b2, const uint4& xp, float acc) {
-  h2 q0, q1, q2, q3;
-  cvt_codes<SYM>(w, q0, q1, q2, q3);
-  acc = dot2(as_u32(__builtin_elementwise_fma(q0, s2, b2)), xp.x, acc);
-  acc = dot2(as_u32(__builtin_elementwise_fma(q1, s2, b2)), xp.y, acc);
-  acc = dot2(as_u32(__builtin_elementwise_fma(q2, s2, b2)), xp.z, acc);
-  acc = dot2(as_u32(__builtin_elementwise_fma(q3, s2, b2)), xp.w, acc);
-  return acc;
 }
 
 template <int MT, int R, int P, bool SYM>
@@ -694,20 +632,26 @@ void launch_mf(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const u
 //    word with the FMA and the dot products.  The symmetric format subtracts 8 (exact) before
 //    its FMA, so both formats pair and sum their products in the same order and give the same
 //    bits where their weights agree (b = -8 s).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* p) {
-  // raw buffer (stride 0) over the 31-bit offset range from p; offsets stay far below it
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, 0x7FFFFFFF, 0x00020000);
-}
-
 // BIG: 2 GB of codes or more -- the buffers then start at each wave's own rows (64-bit base,
 // offsets below R rows); otherwise one buffer per array and the row offset in the scalar
 // register (measured 1-2 % faster).
-template <int R, int KS, bool SYM, bool BIG, int MT>
+// MAXK (M = 1 only): each workgroup also writes the largest selection key (w4_select.h) of its
+// rows to wgmax[blockIdx.x] -- 4 R rows with KS = 1, R rows otherwise -- the first step of the
+// int4 LM head's fused token selection.
+template <int R, int KS, bool SYM, bool BIG, int MT, bool MAXK = false>
 __global__ __launch_bounds__(KS == 1 ? kWG : KS * 64) void gemv1s_kernel(
     const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc, const uint16_t* __restrict__ bi,
     const uint16_t* __restrict__ x, int64_t ldx, float* __restrict__ y, int64_t ldy, int N, int K,
-    int nblocks, uint32_t qblk, uint32_t sblk) {  // bytes of codes / of scales per block of R rows
+    int nblocks, uint32_t qblk, uint32_t sblk,  // bytes of codes / of scales per block of R rows
+    uint64_t* __restrict__ wgmax = nullptr) {
+  static_assert(!MAXK || MT == 1, "workgroup maxima for one activation row");
   __shared__ float red[KS][R * MT];
+  __shared__ uint64_t wmax[kWG / 64];
+  __shared__ int nwaves_done;
+  if constexpr (MAXK && KS == 1) {  // the last wave to finish writes the workgroup's maximum
+    if (threadIdx.x == 0) nwaves_done = 0;
+    __syncthreads();  // at the start, where every wave is anyway
+  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int slice = KS == 1 ? 0 : wave;
@@ -742,7 +686,7 @@ __global__ __launch_bounds__(KS == 1 ? kWG : KS * 64) void gemv1s_kernel(
     bv[r] = SYM ? 0u : __builtin_amdgcn_raw_buffer_load_b16(rb, voff_s, dn * G * 2, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
-  if (KS == 1 && blk >= nblocks) return;
+  if (!MAXK && KS == 1 && blk >= nblocks) return;  // with MAXK every wave meets the barrier below
 
   uint4 xp[MT][4];
 #pragma unroll
@@ -791,11 +735,28 @@ __global__ __launch_bounds__(KS == 1 ? kWG : KS * 64) void gemv1s_kernel(
   }
   if constexpr (KS == 1) {
     if (lane == 63) {
+      uint64_t km = 0;  // below every real key
 #pragma unroll
-      for (int r = 0; r < R; ++r)
+      for (int r = 0; r < R; ++r) {
+        const bool ok = blk < nblocks && blk * R + r < N;
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-          if (blk * R + r < N) y[m * ldy + blk * R + r] = acc[r][m];
+          if (ok) y[m * ldy + blk * R + r] = acc[r][m];
+        if constexpr (MAXK) {
+          const uint64_t kr = ok ? make_key(acc[r][0], (uint32_t)(blk * R + r)) : 0ull;
+          km = kr > km ? kr : km;
+        }
+      }
+      if constexpr (MAXK) {
+        wmax[wave] = km;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        if (atomicAdd(&nwaves_done, 1) == kWG / 64 - 1) {  // the other waves' maxima are in LDS
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+          for (int w = 0; w < kWG / 64; ++w) km = wmax[w] > km ? wmax[w] : km;
+          wgmax[blockIdx.x] = km;
+        }
+      }
     }
   } else {
     if (lane == 63) {
@@ -805,11 +766,22 @@ __global__ __launch_bounds__(KS == 1 ? kWG : KS * 64) void gemv1s_kernel(
         for (int m = 0; m < MT; ++m) red[slice][r * MT + m] = acc[r][m];
     }
     __syncthreads();
-    if (wave == 0 && lane < R * MT && blk * R + lane / MT < N) {
-      float v = red[0][lane];
+    if (wave == 0) {
+      const bool ok = lane < R * MT && blk * R + lane / MT < N;
+      float v = red[0][min(lane, R * MT - 1)];
 #pragma unroll
-      for (int j = 1; j < KS; ++j) v += red[j][lane];
-      y[(lane % MT) * ldy + blk * R + lane / MT] = v;
+      for (int j = 1; j < KS; ++j) v += red[j][min(lane, R * MT - 1)];
+      if (ok) y[(lane % MT) * ldy + blk * R + lane / MT] = v;
+      if constexpr (MAXK) {
+        const uint64_t kr = ok ? make_key(v, (uint32_t)(blk * R + lane)) : 0ull;
+        uint64_t km = kr;
+#pragma unroll
+        for (int r = 1; r < R; ++r) {
+          const uint64_t o = readlane64(kr, r);
+          km = o > km ? o : km;
+        }
+        if (lane == 0) wgmax[blockIdx.x] = km;
+      }
     }
   }
 }
@@ -907,6 +879,22 @@ bool launch_gemv_rs(int M, const uint32_t* qw, const uint16_t* s, const uint16_t
   return true;
 }
 
+template <int R, int KS>
+void launch_rs_max(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x, float* y, int N,
+                   int K, uint64_t* wgmax, hipStream_t st) {
+  const int nblocks = (N + R - 1) / R;
+  const int grid = KS == 1 ? (nblocks + kWG / 64 - 1) / (kWG / 64) : nblocks;
+  const uint32_t qblk = (uint32_t)R * (uint32_t)(K / 2);
+  const uint32_t sblk = (uint32_t)R * (uint32_t)(K / 64) * 2;
+  const dim3 block(KS == 1 ? kWG : KS * 64);
+  if ((int64_t)N * (K / 2) >= ((int64_t)1 << 31))
+    hipLaunchKernelGGL((gemv1s_kernel<R, KS, false, true, 1, true>), dim3(grid), block, 0, st, qw, s, b, x, (int64_t)K,
+                       y, (int64_t)N, N, K, nblocks, qblk, sblk, wgmax);
+  else
+    hipLaunchKernelGGL((gemv1s_kernel<R, KS, false, false, 1, true>), dim3(grid), block, 0, st, qw, s, b, x, (int64_t)K,
+                       y, (int64_t)N, N, K, nblocks, qblk, sblk, wgmax);
+}
+
 // M = 1: rows of more than 32 chunks (K > 1024) and up to 8 slices (K <= 16384) on row
 // slices; shorter rows on 32-lane teams of the OR-trick kernel (one chunk per lane, x in
 // LDS); longer rows fall through to the general kernel.
@@ -959,6 +947,35 @@ void launch_gemv_fmt(const uint32_t* qw, const uint16_t* s, const uint16_t* b, c
 void launch_gemv(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
                  int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
   launch_gemv_fmt<false>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+}
+
+// The M = 1 row-slice GEMV's rows per block and slices per row (the policy of launch_gemv_rs),
+// as used for the int4 LM head: R = 4 once there are 30000 (row, slice) units, else 3 or 2.
+HeadGemvPlan head_gemv_plan(int64_t N, int64_t K) {
+  HeadGemvPlan p;
+  const int C = (int)(K / 32);
+  p.KS = (C + 63) / 64;
+  const int64_t units = N * p.KS;
+  constexpr int kSimds = 256 * 4;
+  const bool fits3 = p.KS == 1 && N > 2 * kSimds && N <= 3 * kSimds;
+  p.R = units >= 30000 ? 4 : ((units >= 16000 && p.KS == 1) || fits3) ? 3 : 2;
+  if (p.KS > 1) p.R = p.R == 3 ? 2 : p.R;  // row slices of several waves come in 2 or 4 rows
+  p.rows_per_wg = p.KS == 1 ? p.R * (kWG / 64) : p.R;
+  p.nwg = (int)((N + p.rows_per_wg - 1) / p.rows_per_wg);
+  return p;
+}
+
+void launch_gemv_head(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x, float* y, int N,
+                      int K, uint64_t* wgmax, hipStream_t st) {
+  const HeadGemvPlan p = head_gemv_plan(N, K);
+  if (p.KS == 1) {
+    if (p.R == 4) launch_rs_max<4, 1>(qw, s, b, x, y, N, K, wgmax, st);
+    else if (p.R == 3) launch_rs_max<3, 1>(qw, s, b, x, y, N, K, wgmax, st);
+    else launch_rs_max<2, 1>(qw, s, b, x, y, N, K, wgmax, st);
+  } else {  // K <= 4096 for the head: two slices
+    if (p.R == 4) launch_rs_max<4, 2>(qw, s, b, x, y, N, K, wgmax, st);
+    else launch_rs_max<2, 2>(qw, s, b, x, y, N, K, wgmax, st);
+  }
 }
 
 void launch_gemv_sym128(const uint32_t* qw, const uint16_t* s, const uint16_t* x, int64_t ldx,

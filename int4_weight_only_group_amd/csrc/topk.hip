@@ -32,6 +32,7 @@
 #include <mutex>
 
 #include "w4_internal.h"
+#include "w4_select.h"
 
 namespace w4 {
 
@@ -39,15 +40,6 @@ namespace {
 
 constexpr int kWG = 256;
 constexpr int kMaxCand = 8192;  // keys per row after pass 1
-
-__device__ __forceinline__ uint64_t make_key(float v, uint32_t i) {
-  uint32_t u = __float_as_uint(v);
-  if (u == 0x80000000u) u = 0u;                      // -0.0 == +0.0
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);   // monotone in the value
-  return ((uint64_t)u << 32) | (uint64_t)(~i);
-}
-
-__device__ __forceinline__ uint32_t key_index(uint64_t key) { return ~(uint32_t)key; }
 
 // Descending bitonic sort of n (a power of two, >= 2) keys in LDS by the whole workgroup.
 __device__ void sort_desc(uint64_t* s, int n) {
@@ -172,168 +164,6 @@ __global__ __launch_bounds__(kWG) void topk_final_kernel(const float* __restrict
 
 // ------------------------------------------------------------------ wave selection (k <= 64)
 
-// Padding key for position p past the data: high word 0 (every real key's high word is at
-// least 0x00800000 for finite logits), low word unique per position.
-__device__ __forceinline__ uint64_t pad_key(uint32_t p) { return (uint64_t)p; }
-
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-__device__ __forceinline__ uint64_t readlane64(uint64_t v, int src) {
-  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, src);
-  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// 16 keys from 128-byte-aligned LDS with eight 16-byte reads issued back to back.
-typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void load16(const uint64_t* src, uint64_t (&v)[16]) {
-  u64x2 p[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) p[q] = reinterpret_cast<const u64x2*>(src)[q];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    v[2 * q] = p[q][0];
-    v[2 * q + 1] = p[q][1];
-  }
-}
-
-// Number of keys greater than x in a descending list of n <= 64 distinct keys (branchless
-// binary search, seven probes).
-__device__ __forceinline__ int count_greater(const uint64_t* list, int n, uint64_t x) {
-  int lo = 0;
-#pragma unroll
-  for (int step = 64; step >= 1; step >>= 1) {
-    const int probe = min(lo + step, n) - 1;
-    if (lo + step <= n && list[probe] > x) lo += step;
-  }
-  return lo;
-}
-
-// The k largest of this wave's 64 * E distinct keys, sorted descending, into out[0..k).
-// wm: 128 keys of LDS, cand: 64 * E keys of LDS (both private to the wave).
-// Threshold: every lane offers its largest key, or with TWO (k > 48, E > 1) its two largest; the
-// one of the offered keys with exactly k - 1 larger ones among them is T, and at least k
-// keys reach it.  With one key per lane and k near 64, T is about the smallest lane maximum
-// and most keys pass (the rank scan below then goes quadratic); two keys per lane keep the
-// candidates near k.  For smaller k one key per lane already does and costs less.
-template <int E, bool TWO>
-__device__ void wave_topk(const uint64_t (&key)[E], int k, uint64_t* wm, uint64_t* cand,
-                          uint64_t* out) {
-  const int lane = threadIdx.x & 63;
-  constexpr bool two = E > 1 && TWO;
-  uint64_t m1 = key[0], m2 = 0;
-  if constexpr (two) {
-#pragma unroll
-    for (int e = 1; e < E; ++e) {
-      const uint64_t hi = key[e] > m1 ? key[e] : m1, lo = key[e] > m1 ? m1 : key[e];
-      m1 = hi;
-      m2 = lo > m2 ? lo : m2;
-    }
-    wm[64 + lane] = m2;
-  } else {
-#pragma unroll
-    for (int e = 1; e < E; ++e) m1 = key[e] > m1 ? key[e] : m1;
-  }
-  wm[lane] = m1;
-  wave_sync();
-  int r1 = 0, r2 = 0;  // LDS reads in batches of 8 x 16 bytes so their latencies overlap
-#pragma unroll
-  for (int bt = 0; bt < 4; ++bt) {  // the 64 lane maxima
-    uint64_t v[16];
-    load16(wm + bt * 16, v);
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      r1 += v[q] > m1 ? 1 : 0;
-      if constexpr (two) r2 += v[q] > m2 ? 1 : 0;
-    }
-  }
-  if constexpr (two) {
-#pragma unroll
-    for (int bt = 4; bt < 8; ++bt) {  // the 64 second keys
-      uint64_t v[16];
-      load16(wm + bt * 16, v);
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        r1 += v[q] > m1 ? 1 : 0;
-        r2 += v[q] > m2 ? 1 : 0;
-      }
-    }
-  }
-  // exactly one offered key has rank k - 1: offered keys are distinct
-  const bool mine = r1 == k - 1 || (two && r2 == k - 1);
-  const uint64_t who = __ballot(mine);
-  const uint64_t T = readlane64(r1 == k - 1 ? m1 : m2, (int)__builtin_ctzll(who));
-  int c = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const bool take = key[e] >= T;
-    const uint64_t bits = __ballot(take);
-    const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(bits >> 32),
-                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)bits, 0));
-    // lanes that drop their key write it to their own dead slot of wm (read before T was
-    // chosen), so the write needs no branch
-    *(take ? cand + c + before : wm + lane) = key[e];
-    c += __builtin_popcountll(bits);
-  }
-  // pad the candidates to a multiple of 16 with 0, below every real or padding key (c <= 64E,
-  // a multiple of 16), so the rank scan reads 16 at a time with its LDS reads overlapped
-  const int c16 = (c + 15) & ~15;
-  if (lane < c16 - c) cand[c + lane] = 0ull;
-  wave_sync();
-  for (int i = lane; i < c; i += 64) {
-    const uint64_t ki = cand[i];
-    int r = 0;
-    for (int j = 0; j < c16; j += 16) {
-      uint64_t v[16];
-      load16(cand + j, v);
-#pragma unroll
-      for (int q = 0; q < 16; ++q) r += v[q] > ki ? 1 : 0;
-    }
-    if (r < k) out[r] = ki;
-  }
-  wave_sync();
-}
-
-// A workgroup of four waves: the k best of 4 * 64 * E keys (key[e] of lane l of wave w is
-// element w * 64 * E + e * 64 + l of the group's range) into out[0..k) (LDS, read after the
-// final barrier).  Each wave selects its sorted k best; the four sorted lists are then
-// merged by rank: survivor i of list w is preceded by the i before it in its own list and by
-// the survivors of the other three lists that are larger (binary search), and lands at that
-// rank if it is below k.
-constexpr int kGrpWm = 0, kGrpSurv = 512, kGrpCand = 768;  // key offsets in a group's LDS
-
-template <int E, bool TWO>
-__device__ void group_topk(const uint64_t (&key)[E], int k, unsigned char* smem, uint64_t* out) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  uint64_t* wm = reinterpret_cast<uint64_t*>(smem) + kGrpWm + w * 128;            // 4 x 128
-  uint64_t* surv = reinterpret_cast<uint64_t*>(smem) + kGrpSurv;                  // 4 x 64
-  uint64_t* cand = reinterpret_cast<uint64_t*>(smem) + kGrpCand + w * 64 * E;     // 4 x 64E
-  wave_topk<E, TWO>(key, k, wm, cand, surv + w * 64);
-  __syncthreads();
-  if (lane < k) {
-    const uint64_t x = surv[w * 64 + lane];
-    int r = lane;
-#pragma unroll
-    for (int o = 1; o < 4; ++o) r += count_greater(surv + ((w + o) & 3) * 64, k, x);
-    if (r < k) out[r] = x;
-  }
-  __syncthreads();
-}
-
-template <int E>
-constexpr size_t group_lds() {
-  return (size_t)(kGrpCand + 4 * 64 * E + 64) * 8;  // wm, surv, 4 candidate areas, out
-}
-
-template <int E>
-__device__ __forceinline__ uint64_t* group_out(unsigned char* smem) {
-  return reinterpret_cast<uint64_t*>(smem) + kGrpCand + 4 * 64 * E;
-}
-
 // Pass 1: the k best keys of logits[m][c*chunk, (c+1)*chunk) into cand[m][c][0:k),
 // chunk = 4 * 64 * E.
 // TWO: k > 48 (two offered keys per lane in the wave selection, lists stored rotated).
@@ -355,8 +185,8 @@ __global__ __launch_bounds__(kWG) void wtopk_chunk_kernel(const float* __restric
     const int v = base + e * 64;  // coalesced: one 256-byte row segment per e and wave
     key[e] = v < V ? make_key(lv[e], (uint32_t)v) : pad_key(~(uint32_t)v & 0x7fffffffu);
   }
-  uint64_t* out = group_out<E>(smem);
-  group_topk<E, TWO>(key, k, smem, out);
+  uint64_t* out = group_out<4, E>(smem);
+  group_topk<4, E, TWO>(key, k, smem, out);
   // With TWO the list is stored rotated by 17 c: pass 2 reads candidate i into lane i % 64, so sorted
   // lists stored as-is would give lane l the rank-l key of every list (k = 64: lane 63 then
   // holds a high maximum, the threshold admits almost every key and the rank scan goes
@@ -398,8 +228,8 @@ __global__ __launch_bounds__(kWG) void wtopk_final_kernel(const float* __restric
       key[e] = i < ncand ? make_key(lv[e], (uint32_t)i) : pad_key(~(uint32_t)i & 0x7fffffffu);
     }
   }
-  uint64_t* out = group_out<E>(smem);
-  group_topk<E, TWO>(key, k, smem, out);
+  uint64_t* out = group_out<4, E>(smem);
+  group_topk<4, E, TWO>(key, k, smem, out);
   for (int i = threadIdx.x; i < k; i += kWG) {
     uint32_t j = key_index(out[i]);
     if (j >= (uint32_t)V) j = (uint32_t)V - 1;  // unreachable for k <= V; keeps reads in bounds
@@ -412,10 +242,10 @@ template <int E>
 void launch_wfinal(const float* logits, int64_t ldl, int M, int V, int k, const uint64_t* cand,
                    int ncand, int32_t* idx, float* val, hipStream_t st) {
   if (k > 48)
-    hipLaunchKernelGGL((wtopk_final_kernel<E, true>), dim3(M), dim3(kWG), group_lds<E>(), st, logits,
+    hipLaunchKernelGGL((wtopk_final_kernel<E, true>), dim3(M), dim3(kWG), (group_lds<4, E>()), st, logits,
                        ldl, V, k, cand, ncand, idx, val);
   else
-    hipLaunchKernelGGL((wtopk_final_kernel<E, false>), dim3(M), dim3(kWG), group_lds<E>(), st, logits,
+    hipLaunchKernelGGL((wtopk_final_kernel<E, false>), dim3(M), dim3(kWG), (group_lds<4, E>()), st, logits,
                        ldl, V, k, cand, ncand, idx, val);
 }
 
@@ -480,7 +310,7 @@ void launch_topk(const float* logits, int64_t ldl, int M, int V, int k, int32_t*
                           reinterpret_cast<const void*>(wtopk_chunk_kernel<32, true>),
                           reinterpret_cast<const void*>(wtopk_final_kernel<32, false>),
                           reinterpret_cast<const void*>(wtopk_final_kernel<32, true>)})
-      (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)group_lds<32>());
+      (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)group_lds<4, 32>());
   });
   const bool wave = k <= 64;
   if (V <= 4096) {
@@ -496,16 +326,16 @@ void launch_topk(const float* logits, int64_t ldl, int M, int V, int k, int32_t*
   if (wave) {
     const dim3 grid(nchunks, M);
     if (chunk == 4096 && k > 48)
-      hipLaunchKernelGGL((wtopk_chunk_kernel<16, true>), grid, dim3(kWG), group_lds<16>(), st, logits,
+      hipLaunchKernelGGL((wtopk_chunk_kernel<16, true>), grid, dim3(kWG), (group_lds<4, 16>()), st, logits,
                          ldl, V, k, cand);
     else if (chunk == 4096)
-      hipLaunchKernelGGL((wtopk_chunk_kernel<16, false>), grid, dim3(kWG), group_lds<16>(), st, logits,
+      hipLaunchKernelGGL((wtopk_chunk_kernel<16, false>), grid, dim3(kWG), (group_lds<4, 16>()), st, logits,
                          ldl, V, k, cand);
     else if (k > 48)
-      hipLaunchKernelGGL((wtopk_chunk_kernel<32, true>), grid, dim3(kWG), group_lds<32>(), st, logits,
+      hipLaunchKernelGGL((wtopk_chunk_kernel<32, true>), grid, dim3(kWG), (group_lds<4, 32>()), st, logits,
                          ldl, V, k, cand);
     else
-      hipLaunchKernelGGL((wtopk_chunk_kernel<32, false>), grid, dim3(kWG), group_lds<32>(), st, logits,
+      hipLaunchKernelGGL((wtopk_chunk_kernel<32, false>), grid, dim3(kWG), (group_lds<4, 32>()), st, logits,
                          ldl, V, k, cand);
     wfinal_pass(logits, ldl, M, V, k, cand, nchunks * k, idx, val, st);
     return;

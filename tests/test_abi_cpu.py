@@ -150,6 +150,33 @@ def test_topk_argument_errors_and_workspace_query():
     assert t(V=2, k=1, M=16, wsb=ctypes.byref(n2)) == W4_OK and n2.value == 0
 
 
+def test_gemv_topk_argument_errors_and_workspace_query():
+    lib = _lib()
+    g = lambda **kw: lib.w4_gemv_topk(kw.get("qw", P), P, P, kw.get("x", P), kw.get("V", 151936), kw.get("K", 2048),
+                                      kw.get("k", 40), kw.get("lg", P), P, P, kw.get("ws", None), kw.get("wsb", None),
+                                      None)
+    assert g(qw=None) == W4_ERR_NULL
+    assert g(lg=None) == W4_ERR_NULL
+    assert g(k=0) == W4_ERR_SHAPE
+    assert g(k=65) == W4_ERR_SHAPE
+    assert g(V=30, k=40) == W4_ERR_SHAPE
+    assert g(K=96) == W4_ERR_SHAPE
+    assert g(K=4160) == W4_ERR_SHAPE
+    assert g(V=524289, k=64) == W4_ERR_SHAPE     # the re-read groups would exceed 8192 rows
+    assert g(V=524288, k=64, wsb=ctypes.byref(ctypes.c_size_t(0))) == W4_OK
+    assert g(x=P + 8) == W4_ERR_ALIGN
+    assert g(lg=P + 2) == W4_ERR_ALIGN
+    n = ctypes.c_size_t(0)
+    assert g(wsb=ctypes.byref(n)) == W4_OK
+    assert n.value == 9496 * 8  # one key per GEMV workgroup of 16 rows (4 waves x 4 rows)
+    small = ctypes.c_size_t(n.value - 8)
+    assert g(ws=P, wsb=ctypes.byref(small)) == W4_ERR_WORKSPACE
+    n2 = ctypes.c_size_t(0)
+    assert g(V=100, K=64, k=3, wsb=ctypes.byref(n2)) == W4_OK and n2.value == 13 * 8  # 8 rows per workgroup
+    n3 = ctypes.c_size_t(0)
+    assert g(V=262144, K=3840, k=64, wsb=ctypes.byref(n3)) == W4_OK and n3.value == 65536 * 8  # 4 rows each
+
+
 @pytest.mark.skipif(_has_gpu(), reason="checks the no-device error path")
 def test_valid_call_without_device_reports_device_error():
     lib = _lib()
