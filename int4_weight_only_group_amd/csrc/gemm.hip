@@ -24,6 +24,7 @@
 //    per (column, 16 rows), threads split K.
 #include <cmath>
 #include <mutex>
+#include <type_traits>
 
 #include "w4_internal.h"
 
@@ -203,7 +204,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs g) {
 // column per lane) is read with two ds_read_b64_tr_b16: within each 16-lane group, result
 // lane i gets element i mod 4 of source lanes 4e + i / 4 (e = 0..3), so source lane L
 // pointing at B[k0 + L / 4][n0 + 4 (L mod 4)] hands lane i the column B[k0 .. k0 + 3][n0 + i].
-// The 16-byte chunks are XOR-swizzled in LDS (a_swz, b_swz below).  Waits are explicit
+// The 16-byte chunks are permuted in LDS (a_rot, b_swz below).  Waits are explicit
 // (vmcnt for this wave's DMA, then a plain s_barrier): a __syncthreads() would drain every
 // K-tile in flight.  Requires K % 32 == 0 (split-K slices are multiples of 32); other K take
 // the register-staged kernel above.
@@ -229,20 +230,31 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
 // (a stage may be refilled right after the barrier), then barrier
 #define W4_SYNC(n) asm volatile("s_waitcnt vmcnt(" #n ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
-// LDS swizzles of the DMA kernel's stages, chosen so that every LDS read of a fragment is
-// free of bank conflicts whether the LDS serves 128 or 256 bytes per clock.
-//  A stage: row r holds 64 B = four 16-B chunks; logical chunk c sits at c ^ a_swz(r).  A
-//  b128 read covers rows r0..r0+15 (r0 % 16 == 0) at one logical chunk: a_swz is a bijection
-//  of (r >> 1) & 3 over any 8 consecutive rows of equal parity, and of (r >> 2) & 3 over the
-//  16 rows of equal r & 3, so both 8-lane and 16-lane phases hit distinct banks.
+// LDS layouts of the DMA kernel's stages (bank conflicts counted with SQ_LDS_BANK_CONFLICT
+// on in-bounds probes of exactly these read patterns: a 16-byte read of 64 lanes takes 4 LDS
+// cycles when conflict-free, a transposing 8-byte read 2).
+//  A stage: row r holds 64 B = four 16-B chunks; logical chunk c sits at physical chunk
+//  (c + a_rot(r)) & 3, a_rot(r) = (r + (r >> 2)) & 3.  A fragment read takes 32 consecutive
+//  rows (r0 % 32 == 0) at logical chunk c for lanes 0-31 and c + 1 for lanes 32-63; the
+//  rotation gives each of any 4 rows of equal r & 3 (r0 + j + 4t, t = 0..3) a different
+//  chunk, and measured 4 cycles per read, where an XOR layout bijective over the same row
+//  sets took 8 and the plain layout 16.
 //  B stage: k-row holds 512 B = 32 chunks; chunk c sits at c ^ b_swz(k).  A transposing b64
 //  read takes, per 16 lanes, 4 consecutive k-rows x 2 chunks and, per 32 lanes, 4 k-rows x
 //  4 chunks; b_swz(k) = 2 * h(k & 3) with h(x) = (x ^ 2x) & 7, whose bits 1..2 and 2..3 are
-//  both bijective in k & 3, spreads either phase over distinct banks.
-__device__ __forceinline__ int a_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+//  both bijective in k & 3, spreads either phase over distinct banks (measured 2 cycles per
+//  read).
+__device__ __forceinline__ int a_rot(int r) { return (r + (r >> 2)) & 3; }
 __device__ __forceinline__ int b_swz(int k) {
   const int x = k & 3;
   return ((x ^ (x << 1)) & 7) << 1;
+}
+
+// W4_SYNC with a compile-time count
+template <int N>
+__device__ __forceinline__ void dma_sync_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 0..63");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 // W4_SYNC with a wave-uniform count of DMA instructions allowed to stay in flight
@@ -299,7 +311,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_dma_kernel(GemmArgs g) {
   for (int ta = 0; ta < AW; ++ta) {
     const int i = min(wave + NW * ta, AI - 1);
     const int row = 16 * i + (lane >> 2);
-    const int ca = (lane & 3) ^ a_swz(row);
+    const int ca = ((lane & 3) - a_rot(row)) & 3;  // the logical chunk that lands at chunk lane & 3
     a_src[ta] = g.A + (int64_t)min(m0 + row, g.M - 1) * g.lda + kbeg + ca * 8;
   }
 #pragma unroll
@@ -321,14 +333,27 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_dma_kernel(GemmArgs g) {
             st + (uint32_t)(BMT * DBK * 2 + (wave * DI + ii) * 1024));
   };
 
+  // DMA instruction d of this wave for tile t: d < AW the A rows of instruction wave + NW d
+  // (when d < na), else B k-rows 2 (DI wave + d - AW) .. + 1
+  auto dma_one = [&](int t, int d) {
+    const uint32_t st = lds_base + (uint32_t)((t % DSTAGES) * STAGE);
+    if (d < AW) {
+      if (AI % NW == 0 || d < na)  // every wave issues AW A instructions when NW divides AI
+        dma16(a_src[d] + t * DBK, st + (uint32_t)((wave + NW * d) * 1024));
+    } else {
+      const int ii = d - AW;
+      dma16(b_src[ii] + (int64_t)t * DBK * g.ldb, st + (uint32_t)(BMT * DBK * 2 + (wave * DI + ii) * 1024));
+    }
+  };
+
   // per-lane LDS read offsets (bytes within a stage)
-  // a_swz depends on row bits 1..4 only, so the row blocks mi differ by a constant 2 KB
+  // a_rot depends on r mod 16 only, so the row blocks mi differ by a constant 2 KB
   int a_off[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     const int r = wm * WTM + (lane & 31);
     const int c = 2 * ks + (lane >> 5);
-    a_off[ks] = r * 64 + ((c ^ a_swz(r)) * 16);
+    a_off[ks] = r * 64 + (((c + a_rot(r)) & 3) * 16);
   }
   int b_off[NJ][2][2];
   {
@@ -358,26 +383,36 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_dma_kernel(GemmArgs g) {
   // transposing b64 reads each).  Two sets alternate so that the reads of the next k-step
   // are in flight while the 16 MFMAs of the current one run.
   struct Frag {
-    f16x8 a[MI], b[NJ];
+    f16x8 a[MI];
+    s16x4 blo[NJ], bhi[NJ];
+  };
+  // LDS read r of a fragment set: r < MI the A rows of block r, else half (r - MI) & 1 of the
+  // B columns of block (r - MI) / 2
+  auto load_one = [&](const unsigned char* st, int ks, Frag& f, int r) {
+    if (r < MI) {
+      f.a[r] = *reinterpret_cast<const f16x8*>(st + a_off[ks] + r * 2048);
+    } else {
+      const int nj = (r - MI) >> 1, h = (r - MI) & 1;
+      const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(st + b_off[nj][ks][h]));
+      if (h == 0)
+        f.blo[nj] = v;
+      else
+        f.bhi[nj] = v;
+    }
   };
   auto load = [&](const unsigned char* st, int ks, Frag& f) {
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) f.a[mi] = *reinterpret_cast<const f16x8*>(st + a_off[ks] + mi * 2048);
-#pragma unroll
-    for (int nj = 0; nj < NJ; ++nj) {
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(st + b_off[nj][ks][0]));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(st + b_off[nj][ks][1]));
-      f.b[nj] = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
+    for (int r = 0; r < MI + 2 * NJ; ++r) load_one(st, ks, f, r);
+  };
+  auto mma_one = [&](const Frag& f, int j) {
+    const int mi = j / NJ, nj = j % NJ;
+    const f16x8 b = __builtin_bit_cast(f16x8, __builtin_shufflevector(f.blo[nj], f.bhi[nj], 0, 1, 2, 3, 4, 5, 6, 7));
+    acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, f.a[mi], acc[mi][nj], 0, 0, 0);
   };
   auto mma = [&](const Frag& f) {
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int nj = 0; nj < NJ; ++nj)
-        acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[nj], f.a[mi], acc[mi][nj], 0, 0, 0);
+    for (int j = 0; j < MI * NJ; ++j) mma_one(f, j);
   };
   // the MI + 2 * NJ LDS reads of the next fragments interleaved one-to-one with the first
   // of the MI * NJ MFMAs
@@ -397,24 +432,45 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_dma_kernel(GemmArgs g) {
   // reads k-step 1 of tile t while computing k-step 0, meets the other waves at a barrier
   // (after it tile t + 1 has landed and no wave reads tile t's stage any more, so the DMA of
   // tile t + 4 may overwrite it), then reads k-step 0 of tile t + 1 while computing k-step 1
-  // of tile t.
-  const int pre = min(DSTAGES, nk);
-  for (int t = 0; t < pre; ++t) issue(t);
-  dma_sync((pre - 1) * per_tile);  // tile 0 landed; tiles 1 .. pre-1 may be in flight
+  // of tile t, with this wave's DMA instructions for tile t + 4 issued one after every second
+  // MFMA.  (Issued together right after the barrier, the eight waves' DMA instructions queue
+  // for the vector memory path at once and every wave stalls there while the matrix cores
+  // idle: ~20 % of each K-tile.)
   Frag f0, f1;
-  load(dlds, 0, f0);
-  for (int t = 0; t + 1 < nk; ++t) {
+  constexpr int NDMA = AW + DI;  // DMA instructions per wave and K-tile, at most
+  constexpr int STEPS = (MF > RD ? MF : RD) > 2 * NDMA ? (MF > RD ? MF : RD) : 2 * NDMA;
+  auto iter = [&](int t, auto refill_c) {
+    constexpr bool REFILL = decltype(refill_c)::value;
     load(dlds + (t % DSTAGES) * STAGE, 1, f1);
     mma(f0);
     interleave();
     __builtin_amdgcn_sched_barrier(0);
-    dma_sync(min(2, nk - 2 - t) * per_tile);  // tiles after t + 1 already issued may fly
-    if (t + DSTAGES < nk) issue(t + DSTAGES);
-    load(dlds + ((t + 1) % DSTAGES) * STAGE, 0, f0);
-    mma(f1);
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
-  }
+    if constexpr (REFILL) {
+      // tiles t + 2 and t + 3 may fly: 2 per_tile instructions, per_tile = na + DI
+      if (na == AW)
+        dma_sync_n<2 * (AW + DI)>();
+      else
+        dma_sync_n<2 * (AW - 1 + DI)>();
+    } else {
+      dma_sync(min(2, nk - 2 - t) * per_tile);  // tiles after t + 1 already issued may fly
+    }
+    const unsigned char* nst = dlds + ((t + 1) % DSTAGES) * STAGE;
+#pragma unroll
+    for (int j = 0; j < STEPS; ++j) {
+      if (j < RD) load_one(nst, 0, f0, j);
+      if (j < MF) mma_one(f1, j);
+      if constexpr (REFILL)
+        if ((j & 1) && (j >> 1) < NDMA) dma_one(t + DSTAGES, j >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  const int pre = min(DSTAGES, nk);
+  for (int t = 0; t < pre; ++t) issue(t);
+  dma_sync((pre - 1) * per_tile);  // tile 0 landed; tiles 1 .. pre-1 may be in flight
+  load(dlds, 0, f0);
+  int t = 0;
+  for (; t + DSTAGES < nk; ++t) iter(t, std::true_type{});
+  for (; t + 1 < nk; ++t) iter(t, std::false_type{});
   load(dlds + ((nk - 1) % DSTAGES) * STAGE, 1, f1);
   mma(f0);
   interleave();
