@@ -157,7 +157,9 @@ int gemm_f16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, flo
  * -0.0 equal to +0.0; idx[m][0] is the argmax; val[m][r] == logits[m][idx[m][r]] bit for bit.
  * Requires 1 <= M, 1 <= k <= min(V, 256), V < 2^31, ldl >= V, ceil(V / 8192) * k <= 8192;
  * logits 4-byte aligned, idx/val 4-byte aligned.  Logits must be finite (unchecked).
- * Workspace: M * ceil(V / chunk) * k * 8 bytes (query it; 0 when V <= 4096).
+ * Workspace (query it; 0 when V <= 4096): k <= 64: one 8-byte key per 64 logits,
+ * M * ceil(V / 64) * 8 bytes (19 KB for one 151936-logit row); k > 64: M * ceil(V / chunk) * k * 8
+ * bytes with chunk = 4096 or 8192 logits.  Contents need no initialisation.
  */
 int logits_argmax_topk(const float* logits, int64_t ldl, int64_t M, int64_t V, int64_t k,
                        int32_t* idx, float* val, void* ws, size_t* ws_bytes, w4_stream_t stream);
@@ -175,8 +177,9 @@ int logits_argmax_topk(const float* logits, int64_t ldl, int64_t M, int64_t V, i
  * Each logit is within 2e-3 * sum_k |w[v][k] x[k]| of the exact sum (as w4_gemv at M = 1), and
  * the selection is exact on the logits it writes.
  * Two launches: the M = 1 GEMV, whose workgroups also write the largest key of their rows (8 to
- * 16 rows each at K <= 2048, 2 to 4 above) to the workspace, then one workgroup that takes the k
- * largest of those, re-reads those k groups' rows and selects (every top-k logit lies in them).
+ * 16 rows each at K <= 2048, 2 to 4 above) to the workspace, then one workgroup that finds the
+ * k-th largest of those keys (radix select), re-reads the rows of the k groups that reach it
+ * and selects from them (every top-k logit lies in them).
  * Requires 1 <= k <= 64, k <= V <= 524288, 64 <= K <= 4096, K % 64 == 0; qw, scales, biases, x
  * 16-byte aligned; logits, idx, val 4-byte aligned.  Workspace: 8 bytes per GEMV workgroup
  * (query it; 74.2 KiB for 151936 rows at K = 2048); nothing in it has to be initialised.
@@ -190,8 +193,8 @@ int w4_gemv_topk(const uint32_t* qw, const uint16_t* scales, const uint16_t* bia
  * logits_argmax_topk_noalloc -- logits_argmax_topk for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc).  Same arguments, requirements, results and errors as logits_argmax_topk, minus
- * the workspace: the pass-1 candidates (M * ceil(V / chunk) * k * 8 bytes, the size
- * logits_argmax_topk would ask for) go to a 4 MiB array that the library holds on each device
+ * the workspace: what logits_argmax_topk would keep there (the size it would ask for) goes
+ * to a 4 MiB array that the library holds on each device
  * until the process ends.  Needing more than 4 MiB returns W4_ERR_WORKSPACE without launching
  * (e.g. top-64 of 262144 logits needs 32 KiB per row, so up to 128 such rows per call).  The
  * call allocates nothing.  Calls that overlap on one device (concurrent streams, or host

@@ -636,8 +636,8 @@ void launch_mf(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const u
 // offsets below R rows); otherwise one buffer per array and the row offset in the scalar
 // register (measured 1-2 % faster).
 // MAXK (M = 1 only): each workgroup also writes the largest selection key (w4_select.h) of its
-// rows to wgmax[blockIdx.x] -- 4 R rows with KS = 1, R rows otherwise -- the first step of the
-// int4 LM head's fused token selection.
+// rows to wgmax[blockIdx.x] (4 R rows with KS = 1, after one barrier at the end; R rows
+// otherwise) -- the first step of the int4 LM head's fused token selection.
 template <int R, int KS, bool SYM, bool BIG, int MT, bool MAXK = false>
 __global__ __launch_bounds__(KS == 1 ? kWG : KS * 64) void gemv1s_kernel(
     const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc, const uint16_t* __restrict__ bi,
@@ -647,11 +647,6 @@ __global__ __launch_bounds__(KS == 1 ? kWG : KS * 64) void gemv1s_kernel(
   static_assert(!MAXK || MT == 1, "workgroup maxima for one activation row");
   __shared__ float red[KS][R * MT];
   __shared__ uint64_t wmax[kWG / 64];
-  __shared__ int nwaves_done;
-  if constexpr (MAXK && KS == 1) {  // the last wave to finish writes the workgroup's maximum
-    if (threadIdx.x == 0) nwaves_done = 0;
-    __syncthreads();  // at the start, where every wave is anyway
-  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int slice = KS == 1 ? 0 : wave;
@@ -747,15 +742,15 @@ __global__ __launch_bounds__(KS == 1 ? kWG : KS * 64) void gemv1s_kernel(
           km = kr > km ? kr : km;
         }
       }
-      if constexpr (MAXK) {
-        wmax[wave] = km;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        if (atomicAdd(&nwaves_done, 1) == kWG / 64 - 1) {  // the other waves' maxima are in LDS
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      if constexpr (MAXK) wmax[wave] = km;
+    }
+    if constexpr (MAXK) {  // one barrier at the end: wave 0 writes the workgroup's maximum
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        uint64_t km = wmax[0];
 #pragma unroll
-          for (int w = 0; w < kWG / 64; ++w) km = wmax[w] > km ? wmax[w] : km;
-          wgmax[blockIdx.x] = km;
-        }
+        for (int w = 1; w < kWG / 64; ++w) km = wmax[w] > km ? wmax[w] : km;
+        wgmax[blockIdx.x] = km;
       }
     }
   } else {
@@ -960,8 +955,8 @@ HeadGemvPlan head_gemv_plan(int64_t N, int64_t K) {
   const bool fits3 = p.KS == 1 && N > 2 * kSimds && N <= 3 * kSimds;
   p.R = units >= 30000 ? 4 : ((units >= 16000 && p.KS == 1) || fits3) ? 3 : 2;
   if (p.KS > 1) p.R = p.R == 3 ? 2 : p.R;  // row slices of several waves come in 2 or 4 rows
-  p.rows_per_wg = p.KS == 1 ? p.R * (kWG / 64) : p.R;
-  p.nwg = (int)((N + p.rows_per_wg - 1) / p.rows_per_wg);
+  p.rows_per_key = p.KS == 1 ? p.R * (kWG / 64) : p.R;  // one key per workgroup
+  p.nkeys = (int)((N + p.rows_per_key - 1) / p.rows_per_key);
   return p;
 }
 

@@ -238,6 +238,44 @@ __global__ __launch_bounds__(kWG) void wtopk_final_kernel(const float* __restric
   }
 }
 
+// Pass 1 of the group-maxima selection (k <= 64): gkeys[m][g] = the largest key among
+// logits[m][64 g, 64 g + 64).  A workgroup of 256 threads covers 4096 logits: thread t holds
+// 16 consecutive ones (four 16-byte loads when the row allows them), four lanes a group.
+__global__ __launch_bounds__(kWG) void group_max_kernel(const float* __restrict__ logits, int64_t ldl, int V,
+                                                         int G, uint64_t* __restrict__ gkeys, int vec) {
+  const int m = blockIdx.y, t = threadIdx.x;
+  const float* row = logits + (int64_t)m * ldl;
+  const int base = blockIdx.x * 4096 + t * 16;
+  float v[16];
+  if (vec && base + 16 <= V) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 f = reinterpret_cast<const float4*>(row + base)[q];
+      v[4 * q] = f.x;
+      v[4 * q + 1] = f.y;
+      v[4 * q + 2] = f.z;
+      v[4 * q + 3] = f.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = row[min(base + j, V - 1)];
+  }
+  uint64_t mx = 0;  // below every real key
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint64_t x = base + j < V ? make_key(v[j], (uint32_t)(base + j)) : 0ull;
+    mx = x > mx ? x : mx;
+  }
+#pragma unroll
+  for (int o = 1; o <= 2; o <<= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)mx, o), hi = __shfl_xor((uint32_t)(mx >> 32), o);
+    const uint64_t y = ((uint64_t)hi << 32) | lo;
+    mx = y > mx ? y : mx;
+  }
+  const int g = base / 64;
+  if ((t & 3) == 0 && g < G) gkeys[(int64_t)m * G + g] = mx;
+}
+
 template <int E>
 void launch_wfinal(const float* logits, int64_t ldl, int M, int V, int k, const uint64_t* cand,
                    int ncand, int32_t* idx, float* val, hipStream_t st) {
@@ -295,8 +333,16 @@ int topk_chunk(int64_t V, int k) {
   return 0;
 }
 
+// k <= 64 and rows longer than 4096 logits (up to 4M with k = 64): group maxima of 64 logits
+// (pass 1), then one selection workgroup per row (group_select_kernel); otherwise chunks of
+// topk_chunk() logits whose k best go to the workspace, then a final pass over those.
+bool topk_groups(int64_t V, int k) {
+  return k <= 64 && V > 4096 && gs_prereduce((V + 63) / 64, 64, k) != 0;
+}
+
 size_t topk_ws_bytes(int64_t M, int64_t V, int k) {
   if (V <= 4096) return 0;
+  if (topk_groups(V, k)) return (size_t)M * (size_t)((V + 63) / 64) * sizeof(uint64_t);
   const int chunk = topk_chunk(V, k);
   if (chunk == 0) return 0;
   return (size_t)M * (size_t)((V + chunk - 1) / chunk) * (size_t)k * sizeof(uint64_t);
@@ -304,13 +350,15 @@ size_t topk_ws_bytes(int64_t M, int64_t V, int k) {
 
 void launch_topk(const float* logits, int64_t ldl, int M, int V, int k, int32_t* idx, float* val,
                  void* ws, hipStream_t st) {
-  static std::once_flag lds_attr[kMaxDevices];  // the E = 32 wave kernels use more than 64 KB of LDS
+  static std::once_flag lds_attr[kMaxDevices];  // several kernels use more than 64 KB of LDS
   once_per_device(lds_attr, [] {
     for (const void* f : {reinterpret_cast<const void*>(wtopk_chunk_kernel<32, false>),
                           reinterpret_cast<const void*>(wtopk_chunk_kernel<32, true>),
                           reinterpret_cast<const void*>(wtopk_final_kernel<32, false>),
                           reinterpret_cast<const void*>(wtopk_final_kernel<32, true>)})
       (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)group_lds<4, 32>());
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(group_select_kernel<>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)gs_lds_bytes(kGsMaxKeys));
   });
   const bool wave = k <= 64;
   if (V <= 4096) {
@@ -320,9 +368,21 @@ void launch_topk(const float* logits, int64_t ldl, int M, int V, int k, int32_t*
       final_pass(logits, ldl, M, V, k, nullptr, V, idx, val, st);
     return;
   }
+  uint64_t* cand = reinterpret_cast<uint64_t*>(ws);
+  if (topk_groups(V, k)) {
+    const int G0 = (V + 63) / 64;
+    const int vec = ((uintptr_t)logits & 15u) == 0 && ldl % 4 == 0;
+    hipLaunchKernelGGL(group_max_kernel, dim3((V + 4095) / 4096, M), dim3(kWG), 0, st, logits, ldl, V, G0, cand,
+                       vec);
+    const int P = gs_prereduce(G0, 64, k);
+    const int G = (G0 + P - 1) / P;
+    const int cap = G > k * 64 * P ? G : k * 64 * P;
+    hipLaunchKernelGGL(group_select_kernel<>, dim3(M), dim3(kGsThreads), gs_lds_bytes(cap), st, logits, ldl, V, k,
+                       cand, G0, 64, P, cap, idx, val);
+    return;
+  }
   const int chunk = topk_chunk(V, k);
   const int nchunks = (V + chunk - 1) / chunk;
-  uint64_t* cand = reinterpret_cast<uint64_t*>(ws);
   if (wave) {
     const dim3 grid(nchunks, M);
     if (chunk == 4096 && k > 48)

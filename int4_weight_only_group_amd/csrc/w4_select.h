@@ -192,4 +192,244 @@ __device__ void group_topk(const uint64_t (&key)[E], int k, unsigned char* smem,
   __syncthreads();
 }
 
+// ------------------------------------------------ group-maxima selection (one workgroup)
+// Top k (k <= 64) of a row from the largest key of each group of its logits.  T, the k-th
+// largest group key, is reached by k distinct keys of the row, so the row's k-th best key is
+// >= T and so is every key of its top k; the group of such a key has a maximum >= T, i.e. it is
+// one of the k groups whose keys are >= T.  Only those groups' logits are read again; their
+// keys >= T (at least the k group maxima) hold the row's top k, which is selected from them
+// the same way.  Every step is exact; values are re-read from the logits (-0.0 stays -0.0).
+constexpr int kGsThreads = 1024;   // threads of the selection workgroup
+constexpr int kGsBins = 4096;      // radix digits of 12 bits (4 bins per thread)
+constexpr int kGsRank = 256;       // matching keys ranked directly from this few on
+constexpr int kGsMaxKeys = 16384;  // group keys (after pre-reduction) / re-read keys in LDS
+
+// LDS bytes of group_select_kernel for cap keys: keys, the rank pool, the histogram, 8 ints
+// and kGsThreads / 64 wave totals
+__host__ __device__ constexpr size_t gs_lds_bytes(int cap) {
+  return (size_t)(((cap + 15) & ~15) + kGsRank) * 8 + (size_t)(kGsBins + 8 + kGsThreads / 64) * 4;
+}
+
+// Number of keys of pool[0 .. n) larger than x; pool is padded with zeros (below every real
+// key) to a multiple of 16, read 16 at a time so the LDS reads overlap.
+__device__ __forceinline__ int rank_in(const uint64_t* pool, int n, uint64_t x) {
+  int r = 0;
+  for (int j = 0; j < n; j += 16) {
+    uint64_t v[16];
+    load16(pool + j, v);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) r += v[q] > x ? 1 : 0;
+  }
+  return r;
+}
+
+// The kk-th largest (1 <= kk <= n) of the n distinct keys A[0..n) in LDS, by the whole
+// workgroup (every thread calls it; all get the result).  Radix select from the top, 12 bits a
+// round (4 in the last): a histogram of the next digit over the keys matching the digits
+// chosen so far, the digit at which the count from the top reaches kk, then the next digit
+// among the keys with that one; once at most kGsRank keys match (after at most 6 rounds, keys
+// being distinct) they are ranked by counting the larger ones.  hist: kGsBins ints, misc: 8
+// ints, wt: kGsThreads / 64 ints, pool: kGsRank keys (16-key aligned), all LDS.
+__device__ inline uint64_t block_kth(const uint64_t* A, int n, int kk, int* hist, int* misc, int* wt,
+                                     uint64_t* pool) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  uint64_t prefix = 0, mask = 0;
+  int m = n;
+  // m is the same in every thread (read from LDS after a barrier); 6 rounds fix all 64 bits
+  for (int round = 0; round < 6 && m > kGsRank; ++round) {
+    const int shift = round < 5 ? 52 - 12 * round : 0;
+    const uint64_t dmask = round < 5 ? 0xFFFull : 0xFull;
+#pragma unroll
+    for (int q = 0; q < kGsBins / kGsThreads; ++q) hist[q * kGsThreads + tid] = 0;
+    __syncthreads();
+#pragma unroll 4
+    for (int i = tid; i < n; i += kGsThreads) {
+      const uint64_t x = A[i];
+      if ((x & mask) == prefix) atomicAdd(&hist[(int)((x >> shift) & dmask)], 1);
+    }
+    __syncthreads();
+    // thread t holds bins 4t .. 4t + 3 (one 16-byte read); counts from the top digit down
+    const int4 hv = reinterpret_cast<const int4*>(hist)[tid];
+    const int h0 = hv.x, h1 = hv.y, h2 = hv.z, h3 = hv.w;
+    const int s = h0 + h1 + h2 + h3;
+    int S = s;  // keys in bins >= 4t within this wave's range
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_down(S, o);
+      if (lane + o < 64) S += u;
+    }
+    if (lane == 0) wt[w] = S;
+    __syncthreads();
+#pragma unroll
+    for (int v = 1; v < kGsThreads / 64; ++v)
+      if (v > w) S += wt[v];  // keys in the later waves' bins
+    const int above = S - s;  // keys in bins > 4t + 3
+    if (above < kk && kk <= S) {  // exactly one thread
+      int c = above, d = 4 * tid, cnt = h0;
+      if (c + h3 >= kk) {
+        d = 4 * tid + 3, cnt = h3;
+      } else if ((c += h3) + h2 >= kk) {
+        d = 4 * tid + 2, cnt = h2;
+      } else if ((c += h2) + h1 >= kk) {
+        d = 4 * tid + 1, cnt = h1;
+      } else {
+        c += h1;
+      }
+      misc[0] = d;
+      misc[1] = c;
+      misc[2] = cnt;
+    }
+    __syncthreads();
+    const int d = misc[0];
+    kk -= misc[1];
+    m = misc[2];
+    prefix |= (uint64_t)d << shift;
+    mask |= dmask << shift;
+    __syncthreads();  // hist, wt and misc are rewritten by the next round
+  }
+  if (tid == 0) misc[3] = 0;
+  if (tid < kGsRank) pool[tid] = 0ull;  // padding of the rank reads
+  __syncthreads();
+#pragma unroll 4
+  for (int i = tid; i < n; i += kGsThreads) {
+    const uint64_t x = A[i];
+    if ((x & mask) == prefix) {
+      const int p = atomicAdd(&misc[3], 1);
+      if (p < kGsRank) pool[p] = x;  // m <= kGsRank for distinct keys
+    }
+  }
+  __syncthreads();
+  m = m < kGsRank ? m : kGsRank;
+  if (tid < m) {
+    const uint64_t x = pool[tid];
+    if (rank_in(pool, m, x) == kk - 1) {  // exactly one key
+      misc[4] = (int)(uint32_t)x;
+      misc[5] = (int)(uint32_t)(x >> 32);
+    }
+  }
+  __syncthreads();
+  const uint64_t T = ((uint64_t)(uint32_t)misc[5] << 32) | (uint32_t)misc[4];
+  __syncthreads();  // misc may be rewritten right after the return
+  return T;
+}
+
+// Row blockIdx.x: gkeys[row][0 .. G0) are the largest keys of consecutive groups of gs logits
+// (the last group may be short); P consecutive ones are combined first (groups of P gs
+// logits), so G = ceil(G0 / P) <= kGsMaxKeys and k P gs <= kGsMaxKeys.  Writes the row's top k
+// (k <= 64, k <= V) to idx/val in order.  Dynamic LDS: gs_lds_bytes(max(G, k P gs)).  (A template
+// only so that every file including this header may instantiate it.)
+template <int = 0>
+__global__ __launch_bounds__(kGsThreads) void group_select_kernel(const float* __restrict__ logits, int64_t ldl,
+                                                                  int V, int k, const uint64_t* __restrict__ gkeys,
+                                                                  int G0, int gs, int P, int cap,
+                                                                  int32_t* __restrict__ idx,
+                                                                  float* __restrict__ val) {
+  extern __shared__ __align__(16) unsigned char gsmem[];
+  uint64_t* A = reinterpret_cast<uint64_t*>(gsmem);
+  uint64_t* pool = A + ((cap + 15) & ~15);  // 128-byte aligned for the rank reads
+  int* hist = reinterpret_cast<int*>(pool + kGsRank);
+  int* misc = hist + kGsBins;
+  int* wt = misc + 8;
+  __shared__ int sel[64];
+  __shared__ int nsel, npool;
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const uint64_t* gk = gkeys + (int64_t)m * G0;
+  const float* row = logits + (int64_t)m * ldl;
+  const int G = (G0 + P - 1) / P, gsp = gs * P;
+  // group keys: thread t combines the P consecutive keys of groups t, t + kGsThreads, ...,
+  // U groups and 4 keys of each in flight at a time
+  constexpr int U = 8;
+  const int iters = (G + U * kGsThreads - 1) / (U * kGsThreads);
+  for (int it = 0; it < iters; ++it) {
+    uint64_t x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = 0;
+    for (int p0 = 0; p0 < P; p0 += 4) {
+      uint64_t y[U][4];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int g = tid + (it * U + u) * kGsThreads;
+          const int64_t e = (int64_t)g * P + p0 + q;
+          y[u][q] = g < G && p0 + q < P && e < G0 ? gk[e] : 0ull;
+        }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x[u] = y[u][q] > x[u] ? y[u][q] : x[u];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int g = tid + (it * U + u) * kGsThreads;
+      if (g < G) A[g] = x[u];
+    }
+  }
+  if (tid == 0) {
+    nsel = 0;
+    npool = 0;
+  }
+  __syncthreads();
+  // fewer groups than k: all of them (T = 0 is below every real key)
+  const uint64_t T = k <= G ? block_kth(A, G, k, hist, misc, wt, pool) : 0ull;
+  for (int g = tid; g < G; g += kGsThreads)
+    if (A[g] >= T) {
+      const int p = atomicAdd(&nsel, 1);  // exactly min(k, G) groups
+      if (p < 64) sel[p] = g;
+    }
+  __syncthreads();
+  const int nre = (nsel < k ? nsel : k) * gsp;
+  constexpr int UR = 4;
+  for (int i0 = tid; i0 < nre; i0 += UR * kGsThreads) {
+    float f[UR];
+    int64_t r[UR];
+#pragma unroll
+    for (int u = 0; u < UR; ++u) {
+      const int i = i0 + u * kGsThreads;
+      r[u] = i < nre ? (int64_t)sel[i / gsp] * gsp + i % gsp : (int64_t)V;
+      f[u] = r[u] < V ? row[r[u]] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < UR; ++u) {
+      if (r[u] < V) {
+        const uint64_t x = make_key(f[u], (uint32_t)r[u]);
+        if (x >= T) {
+          const int p = atomicAdd(&npool, 1);
+          if (p < cap) A[p] = x;  // nre <= cap
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const int n2 = npool < cap ? npool : cap;  // >= k: the selected groups' maxima, or every logit when G < k
+  const uint64_t T2 = block_kth(A, n2, k, hist, misc, wt, pool);
+  if (tid == 0) misc[6] = 0;
+  if (tid < 64) pool[tid] = 0ull;  // padding of the rank reads
+  __syncthreads();
+  for (int i = tid; i < n2; i += kGsThreads) {
+    const uint64_t x = A[i];
+    if (x >= T2) {
+      const int p = atomicAdd(&misc[6], 1);  // exactly k keys
+      if (p < kGsRank) pool[p] = x;
+    }
+  }
+  __syncthreads();
+  if (tid < k) {
+    const uint64_t x = pool[tid];
+    const int r = rank_in(pool, k, x);
+    uint32_t j = key_index(x);
+    if (j >= (uint32_t)V) j = (uint32_t)V - 1;  // unreachable: the keys are real logits
+    idx[(int64_t)m * k + r] = (int32_t)j;
+    val[(int64_t)m * k + r] = row[j];
+  }
+}
+
+// Pre-reduction for G0 group keys of gs logits each: the smallest power of two P with
+// ceil(G0 / P) <= kGsMaxKeys, or 0 when k P gs would exceed kGsMaxKeys.
+__host__ __device__ inline int gs_prereduce(int64_t G0, int gs, int k) {
+  int P = 1;
+  while ((G0 + P - 1) / P > kGsMaxKeys) P *= 2;
+  return (int64_t)k * P * gs <= kGsMaxKeys ? P : 0;
+}
+
 }  // namespace w4

@@ -142,7 +142,7 @@ def test_topk_argument_errors_and_workspace_query():
     assert t(lg=P + 2) == W4_ERR_ALIGN
     n = ctypes.c_size_t(0)
     assert t(V=151936, k=40, M=1, wsb=ctypes.byref(n)) == W4_OK
-    assert n.value == 38 * 40 * 8  # 38 chunks of 4096 logits, 40 keys of 8 bytes each
+    assert n.value == 2374 * 8  # one row: one 8-byte key per group of 64 logits
     small = ctypes.c_size_t(n.value - 8)
     assert t(V=151936, k=40, ws=P, wsb=ctypes.byref(small)) == W4_ERR_WORKSPACE
     assert t(V=151936, k=40, ws=None, wsb=None) == W4_ERR_WORKSPACE
@@ -162,7 +162,7 @@ def test_gemv_topk_argument_errors_and_workspace_query():
     assert g(V=30, k=40) == W4_ERR_SHAPE
     assert g(K=96) == W4_ERR_SHAPE
     assert g(K=4160) == W4_ERR_SHAPE
-    assert g(V=524289, k=64) == W4_ERR_SHAPE     # the re-read groups would exceed 8192 rows
+    assert g(V=524289, k=64) == W4_ERR_SHAPE     # beyond the documented 524288 rows
     assert g(V=524288, k=64, wsb=ctypes.byref(ctypes.c_size_t(0))) == W4_OK
     assert g(x=P + 8) == W4_ERR_ALIGN
     assert g(lg=P + 2) == W4_ERR_ALIGN
