@@ -189,3 +189,21 @@ def test_binding_names_match_abi():
     for n in ("w4_pack", "w4_gemv", "w4_dequant_f16_t", "gemm_f16", "logits_argmax_topk"):
         assert callable(getattr(w4, n))
     assert w4.topk_workspace_bytes(8, 262144, 64) == 8 * 64 * 64 * 8
+
+
+def test_gemm_workspace_query():
+    # The workspace each GEMM plan asks for: none when the output tiles fill the CUs at least
+    # half way; ksplit * M * N * 4 bytes when K is split
+    lib = _lib()
+    A = 1 << 20
+
+    def need(m, n, k):
+        nb = ctypes.c_size_t(0)
+        assert lib.gemm_f16(A, k, A, n, A, n, m, n, k, None, ctypes.byref(nb), None) == W4_OK
+        return nb.value
+    assert need(4096, 4096, 4096) == 0                      # 256 tiles: one full round
+    assert need(1570, 22016, 2048) == 0                     # 430 tiles of 320 x 256
+    assert need(1570, 2048, 11008) == 6 * 1570 * 2048 * 4   # 40 tiles, K split 6 ways
+    assert need(600, 2048, 4096) == 8 * 600 * 2048 * 4      # 24 tiles, 8 slices of 8 K-tiles of 64
+    assert need(600, 25608, 64) == 0                        # 202 tiles
+    assert need(8, 4096, 256) == 0                          # small-M path

@@ -625,6 +625,34 @@ def test_gemm_tall_tiles(w4, m, n, k, sampled):
     assert ok, worst
 
 
+# Several rounds of 256-row output tiles over the 256 CUs (471, 471 and 472 tiles: the last
+# round partly filled), ragged in M and N, with 2, 3 and 32 K-tiles of 32 per tile.
+@pytest.mark.parametrize("m,n,k,sampled", [
+    (600, 40000, 64, False), (700, 40000, 96, False), (1000, 30000, 1024, True),
+])
+def test_gemm_multi_round(w4, m, n, k, sampled):
+    a = synth.activations(m, k, seed=m + k)
+    bmat = synth.activations(k, n, seed=n + 3)
+    c = to_np(w4.gemm_f16(dev(a), dev(bmat)))
+    rows = np.arange(m)
+    if sampled:  # the last row tile (768..999) whole, 40 rows of the others
+        rows = np.unique(np.concatenate([np.random.default_rng(m).choice(768, 40, replace=False),
+                                         np.arange(768, m)]))
+    c_ref, bound = oracle.gemm_ref(a[rows], bmat)
+    ok, worst = oracle.check_bound(c[rows], c_ref, bound, RTOL)
+    assert ok, worst
+
+
+def test_gemm_prefill_deterministic(w4):
+    # the prefill gate|up shape (two rounds of 320-row tiles): bit-identical on repeat
+    m, n, k = 1570, 22016, 2048
+    a = dev(synth.activations(m, k, seed=11))
+    b = dev(synth.activations(k, n, seed=12))
+    c1 = to_np(w4.gemm_f16(a, b))
+    c2 = to_np(w4.gemm_f16(a, b))
+    assert np.array_equal(c1.view(np.uint32), c2.view(np.uint32))
+
+
 def test_gemm_deterministic(w4):
     a = dev(synth.activations(300, 512, seed=7))
     b = dev(synth.activations(512, 1024, seed=8))
