@@ -424,12 +424,22 @@ __global__ __launch_bounds__(kGsThreads) void group_select_kernel(const float* _
   }
 }
 
-// Pre-reduction for G0 group keys of gs logits each: the smallest power of two P with
-// ceil(G0 / P) <= kGsMaxKeys, or 0 when k P gs would exceed kGsMaxKeys.
+// Pre-reduction for G0 group keys of gs logits each: the power of two P that minimises the
+// keys the two radix selections sweep, ceil(G0 / P) group keys plus k P gs re-read logits,
+// among those with both counts <= kGsMaxKeys; 0 when there is none.  (The int4 head's 9496
+// keys of 16 rows at k = 40 take P = 4: 2374 + 2560 keys instead of 9496 + 640.)
 __host__ __device__ inline int gs_prereduce(int64_t G0, int gs, int k) {
-  int P = 1;
-  while ((G0 + P - 1) / P > kGsMaxKeys) P *= 2;
-  return (int64_t)k * P * gs <= kGsMaxKeys ? P : 0;
+  int best = 0;
+  int64_t cost = 0;
+  for (int64_t P = 1; P <= kGsMaxKeys; P *= 2) {
+    const int64_t G = (G0 + P - 1) / P, re = (int64_t)k * P * gs;
+    if (re > kGsMaxKeys) break;
+    if (G <= kGsMaxKeys && (best == 0 || G + re < cost)) {
+      best = (int)P;
+      cost = G + re;
+    }
+  }
+  return best;
 }
 
 }  // namespace w4
