@@ -151,8 +151,9 @@ class Workload:
 
         t0 = time.time()
         self.M = synth.PREFILL_TOKENS
-        # gate and up read the same activations: both are dequantized into the two column
-        # halves of one [2048][22016] scratch (ldwt = 22016) and multiplied as one GEMM.
+        # gate and up read the same activations: stored row-concatenated (as in the decode
+        # step), they are dequantized by one call into one [2048][22016] scratch and multiplied
+        # as one GEMM.
         self.prefill_w = []  # (name, qw, s, b, scratch view, (N, K), host (q, s, b))
         self.prefill_g = []  # (name, A, scratch, C, (M, N, K), host A, [(part, column offset)])
         mats = {name: (j, n, k) for j, (name, n, k) in enumerate(synth.PREFILL_MATS)}
@@ -164,18 +165,19 @@ class Workload:
                 a_host[k] = synth.activations(self.M, k, seed=0, workload=synth.W_PREFILL, layer=100 + k)
                 self.sha[f"prefill_A_{self.M}x{k}"] = sha256_of(a_host[k])
             wt = torch.empty((k, ntot), dtype=torch.float16, device=dev)
-            col = 0
-            parts = []
+            qs, ss, bs = [], [], []
             for nm in names:
                 j, n, _ = mats[nm]
                 q, s, b = synth.w4_weights(n, k, seed=0, workload=synth.W_PREFILL, layer=j)
                 self.sha[f"prefill_{nm}_q"], self.sha[f"prefill_{nm}_s"], self.sha[f"prefill_{nm}_b"] = (
                     sha256_of(q), sha256_of(s), sha256_of(b))
-                qw = w4.w4_pack(torch.from_numpy(q).to(dev))
-                self.prefill_w.append((nm, qw, torch.from_numpy(s).to(dev), torch.from_numpy(b).to(dev),
-                                       wt[:, col:col + n], (n, k), (q, s, b)))
-                parts.append((nm, col))
-                col += n
+                qs.append(q), ss.append(s), bs.append(b)
+            q, s, b = np.concatenate(qs), np.concatenate(ss), np.concatenate(bs)
+            qw = w4.w4_pack(torch.from_numpy(q).to(dev))
+            nm = "|".join(names)
+            self.prefill_w.append((nm, qw, torch.from_numpy(s).to(dev), torch.from_numpy(b).to(dev), wt,
+                                   (ntot, k), (q, s, b)))
+            parts = [(nm, 0)]
             c = torch.empty((self.M, ntot), dtype=torch.float32, device=dev)
             self.prefill_g.append(("|".join(names), torch.from_numpy(a_host[k]).to(dev), wt, c, (self.M, ntot, k),
                                    a_host[k], parts))
