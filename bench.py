@@ -438,10 +438,12 @@ def small_m_groups(torch, np, w4, synth):
             x = torch.from_numpy(synth.activations(m, k, seed=0, workload=wk,
                                                    layer=100 * cfg + 50 + shapes[grp[0]][0])).cuda()
             y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+            ws = torch.empty(max(16, w4.gemv_workspace_bytes(m, n, k)), dtype=torch.uint8, device="cuda")
             qw0, s0, b0 = w4.w4_pack(torch.from_numpy(q).cuda()), torch.from_numpy(sc).cuda(), torch.from_numpy(b).cuda()
             mats = [(qw0, s0, b0)] + [(qw0.clone(), s0.clone(), b0.clone()) for _ in range(COUNTER_REPS - 1)]
             groups[("w4_gemv", m, n, k)] = {"bytes": gemv_bytes(m, n, k), "flops": 0,
-                                            "fns": [lambda t=t, x=x, y=y: w4.w4_gemv(t[0], t[1], t[2], x, out=y)
+                                            "fns": [lambda t=t, x=x, y=y, ws=ws: w4.w4_gemv(t[0], t[1], t[2], x, out=y,
+                                                                                             workspace=ws)
                                                     for t in mats]}
     return groups
 
@@ -747,10 +749,11 @@ def small_m(torch, np, w4, synth, oracle, reps=5):
             mats = [(qw0, s0, b0)] + [(qw0.clone(), s0.clone(), None if sym else b0.clone()) for _ in range(copies - 1)]
             x = torch.from_numpy(x_host).cuda()
             y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+            ws = torch.empty(max(16, w4.gemv_workspace_bytes(m, n, k)), dtype=torch.uint8, device="cuda")
             if sym:
-                fns = [lambda t=t: w4.w4_gemv_sym128(t[0], t[1], x, out=y) for t in mats]
+                fns = [lambda t=t: w4.w4_gemv_sym128(t[0], t[1], x, out=y, workspace=ws) for t in mats]
             else:
-                fns = [lambda t=t: w4.w4_gemv(t[0], t[1], t[2], x, out=y) for t in mats]
+                fns = [lambda t=t: w4.w4_gemv(t[0], t[1], t[2], x, out=y, workspace=ws) for t in mats]
             graph = capture(torch, lambda: [f() for f in fns])
             graph.replay()
             stream = torch.cuda.current_stream()

@@ -97,7 +97,11 @@ int w4_quantize(const uint16_t* w, int64_t ldw, uint32_t* qw, uint16_t* scales, 
  * Requires 1 <= M <= 16, N >= 1, K >= 64, K % 64 == 0, ldx >= K, ldy >= N, ldx % 8 == 0;
  * qw, scales, biases, x 16-byte aligned; y 4-byte aligned.  The result is deterministic;
  * per output it is within 2e-3 * sum_k |w[n][k] x[m][k]| of the exact sum.
- * Workspace: currently none (required size 0); ws/ws_bytes may be NULL.
+ * Workspace (query it: ws = NULL and ws_bytes set returns the size): 0 for most shapes, when
+ * ws/ws_bytes may be NULL; on the matrix-core path (5 <= M, or M = 3..4 with K > 16384) rows
+ * of K >= 6144 elements that would give at most 128 workgroups (N <= 2048 rows, e.g. the
+ * 2048 x 6144 and 2048 x 11008 down projections) split K two ways across workgroups and need
+ * 2 * M * N * 4 bytes for the partial sums, 16-byte aligned.  Contents need no initialisation.
  */
 int w4_gemv(const uint32_t* qw, const uint16_t* scales, const uint16_t* biases,
             const uint16_t* x, int64_t ldx, float* y, int64_t ldy,
@@ -121,12 +125,14 @@ int w4_dequant_f16_t(const uint32_t* qw, const uint16_t* scales, const uint16_t*
  * "Appendix: the remaining gap, itemized"), read as
  *   w[n][k] = s[n][k/128] * (q[n][k] - 8)      (zero point 8, no bias),
  * with the same packed codes as above and scales f16 [N][K/128].  These two calls are
- * w4_gemv and w4_dequant_f16_t for that format: same arguments without the biases, same
- * requirements plus K % 128 == 0; the dequant rounds s (q - 8) once (an exact zero is +0)
- * and is bit-exact; the GEMV meets the same per-output bound.  No workspace.
+ * w4_gemv and w4_dequant_f16_t for that format: same arguments without the biases (the GEMV
+ * takes w4_gemv's workspace, of the same size for the same M, N, K), same requirements plus
+ * K % 128 == 0; the dequant rounds s (q - 8) once (an exact zero is +0) and is bit-exact;
+ * the GEMV meets the same per-output bound.
  */
 int w4_gemv_sym128(const uint32_t* qw, const uint16_t* scales, const uint16_t* x, int64_t ldx,
-                   float* y, int64_t ldy, int64_t M, int64_t N, int64_t K, w4_stream_t stream);
+                   float* y, int64_t ldy, int64_t M, int64_t N, int64_t K, void* ws, size_t* ws_bytes,
+                   w4_stream_t stream);
 int w4_dequant_f16_t_sym128(const uint32_t* qw, const uint16_t* scales, uint16_t* wt, int64_t ldwt,
                             int64_t N, int64_t K, w4_stream_t stream);
 

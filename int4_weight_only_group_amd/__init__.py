@@ -12,6 +12,7 @@ w[n][k] = scales[n][k//64] * q[n][k] + biases[n][k//64].
 from __future__ import annotations
 
 import ctypes
+import functools
 
 import torch
 
@@ -124,8 +125,12 @@ def _w4_args(qw, scales, biases):
 
 
 def w4_gemv(qw: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, x: torch.Tensor,
-            out: torch.Tensor | None = None) -> torch.Tensor:
-    """y[m][n] = sum_k w[n][k] x[m][k] for x float16 [M][K] (M <= 16) -> float32 [M][N]."""
+            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y[m][n] = sum_k w[n][k] x[m][k] for x float16 [M][K] (M <= 16) -> float32 [M][N].
+
+    Shapes that split K across workgroups need a workspace (see gemv_workspace_bytes); one is
+    allocated when none (or too small a one) is given.
+    """
     n, k = _w4_args(qw, scales, biases)
     _dev(x, "x", torch.float16)
     if x.dim() != 2 or x.shape[1] != k:
@@ -138,10 +143,26 @@ def w4_gemv(qw: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, x: tor
     if tuple(out.shape) != (m, n):
         raise ValueError("out must be [M][N]")
     ldy = _rowmajor(out, "out")
+    need = gemv_workspace_bytes(m, n, k)
+    ws_ptr, cap = None, None
+    if need:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        ws_ptr = workspace.data_ptr()
+        cap = ctypes.byref(ctypes.c_size_t(workspace.numel() * workspace.element_size()))
     _check("w4_gemv", lib().w4_gemv(qw.data_ptr(), scales.data_ptr(), biases.data_ptr(),
-                                    x.data_ptr(), ldx, out.data_ptr(), ldy, m, n, k, None, None,
+                                    x.data_ptr(), ldx, out.data_ptr(), ldy, m, n, k, ws_ptr, cap,
                                     _stream()))
     return out
+
+
+@functools.lru_cache(maxsize=256)
+def gemv_workspace_bytes(m: int, n: int, k: int) -> int:
+    """Workspace bytes w4_gemv needs for M rows of x and an [N][K] int4 matrix (0 for most shapes)."""
+    need = ctypes.c_size_t(0)
+    p = ctypes.c_void_p(16)
+    _check("w4_gemv", lib().w4_gemv(p, p, p, p, k, p, n, m, n, k, None, ctypes.byref(need), None))
+    return int(need.value)
 
 
 def w4_dequant_f16_t(qw: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor,
@@ -173,8 +194,11 @@ def _sym_args(qw, scales):
 
 
 def w4_gemv_sym128(qw: torch.Tensor, scales: torch.Tensor, x: torch.Tensor,
-                   out: torch.Tensor | None = None) -> torch.Tensor:
-    """Symmetric group-128 GEMV: y[m][n] = sum_k scales[n][k//128] (q[n][k] - 8) x[m][k]."""
+                   out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Symmetric group-128 GEMV: y[m][n] = sum_k scales[n][k//128] (q[n][k] - 8) x[m][k].
+
+    Takes w4_gemv's workspace (gemv_workspace_bytes; allocated when none or too small a one
+    is given)."""
     n, k = _sym_args(qw, scales)
     _dev(x, "x", torch.float16)
     if x.dim() != 2 or x.shape[1] != k:
@@ -187,8 +211,15 @@ def w4_gemv_sym128(qw: torch.Tensor, scales: torch.Tensor, x: torch.Tensor,
     if tuple(out.shape) != (m, n):
         raise ValueError("out must be [M][N]")
     ldy = _rowmajor(out, "out")
+    need = gemv_workspace_bytes(m, n, k)
+    ws_ptr, cap = None, None
+    if need:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        ws_ptr = workspace.data_ptr()
+        cap = ctypes.byref(ctypes.c_size_t(workspace.numel() * workspace.element_size()))
     _check("w4_gemv_sym128", lib().w4_gemv_sym128(qw.data_ptr(), scales.data_ptr(), x.data_ptr(), ldx,
-                                                  out.data_ptr(), ldy, m, n, k, _stream()))
+                                                  out.data_ptr(), ldy, m, n, k, ws_ptr, cap, _stream()))
     return out
 
 

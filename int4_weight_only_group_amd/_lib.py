@@ -16,7 +16,7 @@ SIGNATURES = {
     "w4_gemv": (_c.c_int, [_p, _p, _p, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _sz_p, _p]),
     "w4_dequant_f16_t": (_c.c_int, [_p, _p, _p, _p, _i64, _i64, _i64, _p]),
     "w4_quantize": (_c.c_int, [_p, _i64, _p, _p, _p, _i64, _i64, _p]),
-    "w4_gemv_sym128": (_c.c_int, [_p, _p, _p, _i64, _p, _i64, _i64, _i64, _i64, _p]),
+    "w4_gemv_sym128": (_c.c_int, [_p, _p, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _sz_p, _p]),
     "w4_dequant_f16_t_sym128": (_c.c_int, [_p, _p, _p, _i64, _i64, _i64, _p]),
     "gemm_f16": (_c.c_int, [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _sz_p, _p]),
     "logits_argmax_topk": (_c.c_int, [_p, _i64, _i64, _i64, _i64, _p, _p, _p, _sz_p, _p]),

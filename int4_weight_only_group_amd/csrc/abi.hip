@@ -98,12 +98,13 @@ int w4_gemv(const uint32_t* qw, const uint16_t* scales, const uint16_t* biases, 
     if (M < 1 || M > 16 || ldx < K || ldy < N || ldx > kMaxDim || ldy > kMaxDim) return W4_ERR_SHAPE;
     if (!al16(qw) || !al16(scales) || !al16(biases) || !al16(x) || !al4(y) || ldx % 8 != 0)
       return W4_ERR_ALIGN;
-    const int w = workspace(ws, ws_bytes, 0);
+    const int w = workspace(ws, ws_bytes, w4::gemv_ws_bytes(M, N, K));
     if (w < 0) return w;
     if (w == 1) return W4_OK;
     if (int e = check_device()) return e;
     (void)hipGetLastError();
-    w4::launch_gemv(qw, scales, biases, x, ldx, y, ldy, (int)M, (int)N, (int)K, (hipStream_t)stream);
+    w4::launch_gemv(qw, scales, biases, x, ldx, y, ldy, (int)M, (int)N, (int)K,
+                    w4::gemv_ws_bytes(M, N, K) ? ws : nullptr, (hipStream_t)stream);
     return launched();
   } catch (...) {
     return W4_ERR_INTERNAL;
@@ -127,16 +128,21 @@ int w4_quantize(const uint16_t* w, int64_t ldw, uint32_t* qw, uint16_t* scales, 
 }
 
 int w4_gemv_sym128(const uint32_t* qw, const uint16_t* scales, const uint16_t* x, int64_t ldx,
-                   float* y, int64_t ldy, int64_t M, int64_t N, int64_t K, w4_stream_t stream) {
+                   float* y, int64_t ldy, int64_t M, int64_t N, int64_t K, void* ws, size_t* ws_bytes,
+                   w4_stream_t stream) {
   try {
     if (!qw || !scales || !x || !y) return W4_ERR_NULL;
     if (int e = check_w4_shape(N, K)) return e;
     if (K % 128 != 0) return W4_ERR_SHAPE;
     if (M < 1 || M > 16 || ldx < K || ldy < N || ldx > kMaxDim || ldy > kMaxDim) return W4_ERR_SHAPE;
     if (!al16(qw) || !al16(scales) || !al16(x) || !al4(y) || ldx % 8 != 0) return W4_ERR_ALIGN;
+    const int w = workspace(ws, ws_bytes, w4::gemv_ws_bytes(M, N, K));
+    if (w < 0) return w;
+    if (w == 1) return W4_OK;
     if (int e = check_device()) return e;
     (void)hipGetLastError();
-    w4::launch_gemv_sym128(qw, scales, x, ldx, y, ldy, (int)M, (int)N, (int)K, (hipStream_t)stream);
+    w4::launch_gemv_sym128(qw, scales, x, ldx, y, ldy, (int)M, (int)N, (int)K,
+                           w4::gemv_ws_bytes(M, N, K) ? ws : nullptr, (hipStream_t)stream);
     return launched();
   } catch (...) {
     return W4_ERR_INTERNAL;

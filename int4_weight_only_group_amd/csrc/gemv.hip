@@ -499,14 +499,14 @@ __global__ __launch_bounds__(NW * 64) void gemv_mf_kernel(const uint32_t* __rest
                                                           const uint16_t* __restrict__ x,
                                                           int64_t ldx, float* __restrict__ y,
                                                           int64_t ldy, int M, int N, int K,
-                                                          int U) {
+                                                          int U, float* __restrict__ part) {
   __shared__ f32x4 red[NW][RB][64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int i = lane & 15, g = lane >> 4;
   constexpr int GS = Fmt<SYM>::kChunkShift;
   const int C = K / 32, G = K / Fmt<SYM>::kGroupSize, T = (C + 3) / 4;
   const int rb0 = blockIdx.x * RB;
-  const int t0 = wv * U, tend = min(T, t0 + U);
+  const int t0 = (blockIdx.y * NW + wv) * U, tend = min(T, t0 + U);  // K-range blockIdx.y
   const int nb = (U + V - 1) / V;  // blocks per wave, the same for every wave
 
   const uint4* wrow[RB];
@@ -597,19 +597,39 @@ __global__ __launch_bounds__(NW * 64) void gemv_mf_kernel(const uint32_t* __rest
       float sum = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) sum += red[w][r][16 * gg + m][e];
-      y[(int64_t)m * ldy + n] = sum;
+      if (part)  // one K-range of several: its partial sum, added by mf_reduce_kernel
+        part[((int64_t)blockIdx.y * M + m) * N + n] = sum;
+      else
+        y[(int64_t)m * ldy + n] = sum;
     }
   }
 }
 
+// y[m][n] = the S partial sums part[s][m][n] added in split order (deterministic)
+__global__ __launch_bounds__(256) void mf_reduce_kernel(const float* __restrict__ part, float* __restrict__ y,
+                                                        int64_t ldy, int M, int N, int S) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x, MN = (int64_t)M * N;
+  if (e >= MN) return;
+  const int m = (int)(e / N), n = (int)(e - (int64_t)m * N);
+  float v = part[e];
+  for (int s = 1; s < S; ++s) v += part[s * MN + e];
+  y[(int64_t)m * ldy + n] = v;
+}
+
+// S > 1: S K-ranges on separate workgroups, partial sums in part ([S][M][N] f32), then added
 template <int NW, int RB, int V, bool SYM>
 void launch_mf(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
-               int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
+               int64_t ldx, float* y, int64_t ldy, int M, int N, int K, int S, float* part, hipStream_t st) {
   const int T = (K / 32 + 3) / 4;            // steps of 4 chunks (128 elements) per row
-  const int U = (T + NW - 1) / NW;           // steps per wave
+  const int U = (T + S * NW - 1) / (S * NW); // steps per wave
   const int grid = ((N + 15) / 16 + RB - 1) / RB;
-  hipLaunchKernelGGL((gemv_mf_kernel<NW, RB, V, SYM>), dim3(grid), dim3(NW * 64), 0, st, qw, s, b, x,
-                     ldx, y, ldy, M, N, K, U);
+  hipLaunchKernelGGL((gemv_mf_kernel<NW, RB, V, SYM>), dim3(grid, S), dim3(NW * 64), 0, st, qw, s, b, x,
+                     ldx, y, ldy, M, N, K, U, S > 1 ? part : nullptr);
+  if (S > 1) {
+    const int64_t MN = (int64_t)M * N;
+    hipLaunchKernelGGL(mf_reduce_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, st, part, y, ldy, M, N,
+                       S);
+  }
 }
 
 // ------------------------------------------------------------------ M = 1 on row slices
@@ -904,31 +924,55 @@ bool launch_gemv_m1(const uint32_t* qw, const uint16_t* s, const uint16_t* b, co
   return false;
 }
 
+// Row blocks per wave of the matrix-core path for N rows.
+int mf_rb(int N) {
+  const int nrb = (N + 15) / 16;
+  return nrb >= 768 ? 4 : nrb >= 384 ? 2 : 1;
+}
+
+// Whether (M, K) takes the matrix-core path: 5 <= M, or M = 3..4 past the row slices' 16384
+// elements (mirrors launch_gemv_fmt).
+bool uses_mf(int64_t M, int64_t K) { return M >= 5 || (M >= 3 && (K / 32 + 63) / 64 > 8); }
+
+// K-ranges on separate workgroups for the matrix-core path: long rows (K >= 6144) that give at
+// most 128 workgroups (the 2048-row down projections) run as 2 K-ranges on 256 workgroups; a
+// second launch adds the two partial sums.  Measured (graph-replayed, distinct weights; one /
+// two / four K-ranges): 2048 x 6144 at M = 16 11.8 / 9.4 / 10.1 us, 2048 x 11008 at M = 16
+// 18.0 / 13.4 / 13.8 us and at M = 8 13.8 / 11.4 / 11.5 us; the 240 workgroups of the 3840-row
+// Gemma down lose with any split (M = 8: 22.8 / 25.8 / 26.8 us).
+int mf_splits(int64_t M, int64_t N, int64_t K) {
+  if (!uses_mf(M, K) || K < 6144) return 1;
+  const int64_t grid = ((N + 15) / 16 + mf_rb((int)N) - 1) / mf_rb((int)N);
+  return grid <= 128 ? 2 : 1;
+}
+
 // Matrix-core policy (5 <= M <= 16, and M = 3..4 past 16384 elements), measured on MI355X
 // (back-to-back graph launches on distinct weights):
 // four row blocks per wave once there are >= 768 of them, two from 384, otherwise one with
 // eight waves splitting K when rows are long.  Up to 4 rows of x the row slices are ahead.
+// part: mf_splits(M, N, K) * M * N floats, or nullptr (then one K-range).
 template <bool SYM>
 void launch_gemv_mf(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
-                    int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
-  const int nrb = (N + 15) / 16;
-  if (nrb >= 768)
-    launch_mf<8, 4, 1, SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
-  else if (nrb >= 384)
-    launch_mf<8, 2, 1, SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+                    int64_t ldx, float* y, int64_t ldy, int M, int N, int K, float* part, hipStream_t st) {
+  const int S = part ? mf_splits(M, N, K) : 1;
+  const int rb = mf_rb(N);
+  if (rb == 4)
+    launch_mf<8, 4, 1, SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, S, part, st);
+  else if (rb == 2)
+    launch_mf<8, 2, 1, SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, S, part, st);
   else if (K >= 8192)
-    launch_mf<8, 1, 1, SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+    launch_mf<8, 1, 1, SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, S, part, st);
   else
-    launch_mf<4, 1, 1, SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+    launch_mf<4, 1, 1, SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, S, part, st);
 }
 
 template <bool SYM>
 void launch_gemv_fmt(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
-                     int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
+                     int64_t ldx, float* y, int64_t ldy, int M, int N, int K, float* part, hipStream_t st) {
   if (M <= 1 && launch_gemv_m1<SYM>(qw, s, b, x, y, N, K, st)) return;
   if (M >= 2 && M <= 4 && launch_gemv_rs<SYM>(M, qw, s, b, x, ldx, y, ldy, N, K, st)) return;
   if (M >= 3) {
-    launch_gemv_mf<SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+    launch_gemv_mf<SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, part, st);
     return;
   }
   if (M <= 1)
@@ -940,8 +984,13 @@ void launch_gemv_fmt(const uint32_t* qw, const uint16_t* s, const uint16_t* b, c
 }  // namespace
 
 void launch_gemv(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
-                 int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
-  launch_gemv_fmt<false>(qw, s, b, x, ldx, y, ldy, M, N, K, st);
+                 int64_t ldx, float* y, int64_t ldy, int M, int N, int K, void* ws, hipStream_t st) {
+  launch_gemv_fmt<false>(qw, s, b, x, ldx, y, ldy, M, N, K, reinterpret_cast<float*>(ws), st);
+}
+
+size_t gemv_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  const int S = mf_splits(M, N, K);
+  return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
 // The M = 1 row-slice GEMV's rows per block and slices per row (the policy of launch_gemv_rs),
@@ -974,8 +1023,8 @@ void launch_gemv_head(const uint32_t* qw, const uint16_t* s, const uint16_t* b, 
 }
 
 void launch_gemv_sym128(const uint32_t* qw, const uint16_t* s, const uint16_t* x, int64_t ldx,
-                        float* y, int64_t ldy, int M, int N, int K, hipStream_t st) {
-  launch_gemv_fmt<true>(qw, s, nullptr, x, ldx, y, ldy, M, N, K, st);
+                        float* y, int64_t ldy, int M, int N, int K, void* ws, hipStream_t st) {
+  launch_gemv_fmt<true>(qw, s, nullptr, x, ldx, y, ldy, M, N, K, reinterpret_cast<float*>(ws), st);
 }
 
 }  // namespace w4

@@ -53,14 +53,16 @@ __device__ __forceinline__ float group_sum(float v) {
 // ---------------------------------------------------------------- launchers
 void launch_pack(const uint8_t* q, uint32_t* qw, int64_t N, int64_t K, hipStream_t st);
 
+// ws: gemv_ws_bytes(M, N, K) bytes, 16-byte aligned (nullptr when that is 0)
 void launch_gemv(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
-                 int64_t ldx, float* y, int64_t ldy, int M, int N, int K, hipStream_t st);
+                 int64_t ldx, float* y, int64_t ldy, int M, int N, int K, void* ws, hipStream_t st);
+size_t gemv_ws_bytes(int64_t M, int64_t N, int64_t K);
 
 void launch_quantize(const uint16_t* w, int64_t ldw, uint32_t* qw, uint16_t* s, uint16_t* b,
                      int64_t N, int64_t K, hipStream_t st);
 // The symmetric group-128 format: w = s (q - 8), one scale per 128 elements of K, no bias.
 void launch_gemv_sym128(const uint32_t* qw, const uint16_t* s, const uint16_t* x, int64_t ldx,
-                        float* y, int64_t ldy, int M, int N, int K, hipStream_t st);
+                        float* y, int64_t ldy, int M, int N, int K, void* ws, hipStream_t st);
 void launch_dequant_t_sym128(const uint32_t* qw, const uint16_t* s, uint16_t* wt, int64_t ldwt,
                              int N, int K, hipStream_t st);
 void launch_dequant_t(const uint32_t* qw, const uint16_t* s, const uint16_t* b, uint16_t* wt,

@@ -104,7 +104,7 @@ def test_quantize_argument_errors():
 def test_sym128_argument_errors():
     lib = _lib()
     g = lambda **kw: lib.w4_gemv_sym128(kw.get("qw", P), kw.get("s", P), P, kw.get("ldx", 256), P, 8,
-                                        kw.get("M", 1), 8, kw.get("K", 256), None)
+                                        kw.get("M", 1), 8, kw.get("K", 256), None, None, None)
     assert g(qw=None) == W4_ERR_NULL
     assert g(K=192, ldx=192) == W4_ERR_SHAPE     # K % 128 != 0
     assert g(M=17) == W4_ERR_SHAPE
@@ -207,3 +207,32 @@ def test_gemm_workspace_query():
     assert need(600, 2048, 4096) == 8 * 600 * 2048 * 4      # 24 tiles, 8 slices of 8 K-tiles of 64
     assert need(600, 25608, 64) == 0                        # 202 tiles
     assert need(8, 4096, 256) == 0                          # small-M path
+
+
+def test_gemv_workspace_query_and_errors():
+    # the matrix-core GEMV splits K two ways across workgroups for rows of K >= 6144 on at most
+    # 128 workgroups; the partial sums need 2 * M * N * 4 bytes, every other shape none
+    lib = _lib()
+    A = 1 << 20
+
+    def need(m, n, k):
+        nb = ctypes.c_size_t(7)
+        assert lib.w4_gemv(A, A, A, A, k, A, n, m, n, k, None, ctypes.byref(nb), None) == W4_OK
+        return nb.value
+    assert need(16, 2048, 6144) == 2 * 16 * 2048 * 4      # 128 row blocks
+    assert need(8, 2048, 11008) == 2 * 8 * 2048 * 4
+    assert need(3, 2048, 20480) == 2 * 3 * 2048 * 4      # M = 3 past 16384 elements
+    assert need(5, 2064, 8192) == 0                      # 129 row blocks
+    assert need(8, 3840, 15360) == 0                     # 240 row blocks
+    assert need(16, 2048, 4096) == 0                     # K below 6144
+    assert need(16, 12288, 6144) == 0                    # 768 row blocks, four per wave: 192
+    assert need(1, 2048, 11008) == 0                     # M = 1: row slices
+    assert need(4, 2048, 11008) == 0                     # M = 4 within 16384: row slices
+    n = ctypes.c_size_t(need(16, 2048, 6144) - 16)
+    assert lib.w4_gemv(A, A, A, A, 6144, A, 2048, 16, 2048, 6144, A, ctypes.byref(n), None) == W4_ERR_WORKSPACE
+    assert lib.w4_gemv(A, A, A, A, 6144, A, 2048, 16, 2048, 6144, None, None, None) == W4_ERR_WORKSPACE
+    big = ctypes.c_size_t(1 << 20)
+    assert lib.w4_gemv(A, A, A, A, 6144, A, 2048, 16, 2048, 6144, A + 8, ctypes.byref(big), None) == W4_ERR_ALIGN
+    s = ctypes.c_size_t(0)
+    assert lib.w4_gemv_sym128(A, A, A, 6144, A, 2048, 16, 2048, 6144, None, ctypes.byref(s), None) == W4_OK
+    assert s.value == need(16, 2048, 6144)                # the symmetric GEMV splits the same way

@@ -361,6 +361,27 @@ def test_gemv_matrix_core_edges(w4, m, n, k):
     gemv_case(w4, m, n, k, seed=31 * n + k + m, ldx_pad=8 * (m % 2), ldy_pad=m % 5)
 
 
+# Long rows on few row blocks split K two ways across workgroups, partial sums added by a
+# second launch in split order: the 2048-row down projections (Qwen3-1.7B at M = 16, Qwen2.5-3B
+# at M = 8), a ragged one (rows past the last 16-row block, K ending mid-step, 13 rows of x)
+# and M = 3 past the row slices' 16384 elements.  Workspaces start filled with 0xFF bytes; a
+# second call must give the same bits.
+@pytest.mark.parametrize("m,n,k", [(16, 2048, 6144), (8, 2048, 11008), (13, 2000, 6208), (3, 300, 20480)])
+def test_gemv_k_split_across_workgroups(w4, m, n, k):
+    need = w4.gemv_workspace_bytes(m, n, k)
+    assert need == 2 * m * n * 4
+    q, s, b = synth.w4_weights(n, k, seed=n + k)
+    x = synth.activations(m, k, seed=m + k)
+    qw, sd, bd = upload_layer(w4, q, s, b)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    y1 = to_np(w4.w4_gemv(qw, sd, bd, dev(x), workspace=ws))
+    y2 = to_np(w4.w4_gemv(qw, sd, bd, dev(x), workspace=ws))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    y_ref, bound = oracle.gemv_ref(oracle.pack(q), s, b, x)
+    ok, worst = oracle.check_bound(y1, y_ref, bound, RTOL)
+    assert ok, worst
+
+
 def _sampled_rows(n, seed):
     rng = np.random.default_rng(seed)
     return np.unique(np.concatenate([np.arange(min(n, 8)), np.arange(max(0, n - 8), n),
