@@ -216,14 +216,14 @@ constexpr int kDmaWaves = 8;  // waves per workgroup (4 also builds: one per SIM
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// One 16-byte-per-lane LDS DMA (lds: wave-uniform LDS byte address of the 1 KB destination).
-// Issued as inline asm: through the builtin, the compiler would protect every later LDS read
-// with a wait for all DMA in flight, which serializes the K-tile pipeline; the kernel waits
-// explicitly instead (W4_SYNC).
+// One 16-byte-per-lane LDS DMA (lds: wave-uniform LDS byte address of the 1 KB destination,
+// passed in m0, which the compiler sets).  Issued as inline asm: through the builtin, the
+// compiler would protect every later LDS read with a wait for all DMA in flight, which
+// serializes the K-tile pipeline; the kernel waits explicitly instead (W4_SYNC).  The s_nop
+// gives the wait states an LDS DMA needs after an m0 write, which the compiler does not
+// insert for an asm statement.
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
-               "s"(lds)
-               : "memory", "m0");
+  asm volatile("s_nop 1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds) : "memory");
 }
 
 // wait for this wave's DMA down to n outstanding instructions and for all of its LDS reads
