@@ -181,6 +181,7 @@ class Workload:
             c = torch.empty((self.M, ntot), dtype=torch.float32, device=dev)
             self.prefill_g.append(("|".join(names), torch.from_numpy(a_host[k]).to(dev), wt, c, (self.M, ntot, k),
                                    a_host[k], parts))
+        assert [w[0] for w in self.prefill_w] == [g[0] for g in self.prefill_g]  # weight i feeds GEMM i
         self.prefill_flops = sum(2 * m * n * k for _, _, _, _, (m, n, k), _, _ in self.prefill_g)
         ws = max(w4.gemm_workspace_bytes(a, wt) for _, a, wt, _, _, _, _ in self.prefill_g)
         self.gemm_ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
@@ -199,10 +200,21 @@ class Workload:
         self.w4.logits_argmax_topk(self.logits, TOPK, idx=self.idx, val=self.val, workspace=self.topk_ws)
 
     def run_prefill(self):
-        for _, a, wt, c, _, _, parts in self.prefill_g:
-            for name, qw, s, b, view, _, _ in self.prefill_w:
-                if name in dict(parts):
-                    self.w4.w4_dequant_f16_t(qw, s, b, out=view)
+        # each weight is dequantized once; the next weight's dequant rides in the launch of the
+        # current GEMM (gemm_f16_dequant_next: in the CUs its last round of tiles leaves idle)
+        _, qw, s, b, view, _, _ = self.prefill_w[0]
+        self.w4.w4_dequant_f16_t(qw, s, b, out=view)
+        for i, (_, a, wt, c, _, _, _) in enumerate(self.prefill_g):
+            if i + 1 < len(self.prefill_w):
+                _, qw, s, b, view, _, _ = self.prefill_w[i + 1]
+                self.w4.gemm_f16_dequant_next(a, wt, qw, s, b, out=c, wt=view, workspace=self.gemm_ws)
+            else:
+                self.w4.gemm_f16(a, wt, out=c, workspace=self.gemm_ws)
+
+    def run_prefill_sequential(self):
+        # the same work as four launches: dequant, GEMM, dequant, GEMM
+        for (_, qw, s, b, view, _, _), (_, a, wt, c, _, _, _) in zip(self.prefill_w, self.prefill_g):
+            self.w4.w4_dequant_f16_t(qw, s, b, out=view)
             self.w4.gemm_f16(a, wt, out=c, workspace=self.gemm_ws)
 
 
@@ -296,6 +308,11 @@ def kernel_groups(wl):
     for name, a, wt, c, (m, n, k), _, _ in wl.prefill_g:
         add(("gemm_f16", m, n, k), 2 * (m * k + k * n) + 4 * m * n, 2 * m * n * k,
             lambda a=a, wt=wt, c=c: wl.w4.gemm_f16(a, wt, out=c, workspace=wl.gemm_ws))
+    for i, (name, a, wt, c, (m, n, k), _, _) in enumerate(wl.prefill_g[:-1]):
+        _, qw, s, b, view, (nq, kq), _ = wl.prefill_w[i + 1]
+        add(("gemm_f16_dequant_next", m, n, k), 2 * (m * k + k * n) + 4 * m * n + nq * kq // 2 + nq * kq // 16 + 2 * nq * kq,
+            2 * m * n * k, lambda a=a, wt=wt, c=c, qw=qw, s=s, b=b, view=view:
+            wl.w4.gemm_f16_dequant_next(a, wt, qw, s, b, out=c, wt=view, workspace=wl.gemm_ws))
     add(("gemm_f16", 1, wl.V, wl.H), 2 * wl.H * wl.V + 2 * wl.H + 4 * wl.V, 2 * wl.H * wl.V,
         lambda: wl.w4.gemm_f16(wl.x_head, wl.head, out=wl.logits))
     add(("logits_argmax_topk", 1, wl.V, TOPK), 4 * wl.V, 0,
@@ -1306,6 +1323,27 @@ def main():
         check = parity_check(torch, np, wl, oracle, synth)
         log(f"parity re-check {'ok' if check['ok'] else 'FAILED'} in {time.time() - t0:.1f}s: {check}")
 
+    # The prefill as four launches (each dequant on its own, before its GEMM) in place of the
+    # step's prefill graph, timed inside the same step: what riding the next dequant in the
+    # GEMM's launch saves.
+    seq = None
+    if not args.eager:
+        gseq = capture(torch, wl.run_prefill_sequential)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            runners[0]()
+            runners[1]()
+            evs[i][0].record(stream)
+            gseq.replay()
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        ps = [evs[i][0].elapsed_time(evs[i][1]) * 1e3 for i in range(args.steps)]
+        seq = {"prefill_us": median_ci(np, ps), "prefill_tflops": round(wl.prefill_flops / float(np.median(ps)) / 1e6, 1),
+               "launches": "dequant, GEMM, dequant, GEMM (hipgraph)"}
+        del gseq
+        log(f"prefill as four launches: {seq['prefill_us']['median']} us "
+            f"(step's prefill {stats['prefill_us']['median']} us)")
+
     kt = kernel_timings(torch, wl)
     # dominant decode kernel: the GEMV shape with the largest total time per step
     per_step = {}
@@ -1405,6 +1443,7 @@ def main():
         "decode_step_gbps": decode_bytes * args.steps / (ph[0] + ph[1]) / 1e9,
         "decode_only_loop": dec,
         "stream_launched_step": eager,
+        "prefill_sequential": seq,
         "stats": stats,
         "context": ctx,
         "roofline": roofline,

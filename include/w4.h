@@ -57,7 +57,8 @@ enum {
   W4_ERR_WORKSPACE = -4, /* the workspace is too small */
   W4_ERR_DEVICE = -5,    /* no usable gfx950 device is current */
   W4_ERR_LAUNCH = -6,    /* the HIP runtime rejected a launch */
-  W4_ERR_INTERNAL = -7   /* unexpected internal failure */
+  W4_ERR_INTERNAL = -7,  /* unexpected internal failure */
+  W4_ERR_OVERLAP = -8    /* gemm_f16_dequant_next: one operation's output overlaps the other's data */
 };
 
 /* Static string describing a status code (never NULL). */
@@ -153,6 +154,26 @@ int w4_dequant_f16_t_sym128(const uint32_t* qw, const uint16_t* scales, uint16_t
  */
 int gemm_f16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C, int64_t ldc,
              int64_t M, int64_t N, int64_t K, void* ws, size_t* ws_bytes, w4_stream_t stream);
+
+/*
+ * gemm_f16_dequant_next -- one step of the prefill ("Crossing Mojo 1.0": every weight is
+ * dequantized once per prefill into the transposed f16 scratch, then the f16 GEMM runs on it):
+ * the GEMM of one weight together with the dequant of the next weight, which does not depend
+ * on it.  Results are exactly those of
+ *   gemm_f16(A, lda, B, ldb, C, ldc, M, N, K, ws, ws_bytes, stream) and
+ *   w4_dequant_f16_t(qw, scales, biases, wt, ldwt, Nq, Kq, stream)
+ * (C and wt bit for bit), with the same arguments, requirements, workspace (the GEMM's, same
+ * size query) and errors as those two calls.  When the GEMM's last round of workgroups leaves
+ * at least 32 CUs idle (e.g. 430 tiles of 320 x 256 on 256 CUs for a 1570-token gate|up
+ * projection), the dequant runs in those CUs in the same launch; otherwise the two are
+ * launched one after the other on `stream`.  The two run concurrently, so wt must not overlap
+ * A, B, C, the workspace or the dequant's own inputs, and C and the workspace must not overlap
+ * qw, scales or biases: W4_ERR_OVERLAP otherwise (checked on the host).  Deterministic.
+ */
+int gemm_f16_dequant_next(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C,
+                          int64_t ldc, int64_t M, int64_t N, int64_t K, void* ws, size_t* ws_bytes,
+                          const uint32_t* qw, const uint16_t* scales, const uint16_t* biases,
+                          uint16_t* wt, int64_t ldwt, int64_t Nq, int64_t Kq, w4_stream_t stream);
 
 /*
  * logits_argmax_topk -- on-device token selection ("Crossing Mojo 1.0": argmax/top-k on

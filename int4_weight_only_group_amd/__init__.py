@@ -19,7 +19,7 @@ import torch
 from ._lib import lib, LIB_PATH  # noqa: F401
 
 __all__ = [
-    "W4Error", "w4_pack", "w4_quantize", "w4_gemv", "w4_gemv_sym128", "w4_dequant_f16_t_sym128", "w4_dequant_f16_t", "gemm_f16", "logits_argmax_topk",
+    "W4Error", "w4_pack", "w4_quantize", "w4_gemv", "w4_gemv_sym128", "w4_dequant_f16_t_sym128", "w4_dequant_f16_t", "gemm_f16", "gemm_f16_dequant_next", "logits_argmax_topk",
     "logits_argmax_topk_noalloc", "w4_gemv_topk", "gemv_topk_workspace_bytes",
     "topk_workspace_bytes", "gemm_workspace_bytes", "status_string",
 ]
@@ -270,6 +270,49 @@ def gemm_f16(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None,
     _check("gemm_f16", lib().gemm_f16(a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc,
                                       m, n, k, ws_ptr, cap, _stream()))
     return out
+
+
+def gemm_f16_dequant_next(a: torch.Tensor, b: torch.Tensor, qw: torch.Tensor, scales: torch.Tensor,
+                          biases: torch.Tensor, out: torch.Tensor | None = None,
+                          wt: torch.Tensor | None = None,
+                          workspace: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """gemm_f16(a, b) and w4_dequant_f16_t(qw, scales, biases) in one call (the dequant rides
+    in the CUs the GEMM's last round leaves idle when there are enough): returns (C, wt)."""
+    _dev(a, "a", torch.float16)
+    _dev(b, "b", torch.float16)
+    lda, ldb = _rowmajor(a, "a"), _rowmajor(b, "b")
+    m, k = a.shape
+    k2, n = b.shape
+    if k != k2:
+        raise ValueError("inner dimensions differ")
+    nq, kq = _w4_args(qw, scales, biases)
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=a.device)
+    _dev(out, "out", torch.float32)
+    if tuple(out.shape) != (m, n):
+        raise ValueError("out must be [M][N]")
+    if wt is None:
+        wt = torch.empty((kq, nq), dtype=torch.float16, device=qw.device)
+    _dev(wt, "wt", torch.float16)
+    if tuple(wt.shape) != (kq, nq):
+        raise ValueError("wt must be [Kq][Nq]")
+    ldc, ldwt = _rowmajor(out, "out"), _rowmajor(wt, "wt")
+
+    def call(ws_ptr, cap, stream):
+        return lib().gemm_f16_dequant_next(a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc, m, n, k,
+                                           ws_ptr, cap, qw.data_ptr(), scales.data_ptr(), biases.data_ptr(),
+                                           wt.data_ptr(), ldwt, nq, kq, stream)
+
+    need = ctypes.c_size_t(0)
+    _check("gemm_f16_dequant_next", call(None, ctypes.byref(need), None))
+    ws_ptr, cap = None, None
+    if need.value:
+        if workspace is None or workspace.numel() * workspace.element_size() < need.value:
+            workspace = torch.empty(need.value, dtype=torch.uint8, device=a.device)
+        ws_ptr = workspace.data_ptr()
+        cap = ctypes.byref(ctypes.c_size_t(workspace.numel() * workspace.element_size()))
+    _check("gemm_f16_dequant_next", call(ws_ptr, cap, _stream()))
+    return out, wt
 
 
 def gemm_workspace_bytes(a: torch.Tensor, b: torch.Tensor) -> int:

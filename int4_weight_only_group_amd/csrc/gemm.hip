@@ -22,10 +22,12 @@
 //    four waves of a workgroup split K and reduce through LDS.
 //  * plain (any other shape or alignment, e.g. one strided column of a head): a workgroup
 //    per (column, 16 rows), threads split K.
+#include <atomic>
 #include <cmath>
 #include <mutex>
 #include <type_traits>
 
+#include "w4_dequant_tile.h"
 #include "w4_internal.h"
 
 namespace w4 {
@@ -70,12 +72,20 @@ struct GemmArgs {
   int M, N, K;
   int tilesM, tilesN, ksplit, kslice;
   int wide;  // C rows take 16-byte stores (C 16-byte aligned, ldc a multiple of 4)
+  int nwg;   // the GEMM's workgroups: blockIdx.x < nwg; dequant workgroups follow (SIDE)
+  // the dequant-transpose that runs in the same launch (affine format, N x K codes)
+  const uint32_t* dq_qw;
+  const uint16_t* dq_s;
+  const uint16_t* dq_b;
+  uint16_t* dq_wt;
+  int64_t dq_ld;
+  int dq_N, dq_K, dq_vec;
 };
 
 __device__ __forceinline__ void tile_of(const GemmArgs& g, int bid, int& tm, int& tn, int& split) {
   // XCD-aware order: the hardware deals workgroups round-robin to 8 XCDs; give each XCD a
   // contiguous range of the linear order below.
-  const int total = gridDim.x;
+  const int total = g.nwg;
   const int q = total / 8, rem = total % 8, xcd = bid % 8, idx = bid / 8;
   const int lin = xcd * q + min(xcd, rem) + idx;
   const int nt = g.tilesM * g.tilesN;
@@ -278,7 +288,28 @@ __device__ __forceinline__ void dma_sync(int n) {
 
 // WMW waves along M and NW / WMW along N (two along M for the prefill tiles; one for the
 // 32-row tiles of small M, where every wave takes 32 rows x 32 columns).
-template <int NW, int BMT, int WMW>
+// The dequant workgroups of a SIDE launch: workgroup j of the nside that follow the GEMM's
+// is two groups of 256 threads; group u = 2j + half takes the u-th of 2 nside equal runs of
+// consecutive dequant tiles (tile t: row block t / KT, K-tile t % KT, so a run stays on a row
+// block and re-reads its scale and bias lines from cache).  Every thread makes the same number
+// of tile calls (two barriers each); a group whose run is shorter passes live = false.
+__device__ __forceinline__ void side_dequant(const GemmArgs& g, int j, int nside, unsigned char* lds) {
+  const int tid = threadIdx.x, half = tid >> 8;
+  const int KT = dqt::k_tiles(g.dq_K), T = dqt::row_blocks(g.dq_N) * KT;
+  const int U = 2 * nside, u = 2 * j + half;
+  const int beg = (int)((int64_t)T * u / U), end = (int)((int64_t)T * (u + 1) / U);
+  const int iters = (T + U - 1) / U;  // >= end - beg for every u
+  for (int it = 0; it < iters; ++it) {
+    const int t = beg + it;
+    const bool live = t < end;
+    dqt::tile<false>(g.dq_qw, g.dq_s, g.dq_b, g.dq_wt, g.dq_ld, g.dq_N, g.dq_K, g.dq_vec != 0, live ? t / KT : 0,
+                     live ? t % KT : 0, tid & 255, live, lds + half * dqt::kLds);
+  }
+}
+
+// SIDE: workgroups from g.nwg on run side_dequant instead of a tile (whole workgroups, before
+// any barrier of the GEMM's code).
+template <int NW, int BMT, int WMW, bool SIDE = false>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_dma_kernel(GemmArgs g) {
   constexpr int WN = NW / WMW;          // waves along N
   constexpr int WTN = BN / WN;          // columns per wave
@@ -291,6 +322,14 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_dma_kernel(GemmArgs g) {
   constexpr int AW = (AI + NW - 1) / NW;  // A DMA instructions per wave, at most
   constexpr int STAGE = (BMT + BN) * DBK * 2;
   extern __shared__ __align__(16) unsigned char dlds[];
+  if constexpr (SIDE) {
+    static_assert(NW == 8 && 2 * dqt::kLds <= (size_t)DSTAGES * (BMT + BN) * DBK * 2,
+                  "two 256-thread dequant groups and their LDS");
+    if ((int)blockIdx.x >= g.nwg) {
+      side_dequant(g, (int)blockIdx.x - g.nwg, (int)gridDim.x - g.nwg, dlds);
+      return;
+    }
+  }
   int tm, tn, split;
   tile_of(g, blockIdx.x, tm, tn, split);
   const int m0 = tm * BMT, n0 = tn * BN;
@@ -770,41 +809,113 @@ GemmPath gemm_path(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ld
   return kGemmSmallM;
 }
 
+namespace {
+
+void set_dma_lds_limits() {
+  static std::once_flag lds_attr[kMaxDevices];
+  once_per_device(lds_attr, [] {
+    auto set = [](const void* f, size_t bytes) {
+      (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    };
+    set(reinterpret_cast<const void*>(gemm_mfma_kernel), kGemmLds);
+    set(reinterpret_cast<const void*>(gemm_dma_kernel<kDmaWaves, 256, 2>), dma_lds(256));
+    set(reinterpret_cast<const void*>(gemm_dma_kernel<kDmaWaves, 320, 2>), dma_lds(320));
+    set(reinterpret_cast<const void*>(gemm_dma_kernel<kDmaWaves, 32, 1>), dma_lds(32));
+    set(reinterpret_cast<const void*>(gemm_dma_kernel<kDmaWaves, 256, 2, true>), dma_lds(256));
+    set(reinterpret_cast<const void*>(gemm_dma_kernel<kDmaWaves, 320, 2, true>), dma_lds(320));
+  });
+}
+
+// The current device's compute units, queried once per device (256 on MI355X).
+int device_cus() {
+  static std::atomic<int> cus[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// The MFMA path: the tile kernel (plus nside dequant workgroups after its own, SIDE), then the
+// split-K reduce when K is split.
+void launch_mfma(GemmArgs g, const GemmPlan& p, int nside, hipStream_t st) {
+  set_dma_lds_limits();
+  const dim3 grid((unsigned)(g.nwg + nside)), block(64 * kDmaWaves);
+  const bool dma = g.K % DBK == 0;
+  if (nside > 0 && p.bm == 320)
+    hipLaunchKernelGGL((gemm_dma_kernel<kDmaWaves, 320, 2, true>), grid, block, dma_lds(320), st, g);
+  else if (nside > 0)
+    hipLaunchKernelGGL((gemm_dma_kernel<kDmaWaves, 256, 2, true>), grid, block, dma_lds(256), st, g);
+  else if (dma && p.bm == 32)
+    hipLaunchKernelGGL((gemm_dma_kernel<kDmaWaves, 32, 1>), grid, block, dma_lds(32), st, g);
+  else if (dma && p.bm == 320)
+    hipLaunchKernelGGL((gemm_dma_kernel<kDmaWaves, 320, 2>), grid, block, dma_lds(320), st, g);
+  else if (dma)
+    hipLaunchKernelGGL((gemm_dma_kernel<kDmaWaves, 256, 2>), grid, block, dma_lds(256), st, g);
+  else
+    hipLaunchKernelGGL(gemm_mfma_kernel, grid, dim3(256), kGemmLds, st, g);
+  if (p.ksplit > 1) {
+    const int64_t MN4 = (int64_t)g.M * g.N / 4;
+    int64_t blocks = (MN4 + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                       reinterpret_cast<const float*>(g.ws), g.C, g.ldc, g.M, g.N, p.ksplit, g.wide);
+  }
+}
+
+GemmArgs mfma_args(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C, int64_t ldc,
+                   int M, int N, int K, void* ws, const GemmPlan& p) {
+  GemmArgs g{};
+  g.A = A;
+  g.B = B;
+  g.C = C;
+  g.ws = reinterpret_cast<float*>(ws);
+  g.lda = lda;
+  g.ldb = ldb;
+  g.ldc = ldc;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.tilesM = p.tilesM;
+  g.tilesN = p.tilesN;
+  g.ksplit = p.ksplit;
+  g.kslice = p.kslice;
+  g.wide = aligned16(C) && ldc % 4 == 0;
+  g.nwg = p.tilesM * p.tilesN * p.ksplit;
+  return g;
+}
+
+// Fewest CUs left idle by the last round of GEMM workgroups for a dequant to ride along.
+constexpr int kMinSide = 32;
+
+}  // namespace
+
+int gemm_side_workgroups(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M,
+                         int64_t N, int64_t K, int cus) {
+  if (gemm_path(A, lda, B, ldb, M, N, K) != kGemmMfma || K % DBK != 0) return 0;
+  const GemmPlan p = choose_plan(M, N, K);
+  if (p.bm != 256 && p.bm != 320) return 0;
+  // one GEMM workgroup per CU (the DMA ring holds 128 or 144 KB of LDS)
+  const int nwg = p.tilesM * p.tilesN * p.ksplit;
+  const int idle = (nwg + cus - 1) / cus * cus - nwg;
+  return idle >= kMinSide ? idle : 0;
+}
+
 void launch_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C,
                  int64_t ldc, int M, int N, int K, void* ws, hipStream_t st) {
   switch (gemm_path(A, lda, B, ldb, M, N, K)) {
     case kGemmMfma: {
-      static std::once_flag lds_attr[kMaxDevices];
-      once_per_device(lds_attr, [] {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_mfma_kernel),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_dma_kernel<kDmaWaves, 256, 2>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)dma_lds(256));
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_dma_kernel<kDmaWaves, 320, 2>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)dma_lds(320));
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_dma_kernel<kDmaWaves, 32, 1>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)dma_lds(32));
-      });
       const GemmPlan p = choose_plan(M, N, K);
-      const int wide = aligned16(C) && ldc % 4 == 0;
-      GemmArgs g{A, B, C, reinterpret_cast<float*>(ws), lda, ldb, ldc, M, N, K,
-                 p.tilesM, p.tilesN, p.ksplit, p.kslice, wide};
-      const dim3 grid((unsigned)(p.tilesM * p.tilesN * p.ksplit));
-      if (K % DBK == 0 && p.bm == 32)
-        hipLaunchKernelGGL((gemm_dma_kernel<kDmaWaves, 32, 1>), grid, dim3(64 * kDmaWaves), dma_lds(32), st, g);
-      else if (K % DBK == 0 && p.bm == 320)
-        hipLaunchKernelGGL((gemm_dma_kernel<kDmaWaves, 320, 2>), grid, dim3(64 * kDmaWaves), dma_lds(320), st, g);
-      else if (K % DBK == 0)
-        hipLaunchKernelGGL((gemm_dma_kernel<kDmaWaves, 256, 2>), grid, dim3(64 * kDmaWaves), dma_lds(256), st, g);
-      else
-        hipLaunchKernelGGL(gemm_mfma_kernel, grid, dim3(256), kGemmLds, st, g);
-      if (p.ksplit > 1) {
-        const int64_t MN4 = (int64_t)M * N / 4;
-        int64_t blocks = (MN4 + 255) / 256;
-        if (blocks > 4096) blocks = 4096;
-        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
-                           reinterpret_cast<const float*>(ws), C, ldc, M, N, p.ksplit, wide);
-      }
+      launch_mfma(mfma_args(A, lda, B, ldb, C, ldc, M, N, K, ws, p), p, 0, st);
       break;
     }
     case kGemmSmallM: {
@@ -823,6 +934,32 @@ void launch_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
       hipLaunchKernelGGL(gemm_plain_kernel, grid, dim3(256), 0, st, A, lda, B, ldb, C, ldc, M, N, K);
     }
   }
+}
+
+}  // namespace w4
+
+namespace w4 {
+
+void launch_gemm_dequant(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C, int64_t ldc,
+                         int M, int N, int K, void* ws, const uint32_t* qw, const uint16_t* s, const uint16_t* b,
+                         uint16_t* wt, int64_t ldwt, int Nq, int Kq, hipStream_t st) {
+  const int nside = gemm_side_workgroups(A, lda, B, ldb, M, N, K, device_cus());
+  if (nside == 0) {
+    launch_gemm(A, lda, B, ldb, C, ldc, M, N, K, ws, st);
+    launch_dequant_t(qw, s, b, wt, ldwt, Nq, Kq, st);
+    return;
+  }
+  const GemmPlan p = choose_plan(M, N, K);
+  GemmArgs g = mfma_args(A, lda, B, ldb, C, ldc, M, N, K, ws, p);
+  g.dq_qw = qw;
+  g.dq_s = s;
+  g.dq_b = b;
+  g.dq_wt = wt;
+  g.dq_ld = ldwt;
+  g.dq_N = Nq;
+  g.dq_K = Kq;
+  g.dq_vec = ldwt % 8 == 0 && aligned16(wt);  // 16-byte stores need 16-byte aligned rows
+  launch_mfma(g, p, nside, st);
 }
 
 }  // namespace w4

@@ -236,3 +236,55 @@ def test_gemv_workspace_query_and_errors():
     s = ctypes.c_size_t(0)
     assert lib.w4_gemv_sym128(A, A, A, 6144, A, 2048, 16, 2048, 6144, None, ctypes.byref(s), None) == W4_OK
     assert s.value == need(16, 2048, 6144)                # the symmetric GEMV splits the same way
+
+
+def test_gemm_dequant_next_argument_errors_and_overlap():
+    # gemm_f16_dequant_next: gemm_f16's and w4_dequant_f16_t's checks, the GEMM's workspace
+    # query, and overlaps between one operation's outputs and the other's data (host-side)
+    lib = _lib()
+    W4_ERR_OVERLAP = -8
+    GB = 1 << 30
+    base = dict(A=1 * GB, lda=64, B=2 * GB, ldb=64, C=3 * GB, ldc=64, M=16, N=64, K=64, ws=None, wsb=None,
+                qw=4 * GB, s=5 * GB, b=6 * GB, wt=7 * GB, ldwt=128, Nq=128, Kq=256)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return lib.gemm_f16_dequant_next(a["A"], a["lda"], a["B"], a["ldb"], a["C"], a["ldc"], a["M"], a["N"],
+                                         a["K"], a["ws"], a["wsb"], a["qw"], a["s"], a["b"], a["wt"], a["ldwt"],
+                                         a["Nq"], a["Kq"], None)
+    assert call(A=None) == W4_ERR_NULL
+    assert call(wt=None) == W4_ERR_NULL
+    assert call(b=None) == W4_ERR_NULL
+    assert call(M=0) == W4_ERR_SHAPE
+    assert call(lda=32) == W4_ERR_SHAPE
+    assert call(Kq=96) == W4_ERR_SHAPE
+    assert call(ldwt=100) == W4_ERR_SHAPE
+    assert call(C=3 * GB + 2) == W4_ERR_ALIGN
+    assert call(qw=4 * GB + 4) == W4_ERR_ALIGN
+    assert call(wt=7 * GB + 1) == W4_ERR_ALIGN
+    # the workspace query answers with gemm_f16's size, before any overlap or device check
+    for m, n, k in ((1570, 2048, 11008), (600, 2048, 4096), (1570, 22016, 2048)):
+        got, ref = ctypes.c_size_t(0), ctypes.c_size_t(0)
+        assert call(M=m, N=n, K=k, lda=k, ldb=n, ldc=n, wsb=ctypes.byref(got)) == W4_OK
+        assert lib.gemm_f16(GB, k, GB, n, GB, n, m, n, k, None, ctypes.byref(ref), None) == W4_OK
+        assert got.value == ref.value
+    small = ctypes.c_size_t(16)
+    assert call(M=600, N=2048, K=4096, lda=4096, ldb=2048, ldc=2048, ws=8 * GB,
+                wsb=ctypes.byref(small)) == W4_ERR_WORKSPACE
+    # wt [256][128] f16 = 64 KiB; C [16][64] f32 = 4 KiB; qw 16 KiB; scales/biases 1 KiB each
+    assert call(wt=1 * GB + 16) == W4_ERR_OVERLAP         # wt inside A
+    assert call(wt=2 * GB - 65536 + 16) == W4_ERR_OVERLAP  # wt's last row reaches into B
+    assert call(wt=3 * GB) == W4_ERR_OVERLAP               # wt on C
+    assert call(wt=4 * GB + 16 * 1024 - 16) == W4_ERR_OVERLAP  # wt's first bytes on qw's last
+    assert call(C=5 * GB + 1024 - 16) == W4_ERR_OVERLAP    # C's first bytes on the scales' last
+    assert call(C=6 * GB - 4096 + 16) == W4_ERR_OVERLAP    # C's last row reaches into the biases
+    need = 8 * 600 * 2048 * 4
+    big = ctypes.c_size_t(need)
+    split = dict(M=600, N=2048, K=4096, lda=4096, ldb=2048, ldc=2048, wsb=ctypes.byref(big))
+    assert call(ws=7 * GB - need + 16, **split) == W4_ERR_OVERLAP  # workspace end on wt
+    assert call(ws=4 * GB + 4096, **split) == W4_ERR_OVERLAP       # workspace over qw
+    # touching ranges do not overlap: wt right after qw's 16 KiB, C right before the scales
+    assert call(wt=4 * GB + 16 * 1024) in (W4_ERR_DEVICE, W4_OK)
+    assert call(C=5 * GB - 4096) in (W4_ERR_DEVICE, W4_OK)
+    if not _has_gpu():
+        assert call() == W4_ERR_DEVICE
