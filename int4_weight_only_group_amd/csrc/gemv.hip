@@ -616,6 +616,184 @@ __global__ __launch_bounds__(256) void mf_reduce_kernel(const float* __restrict_
   y[(int64_t)m * ldy + n] = v;
 }
 
+// Large matrices (24 MB of codes and more) at 5 <= M <= 8: the same matrix-core GEMV with each workgroup's
+// x rows over its K-range (already in the converter's pair order) and its rows' (scale | bias
+// << 16) words staged in LDS once, so that the loop issues only the weight loads (RB per step
+// instead of RB + 4 + 2 RB load instructions).  Measured at M = 8, graph-replayed over distinct
+// weights: the 30720 x 3840 gate|up 29.9 -> 24.8 us, the 3840 x 15360 down 22.2 -> 16.5 us (with
+// four K-ranges); on 4096 x 3840 and on the Qwen3 M = 16 shapes (5-13 MB) the staging does not
+// pay (6.9 -> 8.6 us on the former).  Tiles, steps, masking and the wave-order reduction are
+// those of gemv_mf_kernel; the staged x row of lane i is min(i, M - 1).
+template <int NW, int RB, int V, bool SYM>
+__global__ __launch_bounds__(NW * 64) void gemv_mfs_kernel(const uint32_t* __restrict__ qw,
+                                                           const uint16_t* __restrict__ sc,
+                                                           const uint16_t* __restrict__ bi,
+                                                           const uint16_t* __restrict__ x, int64_t ldx,
+                                                           float* __restrict__ y, int64_t ldy, int M, int N,
+                                                           int K, int U, float* __restrict__ part, int xpitch,
+                                                           int gr) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  constexpr int GS = Fmt<SYM>::kChunkShift;
+  const int C = K / 32, G = K / Fmt<SYM>::kGroupSize, T = (C + 3) / 4;
+  const int rb0 = blockIdx.x * RB;
+  const int s0 = blockIdx.y * NW * U, send = min(T, s0 + NW * U);  // this K-range's steps
+  const int c0 = 4 * s0, cend = min(C, 4 * send);                   // and chunks
+  const int g0 = c0 >> GS, ng = ((cend - 1) >> GS) - g0 + 1;        // and groups
+  unsigned char* lx = smem;                                          // [M][xpitch] bytes
+  uint32_t* lsb = reinterpret_cast<uint32_t*>(smem + M * xpitch);   // [16 RB][gr]
+  const int n8 = (cend - c0) * 4;  // 16-byte pieces of one x row in the range
+  for (int e = threadIdx.x; e < M * n8; e += NW * 64) {
+    const int m = e / n8, c8 = e - m * n8;
+    const uint4 v = *reinterpret_cast<const uint4*>(x + (int64_t)m * ldx + c0 * 32 + c8 * 8);
+    *reinterpret_cast<uint4*>(lx + m * xpitch + c8 * 16) = pair_up_cvt(v);
+  }
+  for (int e = threadIdx.x; e < 16 * RB * ng; e += NW * 64) {
+    const int r = e / ng, gg = e - r * ng;
+    const int64_t o = (int64_t)min(16 * rb0 + r, N - 1) * G + g0 + gg;
+    lsb[r * gr + gg] = (uint32_t)sc[o] | (SYM ? 0u : (uint32_t)bi[o] << 16);
+  }
+  const int t0 = s0 + wv * U, tend = min(send, t0 + U);
+  const int nb = (U + V - 1) / V;
+  const uint4* wrow[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+    wrow[r] = reinterpret_cast<const uint4*>(qw) + (int64_t)min(16 * (rb0 + r) + i, N - 1) * C;
+  const int xrow = min(i, M - 1) * xpitch;
+  auto chunk = [&](int t) { return min(4 * min(t, send - 1) + g, cend - 1); };
+  auto valid = [&](int t) { return t < tend && 4 * t + g < cend; };
+  struct Blk {
+    uint4 w[V][RB];
+  };
+  auto load = [&](int blk, Blk& B) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int c = chunk(t0 + blk * V + v);
+#pragma unroll
+      for (int r = 0; r < RB; ++r) B.w[v][r] = load_nt(wrow[r] + c);
+    }
+  };
+  f32x4 acc[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int blk, const Blk& B) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int t = t0 + blk * V + v;
+      const int c = chunk(t);
+      const uint32_t sb_on = valid(t) ? 0xFFFFFFFFu : 0u;
+      const uint4* xq = reinterpret_cast<const uint4*>(lx + xrow + (c - c0) * 64);
+      uint4 xp[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xp[j] = xq[j];
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        const uint32_t sb = lsb[(16 * r + i) * gr + (c >> GS) - g0] & sb_on;
+        const f16 sv = __builtin_bit_cast(f16, (uint16_t)(sb & 0xFFFFu));
+        const f16 bv = __builtin_bit_cast(f16, (uint16_t)(sb >> 16));
+        const h2 s2 = {sv, sv}, b2 = {bv, bv};
+        const uint32_t wd[4] = {B.w[v][r].x, B.w[v][r].y, B.w[v][r].z, B.w[v][r].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              word_operand<SYM>(wd[j], s2, b2), as_operand(xp[j].x, xp[j].y, xp[j].z, xp[j].w), acc[r], 0, 0, 0);
+      }
+    }
+  };
+  Blk A, B;
+  load(0, A);
+  __syncthreads();  // x, scales and biases staged
+  __builtin_amdgcn_sched_barrier(0);
+  int bk = 0;
+  for (; bk + 2 < nb; bk += 2) {
+    load(bk + 1, B);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(bk, A);
+    load(bk + 2, A);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(bk + 1, B);
+  }
+  if (nb - bk == 2) {
+    load(bk + 1, B);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(bk, A);
+    compute(bk + 1, B);
+  } else {
+    compute(bk, A);
+  }
+  __syncthreads();  // the staged data is dead: the reduction reuses the LDS
+  f32x4* red = reinterpret_cast<f32x4*>(smem);  // [NW][RB][64]
+#pragma unroll
+  for (int r = 0; r < RB; ++r) red[(wv * RB + r) * 64 + lane] = acc[r];
+  __syncthreads();
+  for (int o = threadIdx.x; o < RB * 256; o += NW * 64) {
+    const int e = o & 3, gg = (o >> 2) & 3, m = (o >> 4) & 15, r = o >> 8;
+    const int n = 16 * (rb0 + r) + 4 * gg + e;
+    if (m < M && n < N) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) sum += red[(w * RB + r) * 64 + 16 * gg + m][e];
+      if (part)
+        part[((int64_t)blockIdx.y * M + m) * N + n] = sum;
+      else
+        y[(int64_t)m * ldy + n] = sum;
+    }
+  }
+}
+
+// The staged kernel's launch shape: K-ranges S and LDS bytes; S = 0 when it does not apply.
+constexpr int kMfsNW = 8, kMfsRB = 2, kMfsV = 2;
+constexpr size_t kMfsMaxLds = 80 * 1024;  // two workgroups per CU
+struct MfsPlan {
+  int S, U, xpitch, gr;
+  size_t lds;
+};
+MfsPlan mfs_plan(int64_t M, int64_t N, int64_t K, bool sym) {
+  MfsPlan p{0, 0, 0, 0, 0};
+  if (M < 5 || M > 8 || N * K / 2 < ((int64_t)24 << 20)) return p;  // measured at M = 8
+  const int T = (int)((K / 32 + 3) / 4);
+  const int64_t gx = ((N + 15) / 16 + kMfsRB - 1) / kMfsRB;
+  int S = 1;  // K-ranges: about two workgroups per CU
+  while (S < 16 && gx * S * 2 <= 512) S *= 2;
+  for (; S <= 16; S *= 2) {
+    const int U = (T + S * kMfsNW - 1) / (S * kMfsNW);
+    const int rc = kMfsNW * U * 4;                   // chunks of one K-range, at most
+    const int xpitch = rc * 64 + 16;                 // 16 bytes apart in the LDS banks per x row
+    const int gr = rc / (sym ? 4 : 2) + 1;           // groups of one K-range, at most
+    size_t lds = (size_t)M * xpitch + (size_t)16 * kMfsRB * gr * 4;
+    const size_t red = (size_t)kMfsNW * kMfsRB * 64 * 16;
+    if (lds < red) lds = red;
+    if (lds <= kMfsMaxLds) {
+      p.S = (T + kMfsNW * U - 1) / (kMfsNW * U);     // no empty K-range
+      p.U = U;
+      p.xpitch = xpitch;
+      p.gr = gr;
+      p.lds = lds;
+      return p;
+    }
+  }
+  return p;
+}
+
+template <bool SYM>
+void launch_mfs(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x, int64_t ldx,
+                float* y, int64_t ldy, int M, int N, int K, const MfsPlan& p, float* part, hipStream_t st) {
+  static std::once_flag lds_attr[kMaxDevices];
+  once_per_device(lds_attr, [] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_mfs_kernel<kMfsNW, kMfsRB, kMfsV, SYM>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMfsMaxLds);
+  });
+  const int grid = ((N + 15) / 16 + kMfsRB - 1) / kMfsRB;
+  hipLaunchKernelGGL((gemv_mfs_kernel<kMfsNW, kMfsRB, kMfsV, SYM>), dim3(grid, p.S), dim3(kMfsNW * 64), p.lds, st,
+                     qw, s, b, x, ldx, y, ldy, M, N, K, p.U, p.S > 1 ? part : nullptr, p.xpitch, p.gr);
+  if (p.S > 1) {
+    const int64_t MN = (int64_t)M * N;
+    hipLaunchKernelGGL(mf_reduce_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, st, part, y, ldy, M, N,
+                       p.S);
+  }
+}
+
 // S > 1: S K-ranges on separate workgroups, partial sums in part ([S][M][N] f32), then added
 template <int NW, int RB, int V, bool SYM>
 void launch_mf(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
@@ -954,6 +1132,11 @@ int mf_splits(int64_t M, int64_t N, int64_t K) {
 template <bool SYM>
 void launch_gemv_mf(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x,
                     int64_t ldx, float* y, int64_t ldy, int M, int N, int K, float* part, hipStream_t st) {
+  const MfsPlan ps = mfs_plan(M, N, K, SYM);
+  if (ps.S == 1 || (ps.S > 1 && part)) {
+    launch_mfs<SYM>(qw, s, b, x, ldx, y, ldy, M, N, K, ps, part, st);
+    return;
+  }
   const int S = part ? mf_splits(M, N, K) : 1;
   const int rb = mf_rb(N);
   if (rb == 4)
@@ -989,7 +1172,10 @@ void launch_gemv(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const
 }
 
 size_t gemv_ws_bytes(int64_t M, int64_t N, int64_t K) {
-  const int S = mf_splits(M, N, K);
+  // the staged kernel's plan is the same for both formats except for its LDS bytes, which do not
+  // change S on the shapes it takes (checked by the affine plan, the larger one)
+  const MfsPlan ps = uses_mf(M, K) ? mfs_plan(M, N, K, false) : MfsPlan{0, 0, 0, 0, 0};
+  const int S = ps.S ? ps.S : mf_splits(M, N, K);
   return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 

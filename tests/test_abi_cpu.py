@@ -223,7 +223,10 @@ def test_gemv_workspace_query_and_errors():
     assert need(8, 2048, 11008) == 2 * 8 * 2048 * 4
     assert need(3, 2048, 20480) == 2 * 3 * 2048 * 4      # M = 3 past 16384 elements
     assert need(5, 2064, 8192) == 0                      # 129 row blocks
-    assert need(8, 3840, 15360) == 0                     # 240 row blocks
+    assert need(8, 3840, 15360) == 4 * 8 * 3840 * 4      # 28 MB of codes at M = 8: 4 staged K-ranges
+    assert need(8, 30720, 3840) == 0                     # 56 MB, 960 workgroups: one K-range
+    assert need(7, 1000, 51200) == 13 * 7 * 1000 * 4     # 13 staged K-ranges
+    assert need(16, 3840, 15360) == 0                    # M = 16: 240 row blocks, no split
     assert need(16, 2048, 4096) == 0                     # K below 6144
     assert need(16, 12288, 6144) == 0                    # 768 row blocks, four per wave: 192
     assert need(1, 2048, 11008) == 0                     # M = 1: row slices

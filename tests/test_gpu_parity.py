@@ -382,6 +382,35 @@ def test_gemv_k_split_across_workgroups(w4, m, n, k):
     assert ok, worst
 
 
+# Matrices of 24 MB of codes and more at 5 <= M <= 8 stage each workgroup's x rows and its
+# rows' scales/biases in LDS: ragged rows (the last 16-row block holds one row, in a pair of
+# blocks per wave), rows ending on a half step (K % 128 == 64), 13 K-ranges added by a second
+# launch (workspace filled with 0xFF first; a repeat must give the same bits), and the
+# symmetric group-128 format.  Strided x and y with canary columns.
+@pytest.mark.parametrize("m,n,k,sym", [
+    (5, 24001, 2112, False), (8, 24001, 2112, False), (7, 1000, 51200, False), (6, 24001, 2176, True),
+])
+def test_gemv_staged_large_matrices(w4, m, n, k, sym):
+    if sym:
+        sym_case(w4, m, n, k, seed=n + k + m, ldx_pad=8, ldy_pad=4)
+        return
+    need = w4.gemv_workspace_bytes(m, n, k)
+    q, s, b = synth.w4_weights(n, k, seed=n + k)
+    x = synth.activations(m, k, seed=m + k)
+    qw, sd, bd = upload_layer(w4, q, s, b)
+    ws = torch.full((max(need, 16),), 0xFF, dtype=torch.uint8, device="cuda")
+    xd = dev(np.pad(x, ((0, 0), (0, 8))))[:, :k]
+    yfull = torch.full((m, n + 4), 7.0, dtype=torch.float32, device="cuda")
+    w4.w4_gemv(qw, sd, bd, xd, out=yfull[:, :n], workspace=ws)
+    y1 = to_np(yfull).copy()
+    assert np.all(y1[:, n:] == 7.0), "write outside y"
+    w4.w4_gemv(qw, sd, bd, xd, out=yfull[:, :n], workspace=ws)
+    assert np.array_equal(y1.view(np.uint32), to_np(yfull).view(np.uint32))
+    y_ref, bound = oracle.gemv_ref(oracle.pack(q), s, b, x)
+    ok, worst = oracle.check_bound(y1[:, :n], y_ref, bound, RTOL)
+    assert ok, f"(M,N,K)=({m},{n},{k}) worst err/bound {worst:.3g}"
+
+
 def _sampled_rows(n, seed):
     rng = np.random.default_rng(seed)
     return np.unique(np.concatenate([np.arange(min(n, 8)), np.arange(max(0, n - 8), n),
