@@ -31,6 +31,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -431,7 +432,7 @@ def trace_for(key):
 
 
 SOURCE_OF = {"w4_gemv": "gemv.hip", "w4_dequant_f16_t": "dequant.hip", "gemm_f16": "gemm.hip",
-             "logits_argmax_topk": "topk.hip"}
+             "gemm_f16_dequant_next": "gemm.hip", "logits_argmax_topk": "topk.hip"}
 COUNTER_REPS = 3
 COPY_ELEMS = 128 << 20  # f16 elements of the validation copy (256 MiB read, 256 MiB written)
 
@@ -648,10 +649,20 @@ def traffic_from(manifest_path, read_csv, write_csv, out_path=None):
 
 
 def source_hash(*names):
+    """16 hex digits of the SHA-256 over kernel sources and the local headers they include
+    (transitively, each once, in first-include order)."""
+    csrc = os.path.join(ROOT, "int4_weight_only_group_amd", "csrc")
     h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "int4_weight_only_group_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+    todo, seen = list(names), set()
+    while todo:
+        n = todo.pop(0)
+        if n in seen:
+            continue
+        seen.add(n)
+        with open(os.path.join(csrc, n), "rb") as f:
+            data = f.read()
+        h.update(data)
+        todo += [m.decode() for m in re.findall(rb'#include "([^"/]+)"', data)]
     return h.hexdigest()[:16]
 
 
