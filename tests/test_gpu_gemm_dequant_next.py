@@ -111,3 +111,36 @@ def test_gemm_dequant_next_rejects_overlap(w4):
     with pytest.raises(w4.W4Error):
         w4.gemm_f16_dequant_next(ad, big[:k], w4.w4_pack(dev(q)), dev(s), dev(b), wt=big[k - 32:k + 32])
     assert np.array_equal(to_np(big).view(np.uint16), before.view(np.uint16))
+
+
+def test_gemm_dequant_next_graph_replays(w4):
+    # captured in a HIP graph (as the prefill phase is) and replayed three times with eager work
+    # and a synchronisation between the replays; every replay must equal the separate calls
+    m, n, k, nq, kq = 700, 40000, 96, 2048, 2048
+    ad = dev(synth.activations(m, k, seed=51))
+    bd = dev(synth.activations(k, n, seed=52))
+    q, s, b = synth.w4_weights(nq, kq, seed=53)
+    qw, sd, bd_ = w4.w4_pack(dev(q)), dev(s), dev(b)
+    c_ref = to_np(w4.gemm_f16(ad, bd)).copy()
+    wt_ref = to_np(w4.w4_dequant_f16_t(qw, sd, bd_)).view(np.uint16).copy()
+    c = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    wt = torch.empty((kq, nq), dtype=torch.float16, device="cuda")
+    ws = torch.empty(max(16, w4.gemm_workspace_bytes(ad, bd)), dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        w4.gemm_f16_dequant_next(ad, bd, qw, sd, bd_, out=c, wt=wt, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        w4.gemm_f16_dequant_next(ad, bd, qw, sd, bd_, out=c, wt=wt, workspace=ws)
+    for r in range(3):
+        c.fill_(float("nan"))
+        wt.view(torch.int16).fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        got_c, got_wt = to_np(c), to_np(wt).view(np.uint16)
+        assert np.array_equal(got_c.view(np.uint32), c_ref.view(np.uint32)), f"replay {r}: C"
+        assert np.array_equal(got_wt, wt_ref), f"replay {r}: wt"
+        w4.gemm_f16(ad[:64], bd)  # eager work between the replays
