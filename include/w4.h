@@ -165,8 +165,8 @@ int gemm_f16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, flo
  * (C and wt bit for bit), with the same arguments, requirements, workspace (the GEMM's, same
  * size query) and errors as those two calls.  When the GEMM's last round of workgroups leaves
  * at least 32 CUs idle (e.g. 430 tiles of 320 x 256 on 256 CUs for a 1570-token gate|up
- * projection), the dequant runs in those CUs in the same launch; otherwise the two are
- * launched one after the other on `stream`.  The two run concurrently, so wt must not overlap
+ * projection) and the dequant is estimated to finish within that round, it runs in those CUs
+ * in the same launch; otherwise the two are launched one after the other on `stream`.  The two run concurrently, so wt must not overlap
  * A, B, C, the workspace or the dequant's own inputs, and C and the workspace must not overlap
  * qw, scales or biases: W4_ERR_OVERLAP otherwise (checked on the host).  Deterministic.
  */

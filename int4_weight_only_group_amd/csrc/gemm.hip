@@ -894,20 +894,31 @@ GemmArgs mfma_args(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ld
   return g;
 }
 
-// Fewest CUs left idle by the last round of GEMM workgroups for a dequant to ride along.
+// Fewest CUs left idle by the last round of GEMM workgroups for a dequant to ride along, and
+// the estimates that decide whether it finishes within that round: a side group takes about
+// 4.5 us per dequant tile (measured beside a GEMM of K = 64: 18 tiles per group in 63-75 us),
+// and a GEMM tile takes at least its MFMA work at about 5 TFLOP/s per CU (the 1570-token gate|up
+// GEMM's second round: 320 x 256 x 2048 tiles in about 61 us).  Beside shorter tiles the dequant
+// would run long on a few CUs after the GEMM (75 against 44 us as two launches at K = 64).
 constexpr int kMinSide = 32;
+constexpr double kSideTileNs = 4500.0;
+constexpr double kCuFlopPerNs = 5000.0;
 
 }  // namespace
 
 int gemm_side_workgroups(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M,
-                         int64_t N, int64_t K, int cus) {
+                         int64_t N, int64_t K, int64_t Nq, int64_t Kq, int cus) {
   if (gemm_path(A, lda, B, ldb, M, N, K) != kGemmMfma || K % DBK != 0) return 0;
   const GemmPlan p = choose_plan(M, N, K);
   if (p.bm != 256 && p.bm != 320) return 0;
   // one GEMM workgroup per CU (the DMA ring holds 128 or 144 KB of LDS)
   const int nwg = p.tilesM * p.tilesN * p.ksplit;
   const int idle = (nwg + cus - 1) / cus * cus - nwg;
-  return idle >= kMinSide ? idle : 0;
+  if (idle < kMinSide) return 0;
+  const int64_t tiles = (int64_t)dqt::row_blocks((int)Nq) * dqt::k_tiles((int)Kq);
+  const int64_t iters = (tiles + 2 * idle - 1) / (2 * idle);  // tiles per side group
+  const double tile_ns = 2.0 * p.bm * BN * p.kslice / kCuFlopPerNs;
+  return (double)iters * kSideTileNs <= tile_ns ? idle : 0;
 }
 
 void launch_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C,
@@ -943,7 +954,7 @@ namespace w4 {
 void launch_gemm_dequant(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C, int64_t ldc,
                          int M, int N, int K, void* ws, const uint32_t* qw, const uint16_t* s, const uint16_t* b,
                          uint16_t* wt, int64_t ldwt, int Nq, int Kq, hipStream_t st) {
-  const int nside = gemm_side_workgroups(A, lda, B, ldb, M, N, K, device_cus());
+  const int nside = gemm_side_workgroups(A, lda, B, ldb, M, N, K, Nq, Kq, device_cus());
   if (nside == 0) {
     launch_gemm(A, lda, B, ldb, C, ldc, M, N, K, ws, st);
     launch_dequant_t(qw, s, b, wt, ldwt, Nq, Kq, st);

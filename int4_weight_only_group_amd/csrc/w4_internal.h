@@ -76,11 +76,11 @@ size_t gemm_ws_bytes(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t 
                      int64_t N, int64_t K);
 void launch_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C,
                  int64_t ldc, int M, int N, int K, void* ws, hipStream_t st);
-// Dequant workgroups that a GEMM of this shape can take beside its own (the CUs its last round
-// of workgroups leaves idle, on a device of `cus` CUs); 0: the GEMM and the dequant run as two
-// launches.
+// Dequant workgroups that a GEMM of this shape can take beside its own for an Nq x Kq dequant
+// (the CUs its last round of workgroups leaves idle on a device of `cus` CUs, when the dequant
+// is estimated to finish within that round); 0: the GEMM and the dequant run as two launches.
 int gemm_side_workgroups(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M,
-                         int64_t N, int64_t K, int cus);
+                         int64_t N, int64_t K, int64_t Nq, int64_t Kq, int cus);
 // launch_gemm and launch_dequant_t (affine format, Nq x Kq codes) in one launch when
 // gemm_side_workgroups allows it, else one after the other; same results either way.
 void launch_gemm_dequant(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C, int64_t ldc,

@@ -37,15 +37,17 @@ def to_np(t):
 
 # (M, N, K) of the GEMM, (Nq, Kq) of the dequant.  On 256 CUs: 430 workgroups of 320 x 256 with
 # 82 CUs idle in the second round (the 1570-token prefill: gate|up GEMM beside the down
-# projection's dequant); split-K (192 workgroups, 64 idle) beside a dequant of ragged N (2-byte
-# stores); 472 and 471 tiles (40 and 41 idle) beside a single tile and beside the 11008 x 2048
-# dequant (many tiles per side group); 256 tiles, 32-row tiles and the small-M path: no side
-# workgroups, two launches.
+# projection's dequant, 9 tiles per side group); split-K (192 workgroups, 64 idle) beside a
+# dequant of ragged N (2-byte stores); 472 and 471 tiles (40 and 41 idle) beside a single tile
+# and beside the 11008 x 2048 dequant (17 tiles per side group, K long enough to hide them);
+# then shapes that take two launches: the same dequant beside a short GEMM (it would not finish
+# within the last round), 256 tiles (no idle CU), 32-row tiles and the small-M path.
 CASES = [
     (1570, 22016, 2048, 2048, 11008),
     (600, 2048, 4096, 1000, 320),
     (1000, 30000, 1024, 64, 64),
-    (700, 40000, 96, 11008, 2048),
+    (700, 40000, 4096, 11008, 2048),
+    (1000, 30000, 256, 2048, 11008),
     (4096, 4096, 4096, 300, 512),
     (20, 4096, 512, 130, 256),
     (4, 1024, 512, 128, 256),
