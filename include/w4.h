@@ -176,6 +176,18 @@ int gemm_f16_dequant_next(const uint16_t* A, int64_t lda, const uint16_t* B, int
                           uint16_t* wt, int64_t ldwt, int64_t Nq, int64_t Kq, w4_stream_t stream);
 
 /*
+ * gemm_f16_dequant_next_sym128 -- the same for a next weight in the symmetric group-128 format
+ * (see w4_gemv_sym128): gemm_f16 and w4_dequant_f16_t_sym128 in one call, with their arguments,
+ * requirements (Kq % 128 == 0), workspace and errors, and the same overlap rule (scales
+ * f16 [Nq][Kq/128]).  C and wt are bit-identical to the two separate calls.
+ */
+int gemm_f16_dequant_next_sym128(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                                 float* C, int64_t ldc, int64_t M, int64_t N, int64_t K, void* ws,
+                                 size_t* ws_bytes, const uint32_t* qw, const uint16_t* scales,
+                                 uint16_t* wt, int64_t ldwt, int64_t Nq, int64_t Kq,
+                                 w4_stream_t stream);
+
+/*
  * logits_argmax_topk -- on-device token selection ("Crossing Mojo 1.0": argmax/top-k on
  * the GPU instead of downloading the logits; "What's inside the engine today": bit-exact
  * against the host reference; "engine-mlx", "Tech details": in-graph greedy argmax).

@@ -19,7 +19,7 @@ import torch
 from ._lib import lib, LIB_PATH  # noqa: F401
 
 __all__ = [
-    "W4Error", "w4_pack", "w4_quantize", "w4_gemv", "w4_gemv_sym128", "w4_dequant_f16_t_sym128", "w4_dequant_f16_t", "gemm_f16", "gemm_f16_dequant_next", "logits_argmax_topk",
+    "W4Error", "w4_pack", "w4_quantize", "w4_gemv", "w4_gemv_sym128", "w4_dequant_f16_t_sym128", "w4_dequant_f16_t", "gemm_f16", "gemm_f16_dequant_next", "gemm_f16_dequant_next_sym128", "logits_argmax_topk",
     "logits_argmax_topk_noalloc", "w4_gemv_topk", "gemv_topk_workspace_bytes",
     "topk_workspace_bytes", "gemm_workspace_bytes", "status_string",
 ]
@@ -277,7 +277,20 @@ def gemm_f16_dequant_next(a: torch.Tensor, b: torch.Tensor, qw: torch.Tensor, sc
                           wt: torch.Tensor | None = None,
                           workspace: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
     """gemm_f16(a, b) and w4_dequant_f16_t(qw, scales, biases) in one call (the dequant rides
-    in the CUs the GEMM's last round leaves idle when there are enough): returns (C, wt)."""
+    in the CUs the GEMM's last round leaves idle when it fits there): returns (C, wt)."""
+    nq, kq = _w4_args(qw, scales, biases)
+    return _gemm_dequant_next("gemm_f16_dequant_next", a, b, qw, scales, biases, nq, kq, out, wt, workspace)
+
+
+def gemm_f16_dequant_next_sym128(a: torch.Tensor, b: torch.Tensor, qw: torch.Tensor, scales: torch.Tensor,
+                                 out: torch.Tensor | None = None, wt: torch.Tensor | None = None,
+                                 workspace: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """gemm_f16(a, b) and w4_dequant_f16_t_sym128(qw, scales) in one call: returns (C, wt)."""
+    nq, kq = _sym_args(qw, scales)
+    return _gemm_dequant_next("gemm_f16_dequant_next_sym128", a, b, qw, scales, None, nq, kq, out, wt, workspace)
+
+
+def _gemm_dequant_next(fn, a, b, qw, scales, biases, nq, kq, out, wt, workspace):
     _dev(a, "a", torch.float16)
     _dev(b, "b", torch.float16)
     lda, ldb = _rowmajor(a, "a"), _rowmajor(b, "b")
@@ -285,7 +298,6 @@ def gemm_f16_dequant_next(a: torch.Tensor, b: torch.Tensor, qw: torch.Tensor, sc
     k2, n = b.shape
     if k != k2:
         raise ValueError("inner dimensions differ")
-    nq, kq = _w4_args(qw, scales, biases)
     if out is None:
         out = torch.empty((m, n), dtype=torch.float32, device=a.device)
     _dev(out, "out", torch.float32)
@@ -297,21 +309,21 @@ def gemm_f16_dequant_next(a: torch.Tensor, b: torch.Tensor, qw: torch.Tensor, sc
     if tuple(wt.shape) != (kq, nq):
         raise ValueError("wt must be [Kq][Nq]")
     ldc, ldwt = _rowmajor(out, "out"), _rowmajor(wt, "wt")
+    w4q = [qw.data_ptr(), scales.data_ptr()] + ([biases.data_ptr()] if biases is not None else [])
 
     def call(ws_ptr, cap, stream):
-        return lib().gemm_f16_dequant_next(a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc, m, n, k,
-                                           ws_ptr, cap, qw.data_ptr(), scales.data_ptr(), biases.data_ptr(),
-                                           wt.data_ptr(), ldwt, nq, kq, stream)
+        return getattr(lib(), fn)(a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc, m, n, k, ws_ptr, cap,
+                                  *w4q, wt.data_ptr(), ldwt, nq, kq, stream)
 
     need = ctypes.c_size_t(0)
-    _check("gemm_f16_dequant_next", call(None, ctypes.byref(need), None))
+    _check(fn, call(None, ctypes.byref(need), None))
     ws_ptr, cap = None, None
     if need.value:
         if workspace is None or workspace.numel() * workspace.element_size() < need.value:
             workspace = torch.empty(need.value, dtype=torch.uint8, device=a.device)
         ws_ptr = workspace.data_ptr()
         cap = ctypes.byref(ctypes.c_size_t(workspace.numel() * workspace.element_size()))
-    _check("gemm_f16_dequant_next", call(ws_ptr, cap, _stream()))
+    _check(fn, call(ws_ptr, cap, _stream()))
     return out, wt
 
 

@@ -21,6 +21,8 @@ SIGNATURES = {
     "gemm_f16": (_c.c_int, [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _sz_p, _p]),
     "gemm_f16_dequant_next": (_c.c_int, [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _sz_p,
                                          _p, _p, _p, _p, _i64, _i64, _i64, _p]),
+    "gemm_f16_dequant_next_sym128": (_c.c_int, [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _sz_p,
+                                                _p, _p, _p, _i64, _i64, _i64, _p]),
     "logits_argmax_topk": (_c.c_int, [_p, _i64, _i64, _i64, _i64, _p, _p, _p, _sz_p, _p]),
     "logits_argmax_topk_noalloc": (_c.c_int, [_p, _i64, _i64, _i64, _i64, _p, _p, _p]),
     "w4_gemv_topk": (_c.c_int, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p, _sz_p, _p]),

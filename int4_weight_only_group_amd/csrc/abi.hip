@@ -64,6 +64,45 @@ int check_w4_shape(int64_t N, int64_t K) {
   return W4_OK;
 }
 
+// gemm_f16_dequant_next and its symmetric group-128 twin (sym: no biases, K % 128 == 0, one
+// scale per 128 codes): gemm_f16's and the dequant's checks, the GEMM's workspace, then the
+// overlap checks (the two operations run at once), then one launch path.
+int gemm_dequant_next(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C, int64_t ldc, int64_t M,
+                      int64_t N, int64_t K, void* ws, size_t* ws_bytes, const uint32_t* qw, const uint16_t* scales,
+                      const uint16_t* biases, uint16_t* wt, int64_t ldwt, int64_t Nq, int64_t Kq, bool sym,
+                      w4_stream_t stream) {
+  // the GEMM's checks (gemm_f16) ...
+  if (!A || !B || !C || !qw || !scales || !wt) return W4_ERR_NULL;
+  if (M < 1 || N < 1 || K < 1 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return W4_ERR_SHAPE;
+  if (lda < K || ldb < N || ldc < N || lda > kMaxDim || ldb > kMaxDim || ldc > kMaxDim) return W4_ERR_SHAPE;
+  if (!al2(A) || !al2(B) || !al4(C)) return W4_ERR_ALIGN;
+  if (w4::gemm_path(A, lda, B, ldb, M, N, K) == w4::kGemmPlain && (M + 15) / 16 > 65535) return W4_ERR_SHAPE;
+  // ... and the dequant's (w4_dequant_f16_t, w4_dequant_f16_t_sym128)
+  if (int e = check_w4_shape(Nq, Kq)) return e;
+  if (sym && Kq % 128 != 0) return W4_ERR_SHAPE;
+  if (ldwt < Nq || ldwt > kMaxDim || Nq > 65535 * 64) return W4_ERR_SHAPE;
+  if (!al16(qw) || !al16(scales) || (!sym && !al16(biases)) || !al2(wt)) return W4_ERR_ALIGN;
+  const size_t need = w4::gemm_ws_bytes(A, lda, B, ldb, M, N, K);
+  const int w = workspace(ws, ws_bytes, need);
+  if (w < 0) return w;
+  if (w == 1) return W4_OK;
+  // the two run at once: neither's outputs may overlap the other's operands or outputs
+  const int64_t groups = Nq * (Kq / (sym ? 128 : 64));
+  const Span a = span(A, ((M - 1) * lda + K) * 2), b = span(B, ((K - 1) * ldb + N) * 2);
+  const Span c = span(C, ((M - 1) * ldc + N) * 4), wk = span(ws, need ? (int64_t)need : 0);
+  const Span q = span(qw, Nq * Kq / 2), sc = span(scales, groups * 2), bi = span(biases, sym ? 0 : groups * 2),
+             t = span(wt, ((Kq - 1) * ldwt + Nq) * 2);
+  for (const Span& x : {a, b, c, wk, q, sc, bi})
+    if (overlap(t, x)) return W4_ERR_OVERLAP;
+  for (const Span& x : {q, sc, bi})
+    if (overlap(c, x) || overlap(wk, x)) return W4_ERR_OVERLAP;
+  if (int e = check_device()) return e;
+  (void)hipGetLastError();
+  w4::launch_gemm_dequant(A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, ws, qw, scales, biases, wt, ldwt, (int)Nq,
+                          (int)Kq, sym, (hipStream_t)stream);
+  return launched();
+}
+
 }  // namespace
 
 extern "C" {
@@ -217,36 +256,21 @@ int gemm_f16_dequant_next(const uint16_t* A, int64_t lda, const uint16_t* B, int
                           const uint16_t* scales, const uint16_t* biases, uint16_t* wt, int64_t ldwt, int64_t Nq,
                           int64_t Kq, w4_stream_t stream) {
   try {
-    // the GEMM's checks (gemm_f16) ...
-    if (!A || !B || !C || !qw || !scales || !biases || !wt) return W4_ERR_NULL;
-    if (M < 1 || N < 1 || K < 1 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return W4_ERR_SHAPE;
-    if (lda < K || ldb < N || ldc < N || lda > kMaxDim || ldb > kMaxDim || ldc > kMaxDim)
-      return W4_ERR_SHAPE;
-    if (!al2(A) || !al2(B) || !al4(C)) return W4_ERR_ALIGN;
-    if (w4::gemm_path(A, lda, B, ldb, M, N, K) == w4::kGemmPlain && (M + 15) / 16 > 65535)
-      return W4_ERR_SHAPE;
-    // ... and the dequant's (w4_dequant_f16_t)
-    if (int e = check_w4_shape(Nq, Kq)) return e;
-    if (ldwt < Nq || ldwt > kMaxDim || Nq > 65535 * 64) return W4_ERR_SHAPE;
-    if (!al16(qw) || !al16(scales) || !al16(biases) || !al2(wt)) return W4_ERR_ALIGN;
-    const size_t need = w4::gemm_ws_bytes(A, lda, B, ldb, M, N, K);
-    const int w = workspace(ws, ws_bytes, need);
-    if (w < 0) return w;
-    if (w == 1) return W4_OK;
-    // the two run at once: neither's outputs may overlap the other's operands or outputs
-    const Span a = span(A, ((M - 1) * lda + K) * 2), b = span(B, ((K - 1) * ldb + N) * 2);
-    const Span c = span(C, ((M - 1) * ldc + N) * 4), wk = span(ws, need ? (int64_t)need : 0);
-    const Span q = span(qw, Nq * Kq / 2), sc = span(scales, Nq * (Kq / 64) * 2),
-               bi = span(biases, Nq * (Kq / 64) * 2), t = span(wt, ((Kq - 1) * ldwt + Nq) * 2);
-    for (const Span& x : {a, b, c, wk, q, sc, bi})
-      if (overlap(t, x)) return W4_ERR_OVERLAP;
-    for (const Span& x : {q, sc, bi})
-      if (overlap(c, x) || overlap(wk, x)) return W4_ERR_OVERLAP;
-    if (int e = check_device()) return e;
-    (void)hipGetLastError();
-    w4::launch_gemm_dequant(A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, ws, qw, scales, biases, wt, ldwt,
-                            (int)Nq, (int)Kq, (hipStream_t)stream);
-    return launched();
+    if (!biases) return W4_ERR_NULL;
+    return gemm_dequant_next(A, lda, B, ldb, C, ldc, M, N, K, ws, ws_bytes, qw, scales, biases, wt, ldwt, Nq, Kq,
+                             false, stream);
+  } catch (...) {
+    return W4_ERR_INTERNAL;
+  }
+}
+
+int gemm_f16_dequant_next_sym128(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C,
+                                 int64_t ldc, int64_t M, int64_t N, int64_t K, void* ws, size_t* ws_bytes,
+                                 const uint32_t* qw, const uint16_t* scales, uint16_t* wt, int64_t ldwt, int64_t Nq,
+                                 int64_t Kq, w4_stream_t stream) {
+  try {
+    return gemm_dequant_next(A, lda, B, ldb, C, ldc, M, N, K, ws, ws_bytes, qw, scales, nullptr, wt, ldwt, Nq, Kq,
+                             true, stream);
   } catch (...) {
     return W4_ERR_INTERNAL;
   }

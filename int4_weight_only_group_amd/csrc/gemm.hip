@@ -73,13 +73,14 @@ struct GemmArgs {
   int tilesM, tilesN, ksplit, kslice;
   int wide;  // C rows take 16-byte stores (C 16-byte aligned, ldc a multiple of 4)
   int nwg;   // the GEMM's workgroups: blockIdx.x < nwg; dequant workgroups follow (SIDE)
-  // the dequant-transpose that runs in the same launch (affine format, N x K codes)
+  // the dequant-transpose that runs in the same launch (N x K codes; dq_sym: the symmetric
+  // group-128 format, dq_b unused)
   const uint32_t* dq_qw;
   const uint16_t* dq_s;
   const uint16_t* dq_b;
   uint16_t* dq_wt;
   int64_t dq_ld;
-  int dq_N, dq_K, dq_vec;
+  int dq_N, dq_K, dq_vec, dq_sym;
 };
 
 __device__ __forceinline__ void tile_of(const GemmArgs& g, int bid, int& tm, int& tn, int& split) {
@@ -302,8 +303,13 @@ __device__ __forceinline__ void side_dequant(const GemmArgs& g, int j, int nside
   for (int it = 0; it < iters; ++it) {
     const int t = beg + it;
     const bool live = t < end;
-    dqt::tile<false>(g.dq_qw, g.dq_s, g.dq_b, g.dq_wt, g.dq_ld, g.dq_N, g.dq_K, g.dq_vec != 0, live ? t / KT : 0,
-                     live ? t % KT : 0, tid & 255, live, lds + half * dqt::kLds);
+    const int rb = live ? t / KT : 0, kt = live ? t % KT : 0;
+    if (g.dq_sym)  // the same for the whole launch
+      dqt::tile<true>(g.dq_qw, g.dq_s, g.dq_s, g.dq_wt, g.dq_ld, g.dq_N, g.dq_K, g.dq_vec != 0, rb, kt, tid & 255,
+                      live, lds + half * dqt::kLds);
+    else
+      dqt::tile<false>(g.dq_qw, g.dq_s, g.dq_b, g.dq_wt, g.dq_ld, g.dq_N, g.dq_K, g.dq_vec != 0, rb, kt, tid & 255,
+                       live, lds + half * dqt::kLds);
   }
 }
 
@@ -953,11 +959,14 @@ namespace w4 {
 
 void launch_gemm_dequant(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C, int64_t ldc,
                          int M, int N, int K, void* ws, const uint32_t* qw, const uint16_t* s, const uint16_t* b,
-                         uint16_t* wt, int64_t ldwt, int Nq, int Kq, hipStream_t st) {
+                         uint16_t* wt, int64_t ldwt, int Nq, int Kq, bool sym, hipStream_t st) {
   const int nside = gemm_side_workgroups(A, lda, B, ldb, M, N, K, Nq, Kq, device_cus());
   if (nside == 0) {
     launch_gemm(A, lda, B, ldb, C, ldc, M, N, K, ws, st);
-    launch_dequant_t(qw, s, b, wt, ldwt, Nq, Kq, st);
+    if (sym)
+      launch_dequant_t_sym128(qw, s, wt, ldwt, Nq, Kq, st);
+    else
+      launch_dequant_t(qw, s, b, wt, ldwt, Nq, Kq, st);
     return;
   }
   const GemmPlan p = choose_plan(M, N, K);
@@ -970,6 +979,7 @@ void launch_gemm_dequant(const uint16_t* A, int64_t lda, const uint16_t* B, int6
   g.dq_N = Nq;
   g.dq_K = Kq;
   g.dq_vec = ldwt % 8 == 0 && aligned16(wt);  // 16-byte stores need 16-byte aligned rows
+  g.dq_sym = sym;
   launch_mfma(g, p, nside, st);
 }
 

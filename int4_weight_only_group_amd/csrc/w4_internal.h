@@ -81,11 +81,12 @@ void launch_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
 // is estimated to finish within that round); 0: the GEMM and the dequant run as two launches.
 int gemm_side_workgroups(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M,
                          int64_t N, int64_t K, int64_t Nq, int64_t Kq, int cus);
-// launch_gemm and launch_dequant_t (affine format, Nq x Kq codes) in one launch when
-// gemm_side_workgroups allows it, else one after the other; same results either way.
+// launch_gemm and launch_dequant_t (Nq x Kq codes; sym: launch_dequant_t_sym128, b unused) in
+// one launch when gemm_side_workgroups allows it, else one after the other; same results
+// either way.
 void launch_gemm_dequant(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C, int64_t ldc,
                          int M, int N, int K, void* ws, const uint32_t* qw, const uint16_t* s, const uint16_t* b,
-                         uint16_t* wt, int64_t ldwt, int Nq, int Kq, hipStream_t st);
+                         uint16_t* wt, int64_t ldwt, int Nq, int Kq, bool sym, hipStream_t st);
 
 // Top-k: chunk size (in logits) used for rows longer than one block, and workspace bytes.
 int topk_chunk(int64_t V, int k);        // 0 when the shape is unsupported

@@ -291,3 +291,33 @@ def test_gemm_dequant_next_argument_errors_and_overlap():
     assert call(C=5 * GB - 4096) in (W4_ERR_DEVICE, W4_OK)
     if not _has_gpu():
         assert call() == W4_ERR_DEVICE
+
+
+def test_gemm_dequant_next_sym128_argument_errors_and_overlap():
+    # the symmetric group-128 twin: Kq % 128 == 0, scales [Nq][Kq/128], no biases; the same
+    # workspace query and overlap rule
+    lib = _lib()
+    W4_ERR_OVERLAP = -8
+    GB = 1 << 30
+    base = dict(A=1 * GB, lda=64, B=2 * GB, ldb=64, C=3 * GB, ldc=64, M=16, N=64, K=64, ws=None, wsb=None,
+                qw=4 * GB, s=5 * GB, wt=7 * GB, ldwt=128, Nq=128, Kq=256)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return lib.gemm_f16_dequant_next_sym128(a["A"], a["lda"], a["B"], a["ldb"], a["C"], a["ldc"], a["M"],
+                                                a["N"], a["K"], a["ws"], a["wsb"], a["qw"], a["s"], a["wt"],
+                                                a["ldwt"], a["Nq"], a["Kq"], None)
+    assert call(s=None) == W4_ERR_NULL
+    assert call(qw=None) == W4_ERR_NULL
+    assert call(Kq=192) == W4_ERR_SHAPE   # a multiple of 64 but not of 128
+    assert call(s=5 * GB + 2) == W4_ERR_ALIGN
+    got, ref = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert call(M=1570, N=2048, K=11008, lda=11008, ldb=2048, ldc=2048, wsb=ctypes.byref(got)) == W4_OK
+    assert lib.gemm_f16(GB, 11008, GB, 2048, GB, 2048, 1570, 2048, 11008, None, ctypes.byref(ref), None) == W4_OK
+    assert got.value == ref.value
+    # scales [128][2] f16 = 512 bytes: C's first bytes on their last is an overlap, right after is not
+    assert call(C=5 * GB + 512 - 16) == W4_ERR_OVERLAP
+    assert call(C=5 * GB + 512) in (W4_ERR_DEVICE, W4_OK)
+    assert call(wt=5 * GB - 65536 + 16) == W4_ERR_OVERLAP  # wt's last row on the scales
+    if not _has_gpu():
+        assert call() == W4_ERR_DEVICE

@@ -146,3 +146,25 @@ def test_gemm_dequant_next_graph_replays(w4):
         assert np.array_equal(got_c.view(np.uint32), c_ref.view(np.uint32)), f"replay {r}: C"
         assert np.array_equal(got_wt, wt_ref), f"replay {r}: wt"
         w4.gemm_f16(ad[:64], bd)  # eager work between the replays
+
+
+@pytest.mark.parametrize("m,n,k,nq,kq", [(1570, 22016, 2048, 2048, 11008), (600, 2048, 4096, 1000, 384),
+                                         (1000, 30000, 256, 2048, 11008)])
+def test_gemm_dequant_next_sym128(w4, m, n, k, nq, kq):
+    # the symmetric group-128 next weight: in the idle CUs (the prefill shape; split-K beside a
+    # ragged dequant) or as two launches (a short GEMM); bit-equal to the separate calls, wt
+    # bit-exact against the oracle
+    a = synth.activations(m, k, seed=m + 61)
+    bmat = synth.activations(k, n, seed=62)
+    q, s = synth.w4_sym128_weights(nq, kq, seed=63)
+    ad, bd = dev(a), dev(bmat)
+    qw, sd = w4.w4_pack(dev(q)), dev(s)
+    cfull = torch.full((m, n + PAD), float("nan"), dtype=torch.float32, device="cuda")
+    wfull = torch.full((kq, nq + PAD), -1, dtype=torch.int16, device="cuda").view(torch.float16)
+    w4.gemm_f16_dequant_next_sym128(ad, bd, qw, sd, out=cfull[:, :n], wt=wfull[:, :nq])
+    cf, wf = to_np(cfull), to_np(wfull).view(np.uint16)
+    assert np.all(np.isnan(cf[:, n:])) and np.all(wf[:, nq:] == 0xFFFF), "padding written"
+    assert np.array_equal(cf[:, :n].view(np.uint32), to_np(w4.gemm_f16(ad, bd)).view(np.uint32))
+    wt_sep = to_np(w4.w4_dequant_f16_t_sym128(qw, sd)).view(np.uint16)
+    assert np.array_equal(wf[:, :nq], wt_sep)
+    assert np.array_equal(wf[:, :nq], oracle.dequant_f16_t(oracle.pack(q), s, None, group=128))
