@@ -168,3 +168,29 @@ def test_gemm_dequant_next_sym128(w4, m, n, k, nq, kq):
     wt_sep = to_np(w4.w4_dequant_f16_t_sym128(qw, sd)).view(np.uint16)
     assert np.array_equal(wf[:, :nq], wt_sep)
     assert np.array_equal(wf[:, :nq], oracle.dequant_f16_t(oracle.pack(q), s, None, group=128))
+
+
+@pytest.mark.parametrize("sym", [False, True])
+def test_gemm_dequant_next_odd_scratch_pitch(w4, sym):
+    # wt rows 1001 elements apart (not 16-byte aligned): the side dequant takes its 2-byte stores;
+    # split-K GEMM (64 idle CUs) beside a ragged dequant, bit-equal to the separate calls
+    m, n, k, nq, kq = 600, 2048, 4096, 1000, 384
+    ad = dev(synth.activations(m, k, seed=71))
+    bd = dev(synth.activations(k, n, seed=72))
+    if sym:
+        q, s = synth.w4_sym128_weights(nq, kq, seed=73)
+        qw, sd = w4.w4_pack(dev(q)), dev(s)
+    else:
+        q, s, b = synth.w4_weights(nq, kq, seed=73)
+        qw, sd, bd_ = w4.w4_pack(dev(q)), dev(s), dev(b)
+    wfull = torch.full((kq, nq + 1), -1, dtype=torch.int16, device="cuda").view(torch.float16)
+    if sym:
+        c, _ = w4.gemm_f16_dequant_next_sym128(ad, bd, qw, sd, wt=wfull[:, :nq])
+        ref = oracle.dequant_f16_t(oracle.pack(q), s, None, group=128)
+    else:
+        c, _ = w4.gemm_f16_dequant_next(ad, bd, qw, sd, bd_, wt=wfull[:, :nq])
+        ref = oracle.dequant_f16_t(oracle.pack(q), s, b)
+    wf = to_np(wfull).view(np.uint16)
+    assert np.all(wf[:, nq] == 0xFFFF), "padding column written"
+    assert np.array_equal(wf[:, :nq], ref)
+    assert np.array_equal(to_np(c).view(np.uint32), to_np(w4.gemm_f16(ad, bd)).view(np.uint32))
