@@ -814,11 +814,11 @@ def small_m(torch, np, w4, synth, oracle, reps=5):
 
 def int4_head(torch, np, w4, synth, oracle, wl, reps=10):
     """The LM head stored in the int4 format (group-64 affine, [vocab][hidden] = 151936 x 2048,
-    the pages' 622 MB f16 head at 175 MB) at M = 1 with top-40: fused (w4_gemv_topk, the
-    selection in the GEMV's epilogue plus one final launch) and unfused (w4_gemv to f32 logits,
-    then logits_argmax_topk), each graph-timed over distinct copies of the head that together
-    hold at least 1 GiB.  Parity: 64 sampled logits against the fp64 oracle, the selection
-    bit-exact on the GPU's own logits, and the two paths' indices and values equal."""
+    the pages' 622 MB f16 head at 175 MB) at M = 1 with top-40: w4_gemv_topk (one call: the
+    GEMV, the group maxima, the selection) and the same as two calls (w4_gemv to f32 logits, then
+    logits_argmax_topk), each graph-timed over distinct copies of the head that together hold at
+    least 1 GiB.  Parity: 64 sampled logits against the fp64 oracle, the selection bit-exact on
+    the GPU's own logits, and the two ways' indices equal."""
     V, K = wl.V, wl.H
     q, s, b = synth.w4_weights(V, K, seed=0, workload=synth.W_DECODE, layer=990)
     qw = w4.w4_pack(torch.from_numpy(q).cuda())
@@ -834,18 +834,18 @@ def int4_head(torch, np, w4, synth, oracle, wl, reps=10):
     fval = torch.empty(TOPK, dtype=torch.float32, device="cuda")
     fws = torch.empty(w4.gemv_topk_workspace_bytes(V, K, TOPK), dtype=torch.uint8, device="cuda")
 
-    def unfused():
+    def two_calls():
         for h in heads:
             w4.w4_gemv(*h, wl.x_head, out=logits)
             w4.logits_argmax_topk(logits, TOPK, idx=idx, val=val, workspace=wl.topk_ws)
 
-    def fused():
+    def one_call():
         for h in heads:
             w4.w4_gemv_topk(*h, wl.x_head, TOPK, logits=flog, idx=fidx, val=fval, workspace=fws)
 
     stream = torch.cuda.current_stream()
     res = {}
-    for name, fn in (("unfused", unfused), ("fused", fused)):
+    for name, fn in (("two_calls", two_calls), ("one_call", one_call)):
         graph = capture(torch, fn)
         graph.replay()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -864,10 +864,10 @@ def int4_head(torch, np, w4, synth, oracle, wl, reps=10):
     ok &= oracle.check_bound(fl[:, rows], y_ref, bound)[0]
     ok &= oracle.check_topk_selection(fl, fidx.cpu().numpy()[None], fval.cpu().numpy()[None], TOPK)
     ok &= bool(np.array_equal(fidx.cpu().numpy(), idx.cpu().numpy()[0]))
-    us = res["fused"]
+    us = res["one_call"]
     return {"workload": f"int4 LM head [{V}][{K}] (affine group 64) at M=1 + top-{TOPK}", "us": round(us, 3),
             "gbps": round(nb / us / 1e3, 1), "frac_hbm": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
-            "launch": "w4_gemv_topk (fused)", "unfused_us": round(res["unfused"], 3),
+            "launch": "w4_gemv_topk (GEMV, group maxima, selection)", "two_calls_us": round(res["two_calls"], 3),
             "head_bytes": gemv_bytes(1, V, K), "copies": copies, "parity_ok": bool(ok)}
 
 

@@ -204,25 +204,24 @@ int logits_argmax_topk(const float* logits, int64_t ldl, int64_t M, int64_t V, i
                        int32_t* idx, float* val, void* ws, size_t* ws_bytes, w4_stream_t stream);
 
 /*
- * w4_gemv_topk -- the int4 LM head at decode with token selection fused into the GEMV ("The
- * inference engine -- Mojo 1.0 on Metal", "What's inside the engine today": the LM head stored
- * in int4 and token selection on the GPU, bit-exact against the host; "Crossing Mojo 1.0": the
- * logits stay on the device):
+ * w4_gemv_topk -- the int4 LM head at decode with token selection on the device, in one call
+ * ("The inference engine -- Mojo 1.0 on Metal", "What's inside the engine today": the LM head
+ * stored in int4 and token selection on the GPU, bit-exact against the host; "Crossing Mojo
+ * 1.0": the logits stay on the device):
  *   logits[v] = sum_k (s[v][k/64] * q[v][k] + b[v][k/64]) * x[k]      (one activation row)
  *   idx[0..k), val[0..k): the k largest logits, value descending, ties to the lower index,
  *   -0.0 equal to +0.0; val[r] == logits[idx[r]] bit for bit; idx[0] is the argmax.
  *   qw [V][K/8], scales/biases [V][K/64] (the weight format above, V vocabulary rows), x f16 [K],
  *   logits f32 [V] (written in full), idx int32 [k], val f32 [k].
- * Each logit is within 2e-3 * sum_k |w[v][k] x[k]| of the exact sum (as w4_gemv at M = 1), and
- * the selection is exact on the logits it writes.
- * Two launches: the M = 1 GEMV, whose workgroups also write the largest key of their rows (8 to
- * 16 rows each at K <= 2048, 2 to 4 above) to the workspace, then one workgroup that finds the
- * k-th largest of those keys (radix select), re-reads the rows of the k groups that reach it
- * and selects from them (every top-k logit lies in them).
+ * Each logit is within 2e-3 * sum_k |w[v][k] x[k]| of the exact sum, and bit-identical to
+ * w4_gemv's at M = 1; the selection is exact on the logits it writes and equals
+ * logits_argmax_topk's on them.  Launches: the M = 1 GEMV, then logits_argmax_topk's passes
+ * (for V > 4096 the largest key of every 64 logits, then one workgroup that selects from the
+ * groups whose keys can hold the top k and re-reads only those).
  * Requires 1 <= k <= 64, k <= V <= 524288, 64 <= K <= 4096, K % 64 == 0; qw, scales, biases, x
- * 16-byte aligned; logits, idx, val 4-byte aligned.  Workspace: 8 bytes per GEMV workgroup
- * (query it; 74.2 KiB for 151936 rows at K = 2048); nothing in it has to be initialised.
- * Deterministic.
+ * 16-byte aligned; logits, idx, val 4-byte aligned.  Workspace: 8 bytes per 64 logits for
+ * V > 4096, none up to 4096 (query it; 18.5 KiB for 151936 rows); nothing in it has to be
+ * initialised.  Deterministic.
  */
 int w4_gemv_topk(const uint32_t* qw, const uint16_t* scales, const uint16_t* biases, const uint16_t* x,
                  int64_t V, int64_t K, int64_t k, float* logits, int32_t* idx, float* val, void* ws,

@@ -409,7 +409,7 @@ def gemv_topk_workspace_bytes(v: int, k_dim: int, k: int) -> int:
 def w4_gemv_topk(qw: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, x: torch.Tensor, k: int,
                  logits: torch.Tensor | None = None, idx: torch.Tensor | None = None,
                  val: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
-    """The int4 LM head with fused top-k: x float16 [K] (or [1][K]) -> (logits float32 [V],
+    """The int4 LM head with top-k on the device, one call: x float16 [K] (or [1][K]) -> (logits float32 [V],
     idx int32 [k], val float32 [k]), the k largest logits, value descending, ties to the lower
     index.  One is allocated for each of the outputs and the workspace not given."""
     v, kdim = _w4_args(qw, scales, biases)
@@ -429,10 +429,13 @@ def w4_gemv_topk(qw: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, x
         outs.append(t)
     logits, idx, val = outs
     need = gemv_topk_workspace_bytes(v, kdim, k)
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
-    cap = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    ws_ptr, cap = None, None  # no workspace at all when none is needed (a null one would be a query)
+    if need:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        ws_ptr = workspace.data_ptr()
+        cap = ctypes.byref(ctypes.c_size_t(workspace.numel() * workspace.element_size()))
     _check("w4_gemv_topk", lib().w4_gemv_topk(qw.data_ptr(), scales.data_ptr(), biases.data_ptr(), x.data_ptr(),
                                               v, kdim, k, logits.data_ptr(), idx.data_ptr(), val.data_ptr(),
-                                              workspace.data_ptr(), ctypes.byref(cap), _stream()))
+                                              ws_ptr, cap, _stream()))
     return logits, idx, val

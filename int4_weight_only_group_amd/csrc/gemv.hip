@@ -31,7 +31,6 @@
 // moves; one lane stores y.
 #include "w4_dequant.h"
 #include "w4_internal.h"
-#include "w4_select.h"
 
 namespace w4 {
 
@@ -833,18 +832,12 @@ void launch_mf(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const u
 // BIG: 2 GB of codes or more -- the buffers then start at each wave's own rows (64-bit base,
 // offsets below R rows); otherwise one buffer per array and the row offset in the scalar
 // register (measured 1-2 % faster).
-// MAXK (M = 1 only): each workgroup also writes the largest selection key (w4_select.h) of its
-// rows to wgmax[blockIdx.x] (4 R rows with KS = 1, after one barrier at the end; R rows
-// otherwise) -- the first step of the int4 LM head's fused token selection.
-template <int R, int KS, bool SYM, bool BIG, int MT, bool MAXK = false>
+template <int R, int KS, bool SYM, bool BIG, int MT>
 __global__ __launch_bounds__(KS == 1 ? kWG : KS * 64) void gemv1s_kernel(
     const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc, const uint16_t* __restrict__ bi,
     const uint16_t* __restrict__ x, int64_t ldx, float* __restrict__ y, int64_t ldy, int N, int K,
-    int nblocks, uint32_t qblk, uint32_t sblk,  // bytes of codes / of scales per block of R rows
-    uint64_t* __restrict__ wgmax = nullptr) {
-  static_assert(!MAXK || MT == 1, "workgroup maxima for one activation row");
+    int nblocks, uint32_t qblk, uint32_t sblk) {  // bytes of codes / of scales per block of R rows
   __shared__ float red[KS][R * MT];
-  __shared__ uint64_t wmax[kWG / 64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int slice = KS == 1 ? 0 : wave;
@@ -879,7 +872,7 @@ __global__ __launch_bounds__(KS == 1 ? kWG : KS * 64) void gemv1s_kernel(
     bv[r] = SYM ? 0u : __builtin_amdgcn_raw_buffer_load_b16(rb, voff_s, dn * G * 2, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
-  if (!MAXK && KS == 1 && blk >= nblocks) return;  // with MAXK every wave meets the barrier below
+  if (KS == 1 && blk >= nblocks) return;
 
   uint4 xp[MT][4];
 #pragma unroll
@@ -928,28 +921,11 @@ __global__ __launch_bounds__(KS == 1 ? kWG : KS * 64) void gemv1s_kernel(
   }
   if constexpr (KS == 1) {
     if (lane == 63) {
-      uint64_t km = 0;  // below every real key
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const bool ok = blk < nblocks && blk * R + r < N;
+      for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-          if (ok) y[m * ldy + blk * R + r] = acc[r][m];
-        if constexpr (MAXK) {
-          const uint64_t kr = ok ? make_key(acc[r][0], (uint32_t)(blk * R + r)) : 0ull;
-          km = kr > km ? kr : km;
-        }
-      }
-      if constexpr (MAXK) wmax[wave] = km;
-    }
-    if constexpr (MAXK) {  // one barrier at the end: wave 0 writes the workgroup's maximum
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        uint64_t km = wmax[0];
-#pragma unroll
-        for (int w = 1; w < kWG / 64; ++w) km = wmax[w] > km ? wmax[w] : km;
-        wgmax[blockIdx.x] = km;
-      }
+          if (blk * R + r < N) y[m * ldy + blk * R + r] = acc[r][m];
     }
   } else {
     if (lane == 63) {
@@ -959,22 +935,11 @@ __global__ __launch_bounds__(KS == 1 ? kWG : KS * 64) void gemv1s_kernel(
         for (int m = 0; m < MT; ++m) red[slice][r * MT + m] = acc[r][m];
     }
     __syncthreads();
-    if (wave == 0) {
-      const bool ok = lane < R * MT && blk * R + lane / MT < N;
-      float v = red[0][min(lane, R * MT - 1)];
+    if (wave == 0 && lane < R * MT && blk * R + lane / MT < N) {
+      float v = red[0][lane];
 #pragma unroll
-      for (int j = 1; j < KS; ++j) v += red[j][min(lane, R * MT - 1)];
-      if (ok) y[(lane % MT) * ldy + blk * R + lane / MT] = v;
-      if constexpr (MAXK) {
-        const uint64_t kr = ok ? make_key(v, (uint32_t)(blk * R + lane)) : 0ull;
-        uint64_t km = kr;
-#pragma unroll
-        for (int r = 1; r < R; ++r) {
-          const uint64_t o = readlane64(kr, r);
-          km = o > km ? o : km;
-        }
-        if (lane == 0) wgmax[blockIdx.x] = km;
-      }
+      for (int j = 1; j < KS; ++j) v += red[j][lane];
+      y[(lane % MT) * ldy + blk * R + lane / MT] = v;
     }
   }
 }
@@ -1072,22 +1037,6 @@ bool launch_gemv_rs(int M, const uint32_t* qw, const uint16_t* s, const uint16_t
   return true;
 }
 
-template <int R, int KS>
-void launch_rs_max(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x, float* y, int N,
-                   int K, uint64_t* wgmax, hipStream_t st) {
-  const int nblocks = (N + R - 1) / R;
-  const int grid = KS == 1 ? (nblocks + kWG / 64 - 1) / (kWG / 64) : nblocks;
-  const uint32_t qblk = (uint32_t)R * (uint32_t)(K / 2);
-  const uint32_t sblk = (uint32_t)R * (uint32_t)(K / 64) * 2;
-  const dim3 block(KS == 1 ? kWG : KS * 64);
-  if ((int64_t)N * (K / 2) >= ((int64_t)1 << 31))
-    hipLaunchKernelGGL((gemv1s_kernel<R, KS, false, true, 1, true>), dim3(grid), block, 0, st, qw, s, b, x, (int64_t)K,
-                       y, (int64_t)N, N, K, nblocks, qblk, sblk, wgmax);
-  else
-    hipLaunchKernelGGL((gemv1s_kernel<R, KS, false, false, 1, true>), dim3(grid), block, 0, st, qw, s, b, x, (int64_t)K,
-                       y, (int64_t)N, N, K, nblocks, qblk, sblk, wgmax);
-}
-
 // M = 1: rows of more than 32 chunks (K > 1024) and up to 8 slices (K <= 16384) on row
 // slices; shorter rows on 32-lane teams of the OR-trick kernel (one chunk per lane, x in
 // LDS); longer rows fall through to the general kernel.
@@ -1177,35 +1126,6 @@ size_t gemv_ws_bytes(int64_t M, int64_t N, int64_t K) {
   const MfsPlan ps = uses_mf(M, K) ? mfs_plan(M, N, K, false) : MfsPlan{0, 0, 0, 0, 0};
   const int S = ps.S ? ps.S : mf_splits(M, N, K);
   return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
-}
-
-// The M = 1 row-slice GEMV's rows per block and slices per row (the policy of launch_gemv_rs),
-// as used for the int4 LM head: R = 4 once there are 30000 (row, slice) units, else 3 or 2.
-HeadGemvPlan head_gemv_plan(int64_t N, int64_t K) {
-  HeadGemvPlan p;
-  const int C = (int)(K / 32);
-  p.KS = (C + 63) / 64;
-  const int64_t units = N * p.KS;
-  constexpr int kSimds = 256 * 4;
-  const bool fits3 = p.KS == 1 && N > 2 * kSimds && N <= 3 * kSimds;
-  p.R = units >= 30000 ? 4 : ((units >= 16000 && p.KS == 1) || fits3) ? 3 : 2;
-  if (p.KS > 1) p.R = p.R == 3 ? 2 : p.R;  // row slices of several waves come in 2 or 4 rows
-  p.rows_per_key = p.KS == 1 ? p.R * (kWG / 64) : p.R;  // one key per workgroup
-  p.nkeys = (int)((N + p.rows_per_key - 1) / p.rows_per_key);
-  return p;
-}
-
-void launch_gemv_head(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x, float* y, int N,
-                      int K, uint64_t* wgmax, hipStream_t st) {
-  const HeadGemvPlan p = head_gemv_plan(N, K);
-  if (p.KS == 1) {
-    if (p.R == 4) launch_rs_max<4, 1>(qw, s, b, x, y, N, K, wgmax, st);
-    else if (p.R == 3) launch_rs_max<3, 1>(qw, s, b, x, y, N, K, wgmax, st);
-    else launch_rs_max<2, 1>(qw, s, b, x, y, N, K, wgmax, st);
-  } else {  // K <= 4096 for the head: two slices
-    if (p.R == 4) launch_rs_max<4, 2>(qw, s, b, x, y, N, K, wgmax, st);
-    else launch_rs_max<2, 2>(qw, s, b, x, y, N, K, wgmax, st);
-  }
 }
 
 void launch_gemv_sym128(const uint32_t* qw, const uint16_t* s, const uint16_t* x, int64_t ldx,

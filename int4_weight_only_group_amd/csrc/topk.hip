@@ -333,9 +333,10 @@ int topk_chunk(int64_t V, int k) {
   return 0;
 }
 
-// k <= 64 and rows longer than 4096 logits (up to 4M with k = 64): group maxima of 64 logits
-// (pass 1), then one selection workgroup per row (group_select_kernel); otherwise chunks of
-// topk_chunk() logits whose k best go to the workspace, then a final pass over those.
+// k <= 64 and rows longer than 4096 logits (every such shape the entry accepts: V k <= 2^26):
+// group maxima of 64 logits (pass 1), then one selection workgroup per row
+// (group_select_kernel); otherwise chunks of topk_chunk() logits whose k best go to the
+// workspace, then a final pass over those.
 bool topk_groups(int64_t V, int k) {
   return k <= 64 && V > 4096 && gs_prereduce((V + 63) / 64, 64, k) != 0;
 }
@@ -376,7 +377,7 @@ void launch_topk(const float* logits, int64_t ldl, int M, int V, int k, int32_t*
                        vec);
     const int P = gs_prereduce(G0, 64, k);
     const int G = (G0 + P - 1) / P;
-    const int cap = G > k * 64 * P ? G : k * 64 * P;
+    const int cap = gs_cap(G, 64 * P);
     hipLaunchKernelGGL(group_select_kernel<>, dim3(M), dim3(kGsThreads), gs_lds_bytes(cap), st, logits, ldl, V, k,
                        cand, G0, 64, P, cap, idx, val);
     return;

@@ -93,17 +93,9 @@ int topk_chunk(int64_t V, int k);        // 0 when the shape is unsupported
 size_t topk_ws_bytes(int64_t M, int64_t V, int k);
 void launch_topk(const float* logits, int64_t ldl, int M, int V, int k, int32_t* idx, float* val,
                  void* ws, hipStream_t st);
-// The M = 1 row-slice GEMV as the int4 LM head's first step: logits plus nkeys selection keys,
-// key j the largest of rows j rows_per_key .. + rows_per_key - 1 (one key per workgroup).
-struct HeadGemvPlan {
-  int KS, R, rows_per_key, nkeys;
-};
-HeadGemvPlan head_gemv_plan(int64_t N, int64_t K);
-void launch_gemv_head(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x, float* y, int N,
-                      int K, uint64_t* wgmax, hipStream_t st);
-
-// The int4 LM head with fused token selection (one activation row): shapes it supports, its
-// workspace bytes (the per-workgroup candidates), and the two launches.
+// The int4 LM head with token selection (one activation row): shapes it supports, its
+// workspace bytes (the GEMV's and the selection's, which run one after the other), and the
+// launches.
 bool head_topk_supported(int64_t V, int64_t K, int k);
 size_t head_topk_ws_bytes(int64_t V, int64_t K, int k);
 void launch_head_topk(const uint32_t* qw, const uint16_t* s, const uint16_t* b, const uint16_t* x, float* logits,

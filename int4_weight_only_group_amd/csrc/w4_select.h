@@ -196,18 +196,33 @@ __device__ void group_topk(const uint64_t (&key)[E], int k, unsigned char* smem,
 // Top k (k <= 64) of a row from the largest key of each group of its logits.  T, the k-th
 // largest group key, is reached by k distinct keys of the row, so the row's k-th best key is
 // >= T and so is every key of its top k; the group of such a key has a maximum >= T, i.e. it is
-// one of the k groups whose keys are >= T.  Only those groups' logits are read again; their
-// keys >= T (at least the k group maxima) hold the row's top k, which is selected from them
-// the same way.  Every step is exact; values are re-read from the logits (-0.0 stays -0.0).
+// one of the k groups whose keys are >= T.  Any lower bound L <= T keeps this true for the
+// groups whose keys are >= L: the selection takes L from the first radix digit of the group
+// keys (the digit d at which the count from the top reaches k; at least k group keys have a
+// top digit >= d, so T >= d << 52) whenever that admits few groups, and the exact T otherwise.
+// Only the admitted groups' logits are read again; their keys >= L (at least the k largest
+// group maxima) hold the row's top k, ranked directly when there are few, else selected by
+// radix select again.  Every step is exact; values come from the logits (-0.0 stays -0.0).
 constexpr int kGsThreads = 1024;   // threads of the selection workgroup
 constexpr int kGsBins = 4096;      // radix digits of 12 bits (4 bins per thread)
+constexpr int kGsHist = 64 * 65;   // ints of the histogram area (the first round pads rows to 65)
 constexpr int kGsRank = 256;       // matching keys ranked directly from this few on
 constexpr int kGsMaxKeys = 16384;  // group keys (after pre-reduction) / re-read keys in LDS
+constexpr int kGsSel = 256;        // groups admitted by the first-digit bound at most
+constexpr int kGsKeyRegs = 8;      // group keys per thread (held in registers)
+constexpr int kGsMaxGroups = kGsKeyRegs * kGsThreads;  // group keys after pre-reduction
 
-// LDS bytes of group_select_kernel for cap keys: keys, the rank pool, the histogram, 8 ints
-// and kGsThreads / 64 wave totals
+// LDS bytes of group_select_kernel for cap keys: keys, the rank pool, the histogram area, 8
+// ints and kGsThreads / 64 wave totals
 __host__ __device__ constexpr size_t gs_lds_bytes(int cap) {
-  return (size_t)(((cap + 15) & ~15) + kGsRank) * 8 + (size_t)(kGsBins + 8 + kGsThreads / 64) * 4;
+  return (size_t)(((cap + 15) & ~15) + kGsRank) * 8 + (size_t)(kGsHist + 8 + kGsThreads / 64) * 4;
+}
+
+// Keys group_select_kernel holds in LDS for G group keys of gsp logits each: the group keys,
+// and the re-read logits of up to kGsSel groups (at least k groups: k gsp <= kGsMaxKeys).
+__host__ __device__ constexpr int gs_cap(int G, int gsp) {
+  const int re = (int64_t)kGsSel * gsp < kGsMaxKeys ? kGsSel * gsp : kGsMaxKeys;
+  return G > re ? G : re;
 }
 
 // Number of keys of pool[0 .. n) larger than x; pool is padded with zeros (below every real
@@ -223,6 +238,97 @@ __device__ __forceinline__ int rank_in(const uint64_t* pool, int n, uint64_t x) 
   return r;
 }
 
+// One radix round's crossing: hist holds the counts of the current digit over the keys that
+// still match; the digit d at which the count from the top reaches kk goes to misc[0], the keys
+// in higher bins to misc[1], the keys in bin d to misc[2].  Every thread calls it; two
+// workgroup barriers, after which misc may be read.  wt: kGsThreads / 64 ints of LDS.
+__device__ inline void crossing_digit(const int* hist, int kk, int* misc, int* wt) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // thread t holds bins 4t .. 4t + 3 (one 16-byte read); counts from the top digit down
+  const int4 hv = reinterpret_cast<const int4*>(hist)[tid];
+  const int h0 = hv.x, h1 = hv.y, h2 = hv.z, h3 = hv.w;
+  const int s = h0 + h1 + h2 + h3;
+  int S = s;  // keys in bins >= 4t within this wave's range
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_down(S, o);
+    if (lane + o < 64) S += u;
+  }
+  if (lane == 0) wt[w] = S;
+  __syncthreads();
+#pragma unroll
+  for (int v = 1; v < kGsThreads / 64; ++v)
+    if (v > w) S += wt[v];  // keys in the later waves' bins
+  const int above = S - s;  // keys in bins > 4t + 3
+  if (above < kk && kk <= S) {  // exactly one thread
+    int c = above, d = 4 * tid, cnt = h0;
+    if (c + h3 >= kk) {
+      d = 4 * tid + 3, cnt = h3;
+    } else if ((c += h3) + h2 >= kk) {
+      d = 4 * tid + 2, cnt = h2;
+    } else if ((c += h2) + h1 >= kk) {
+      d = 4 * tid + 1, cnt = h1;
+    } else {
+      c += h1;
+    }
+    misc[0] = d;
+    misc[1] = c;
+    misc[2] = cnt;
+  }
+  __syncthreads();
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP lane moves: shifts by 1, 2, 4, 8
+// within each row of 16 lanes (zero from before the row start), then the running total of row
+// 0 into rows 1 and 3 and that of rows 0-1 into rows 2 and 3.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, true);
+}
+__device__ __forceinline__ int wave_prefix_sum(int v) {
+  v += dpp_i<0x111>(v);       // row_shr:1
+  v += dpp_i<0x112>(v);       // row_shr:2
+  v += dpp_i<0x114>(v);       // row_shr:4
+  v += dpp_i<0x118>(v);       // row_shr:8
+  v += dpp_i<0x142, 0xA>(v);  // row_bcast15 into rows 1 and 3
+  v += dpp_i<0x143, 0xC>(v);  // row_bcast31 into rows 2 and 3
+  return v;
+}
+
+// Slot of a key's first digit (its top 12 bits) in the first-round histogram, transposed and
+// padded: the digit of rank t from the top (t = 4095 - digit), i.e. bin i = t % 64 of lane
+// l = t / 64, sits at 65 i + l.  Lane l of one wave then reads its 64 bins at fixed offsets
+// without bank conflicts, and adjacent digits (where the counts of a row cluster) fall in
+// adjacent banks.
+__device__ __forceinline__ int first_slot(uint64_t x) {
+  const int t = 4095 - (int)(x >> 52);
+  return (t & 63) * 65 + (t >> 6);
+}
+
+// The first round's crossing, by wave 0 alone (no workgroup barrier; hist in the first_slot
+// layout): lane l sums the bins of ranks 64 l .. 64 l + 63; the lane whose prefix sum from the top first reaches kk holds the
+// crossing digit, and the same over that lane's 64 bins (one per lane) finds it.  Writes
+// misc[0] = digit, misc[1] = keys with higher digits, misc[2] = keys with this digit.  At least
+// kk keys must be counted.  Called by the 64 lanes of one wave.
+__device__ inline void first_crossing(const int* hist, int kk, int* misc) {
+  const int lane = threadIdx.x & 63;
+  int s = 0;
+#pragma unroll 16
+  for (int i = 0; i < 64; ++i) s += hist[i * 65 + lane];
+  const int pre = wave_prefix_sum(s);
+  const uint64_t hit = __ballot(pre >= kk);
+  const int L = (int)__builtin_ctzll(hit);  // hit != 0: the total is >= kk
+  const int above = __builtin_amdgcn_readlane(pre - s, L);
+  const int c = hist[lane * 65 + L];  // rank 64 L + lane
+  const int pre2 = above + wave_prefix_sum(c);
+  const uint64_t hit2 = __ballot(pre2 >= kk);
+  if (lane == (int)__builtin_ctzll(hit2)) {
+    misc[0] = 4095 - (64 * L + lane);
+    misc[1] = pre2 - c;
+    misc[2] = c;
+  }
+}
+
 // The kk-th largest (1 <= kk <= n) of the n distinct keys A[0..n) in LDS, by the whole
 // workgroup (every thread calls it; all get the result).  Radix select from the top, 12 bits a
 // round (4 in the last): a histogram of the next digit over the keys matching the digits
@@ -232,7 +338,7 @@ __device__ __forceinline__ int rank_in(const uint64_t* pool, int n, uint64_t x) 
 // ints, wt: kGsThreads / 64 ints, pool: kGsRank keys (16-key aligned), all LDS.
 __device__ inline uint64_t block_kth(const uint64_t* A, int n, int kk, int* hist, int* misc, int* wt,
                                      uint64_t* pool) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x;
   uint64_t prefix = 0, mask = 0;
   int m = n;
   // m is the same in every thread (read from LDS after a barrier); 6 rounds fix all 64 bits
@@ -248,38 +354,7 @@ __device__ inline uint64_t block_kth(const uint64_t* A, int n, int kk, int* hist
       if ((x & mask) == prefix) atomicAdd(&hist[(int)((x >> shift) & dmask)], 1);
     }
     __syncthreads();
-    // thread t holds bins 4t .. 4t + 3 (one 16-byte read); counts from the top digit down
-    const int4 hv = reinterpret_cast<const int4*>(hist)[tid];
-    const int h0 = hv.x, h1 = hv.y, h2 = hv.z, h3 = hv.w;
-    const int s = h0 + h1 + h2 + h3;
-    int S = s;  // keys in bins >= 4t within this wave's range
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int u = __shfl_down(S, o);
-      if (lane + o < 64) S += u;
-    }
-    if (lane == 0) wt[w] = S;
-    __syncthreads();
-#pragma unroll
-    for (int v = 1; v < kGsThreads / 64; ++v)
-      if (v > w) S += wt[v];  // keys in the later waves' bins
-    const int above = S - s;  // keys in bins > 4t + 3
-    if (above < kk && kk <= S) {  // exactly one thread
-      int c = above, d = 4 * tid, cnt = h0;
-      if (c + h3 >= kk) {
-        d = 4 * tid + 3, cnt = h3;
-      } else if ((c += h3) + h2 >= kk) {
-        d = 4 * tid + 2, cnt = h2;
-      } else if ((c += h2) + h1 >= kk) {
-        d = 4 * tid + 1, cnt = h1;
-      } else {
-        c += h1;
-      }
-      misc[0] = d;
-      misc[1] = c;
-      misc[2] = cnt;
-    }
-    __syncthreads();
+    crossing_digit(hist, kk, misc, wt);
     const int d = misc[0];
     kk -= misc[1];
     m = misc[2];
@@ -313,11 +388,50 @@ __device__ inline uint64_t block_kth(const uint64_t* A, int n, int kk, int* hist
   return T;
 }
 
+// Logits i = tid, tid + kGsThreads, ... < nre of the listed groups (logit i is offset i % gsp
+// of group sel[i / gsp]), UR at a time with their list reads and loads issued together; keys
+// >= T are appended to A (the first kGsRank values also to vbits) through the counter *np.
+template <bool POW2>
+__device__ __forceinline__ void reread_groups(const float* __restrict__ row, int V, const int* sel, int nre, int gsp,
+                                              uint64_t T, uint64_t* A, uint32_t* vbits, int cap, int* np) {
+  constexpr int UR = 4;
+  const int sh = POW2 ? __builtin_ctz((unsigned)gsp) : 0;
+  for (int i0 = threadIdx.x; i0 < nre; i0 += UR * kGsThreads) {
+    int gi[UR], off[UR], base[UR];
+#pragma unroll
+    for (int u = 0; u < UR; ++u) {
+      const int i = i0 + u * kGsThreads < nre ? i0 + u * kGsThreads : nre - 1;
+      gi[u] = POW2 ? i >> sh : i / gsp;
+      off[u] = POW2 ? i & (gsp - 1) : i - gi[u] * gsp;
+    }
+#pragma unroll
+    for (int u = 0; u < UR; ++u) base[u] = sel[gi[u]];
+    float f[UR];
+    int64_t r[UR];
+#pragma unroll
+    for (int u = 0; u < UR; ++u) {
+      r[u] = i0 + u * kGsThreads < nre ? (int64_t)base[u] * gsp + off[u] : (int64_t)V;
+      f[u] = row[r[u] < V ? r[u] : (int64_t)V - 1];  // always in the row; unused past V
+    }
+#pragma unroll
+    for (int u = 0; u < UR; ++u) {
+      if (r[u] < V) {
+        const uint64_t x = make_key(f[u], (uint32_t)r[u]);
+        if (x >= T) {
+          const int p = atomicAdd(np, 1);
+          if (p < cap) A[p] = x;  // nre <= cap
+          if (p < kGsRank) vbits[p] = __float_as_uint(f[u]);
+        }
+      }
+    }
+  }
+}
+
 // Row blockIdx.x: gkeys[row][0 .. G0) are the largest keys of consecutive groups of gs logits
-// (the last group may be short); P consecutive ones are combined first (groups of P gs
-// logits), so G = ceil(G0 / P) <= kGsMaxKeys and k P gs <= kGsMaxKeys.  Writes the row's top k
-// (k <= 64, k <= V) to idx/val in order.  Dynamic LDS: gs_lds_bytes(max(G, k P gs)).  (A template
-// only so that every file including this header may instantiate it.)
+// (the last group may be short); P consecutive ones are combined first (groups of gsp = P gs
+// logits), so G = ceil(G0 / P) <= kGsMaxGroups and k P gs <= kGsMaxKeys.  Writes the row's top k
+// (k <= 64, k <= V) to idx/val in order.  cap = gs_cap(G, gsp); dynamic LDS gs_lds_bytes(cap).
+// (A template only so that every file including this header may instantiate it.)
 template <int = 0>
 __global__ __launch_bounds__(kGsThreads) void group_select_kernel(const float* __restrict__ logits, int64_t ldl,
                                                                   int V, int k, const uint64_t* __restrict__ gkeys,
@@ -328,80 +442,108 @@ __global__ __launch_bounds__(kGsThreads) void group_select_kernel(const float* _
   uint64_t* A = reinterpret_cast<uint64_t*>(gsmem);
   uint64_t* pool = A + ((cap + 15) & ~15);  // 128-byte aligned for the rank reads
   int* hist = reinterpret_cast<int*>(pool + kGsRank);
-  int* misc = hist + kGsBins;
+  int* misc = hist + kGsHist;
   int* wt = misc + 8;
-  __shared__ int sel[64];
+  __shared__ int sel[kGsSel];
+  __shared__ uint32_t vbits[kGsRank];  // values of the first kGsRank re-read candidates
   __shared__ int nsel, npool;
-  const int m = blockIdx.x, tid = threadIdx.x;
+  const int m = blockIdx.x, tid = threadIdx.x, w = tid >> 6;
   const uint64_t* gk = gkeys + (int64_t)m * G0;
   const float* row = logits + (int64_t)m * ldl;
   const int G = (G0 + P - 1) / P, gsp = gs * P;
-  // group keys: thread t combines the P consecutive keys of groups t, t + kGsThreads, ...,
-  // U groups and 4 keys of each in flight at a time
-  constexpr int U = 8;
-  const int iters = (G + U * kGsThreads - 1) / (U * kGsThreads);
-  for (int it = 0; it < iters; ++it) {
-    uint64_t x[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) x[u] = 0;
-    for (int p0 = 0; p0 < P; p0 += 4) {
-      uint64_t y[U][4];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int g = tid + (it * U + u) * kGsThreads;
-          const int64_t e = (int64_t)g * P + p0 + q;
-          y[u][q] = g < G && p0 + q < P && e < G0 ? gk[e] : 0ull;
-        }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) x[u] = y[u][q] > x[u] ? y[u][q] : x[u];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int g = tid + (it * U + u) * kGsThreads;
-      if (g < G) A[g] = x[u];
-    }
-  }
+  const bool some = k <= G;  // else every group is read again
+  for (int q = tid; q < kGsHist; q += kGsThreads) hist[q] = 0;
   if (tid == 0) {
     nsel = 0;
     npool = 0;
   }
   __syncthreads();
-  // fewer groups than k: all of them (T = 0 is below every real key)
-  const uint64_t T = k <= G ? block_kth(A, G, k, hist, misc, wt, pool) : 0ull;
-  for (int g = tid; g < G; g += kGsThreads)
-    if (A[g] >= T) {
-      const int p = atomicAdd(&nsel, 1);  // exactly min(k, G) groups
-      if (p < 64) sel[p] = g;
-    }
-  __syncthreads();
-  const int nre = (nsel < k ? nsel : k) * gsp;
-  constexpr int UR = 4;
-  for (int i0 = tid; i0 < nre; i0 += UR * kGsThreads) {
-    float f[UR];
-    int64_t r[UR];
+  // group keys: thread t combines the P consecutive keys of groups t + u kGsThreads (u <
+  // kGsKeyRegs: G <= kGsMaxGroups), all of them and 4 keys of each in flight at a time, keeps
+  // them in registers and counts them in the first-digit histogram
+  constexpr int U = kGsKeyRegs;
+  uint64_t mine[U];
 #pragma unroll
-    for (int u = 0; u < UR; ++u) {
-      const int i = i0 + u * kGsThreads;
-      r[u] = i < nre ? (int64_t)sel[i / gsp] * gsp + i % gsp : (int64_t)V;
-      f[u] = r[u] < V ? row[r[u]] : 0.f;
-    }
+  for (int u = 0; u < U; ++u) mine[u] = 0;
+  for (int p0 = 0; p0 < P; p0 += 4) {
+    uint64_t y[U][4];
 #pragma unroll
-    for (int u = 0; u < UR; ++u) {
-      if (r[u] < V) {
-        const uint64_t x = make_key(f[u], (uint32_t)r[u]);
-        if (x >= T) {
-          const int p = atomicAdd(&npool, 1);
-          if (p < cap) A[p] = x;  // nre <= cap
-        }
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int g = tid + u * kGsThreads;
+        const int64_t e = (int64_t)g * P + p0 + q;
+        y[u][q] = g < G && p0 + q < P && e < G0 ? gk[e] : 0ull;
       }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) mine[u] = y[u][q] > mine[u] ? y[u][q] : mine[u];
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int g = tid + u * kGsThreads;
+    if (g < G) {
+      A[g] = mine[u];
+      if (some) atomicAdd(&hist[first_slot(mine[u])], 1);
     }
   }
   __syncthreads();
-  const int n2 = npool < cap ? npool : cap;  // >= k: the selected groups' maxima, or every logit when G < k
+  uint64_t T = 0;  // below every real key
+  if (some) {
+    if (w == 0) first_crossing(hist, k, misc);
+    __syncthreads();
+    const int d = misc[0], admitted = misc[1] + misc[2];  // group keys with a top digit >= d
+    const int capg = cap / gsp < kGsSel ? cap / gsp : kGsSel;
+    if (admitted <= capg)
+      T = (uint64_t)d << 52;  // <= the k-th largest group key
+    else
+      T = block_kth(A, G, k, hist, misc, wt, pool);  // exact (its own histogram rounds)
+  }
+  // the groups whose keys reach T (at most cap / gsp: the admitted ones, k, or G < k)
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int g = tid + u * kGsThreads;
+    if (g < G && mine[u] >= T) {
+      const int p = atomicAdd(&nsel, 1);
+      if (p < kGsSel) sel[p] = g;
+    }
+  }
+  __syncthreads();
+  // their logits, read again by the whole workgroup (a shift instead of a division when the
+  // group size is a power of two); keys >= T are appended to A
+  const int nre = (nsel < kGsSel ? nsel : kGsSel) * gsp;  // <= cap
+  if ((gsp & (gsp - 1)) == 0)
+    reread_groups<true>(row, V, sel, nre, gsp, T, A, vbits, cap, &npool);
+  else
+    reread_groups<false>(row, V, sel, nre, gsp, T, A, vbits, cap, &npool);
+  __syncthreads();
+  const int n2 = npool < cap ? npool : cap;  // >= k: the admitted groups' maxima, or every logit when G < k
+  if (n2 <= kGsRank) {
+    // few candidates: each one's rank among them (the count of larger ones) is its output
+    // position; four threads per candidate, each over every fourth run of 16 keys
+    const int c = tid >> 2, part = tid & 3;
+    uint64_t x = 0;
+    int r = 0;
+    if (c < n2) {
+      x = A[c];
+      for (int j = part * 16; j < n2; j += 64) {
+        uint64_t v[16];
+        load16(A + j, v);  // within A's (cap + 15) & ~15 keys; those at n2 and past are skipped
+#pragma unroll
+        for (int q = 0; q < 16; ++q) r += j + q < n2 && v[q] > x ? 1 : 0;
+      }
+    }
+    r += __shfl_xor(r, 1);
+    r += __shfl_xor(r, 2);
+    if (c < n2 && part == 0 && r < k) {
+      uint32_t j = key_index(x);
+      if (j >= (uint32_t)V) j = (uint32_t)V - 1;  // unreachable: the keys are real logits
+      idx[(int64_t)m * k + r] = (int32_t)j;
+      val[(int64_t)m * k + r] = __uint_as_float(vbits[c]);
+    }
+    return;
+  }
   const uint64_t T2 = block_kth(A, n2, k, hist, misc, wt, pool);
   if (tid == 0) misc[6] = 0;
   if (tid < 64) pool[tid] = 0ull;  // padding of the rank reads
@@ -425,8 +567,8 @@ __global__ __launch_bounds__(kGsThreads) void group_select_kernel(const float* _
 }
 
 // Pre-reduction for G0 group keys of gs logits each: the power of two P that minimises the
-// keys the two radix selections sweep, ceil(G0 / P) group keys plus k P gs re-read logits,
-// among those with both counts <= kGsMaxKeys; 0 when there is none.  (The int4 head's 9496
+// keys the selection sweeps, ceil(G0 / P) group keys plus k P gs re-read logits, among those
+// with at most kGsMaxGroups group keys and kGsMaxKeys re-read logits; 0 when there is none.  (The int4 head's 9496
 // keys of 16 rows at k = 40 take P = 4: 2374 + 2560 keys instead of 9496 + 640.)
 __host__ __device__ inline int gs_prereduce(int64_t G0, int gs, int k) {
   int best = 0;
@@ -434,7 +576,7 @@ __host__ __device__ inline int gs_prereduce(int64_t G0, int gs, int k) {
   for (int64_t P = 1; P <= kGsMaxKeys; P *= 2) {
     const int64_t G = (G0 + P - 1) / P, re = (int64_t)k * P * gs;
     if (re > kGsMaxKeys) break;
-    if (G <= kGsMaxKeys && (best == 0 || G + re < cost)) {
+    if (G <= kGsMaxGroups && (best == 0 || G + re < cost)) {
       best = (int)P;
       cost = G + re;
     }

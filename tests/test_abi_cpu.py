@@ -168,13 +168,13 @@ def test_gemv_topk_argument_errors_and_workspace_query():
     assert g(lg=P + 2) == W4_ERR_ALIGN
     n = ctypes.c_size_t(0)
     assert g(wsb=ctypes.byref(n)) == W4_OK
-    assert n.value == 9496 * 8  # one key per GEMV workgroup of 16 rows (4 waves x 4 rows)
+    assert n.value == 2374 * 8  # one key per 64 logits
     small = ctypes.c_size_t(n.value - 8)
     assert g(ws=P, wsb=ctypes.byref(small)) == W4_ERR_WORKSPACE
     n2 = ctypes.c_size_t(0)
-    assert g(V=100, K=64, k=3, wsb=ctypes.byref(n2)) == W4_OK and n2.value == 13 * 8  # 8 rows per workgroup
+    assert g(V=100, K=64, k=3, wsb=ctypes.byref(n2)) == W4_OK and n2.value == 0  # one selection pass
     n3 = ctypes.c_size_t(0)
-    assert g(V=262144, K=3840, k=64, wsb=ctypes.byref(n3)) == W4_OK and n3.value == 65536 * 8  # 4 rows each
+    assert g(V=262144, K=3840, k=64, wsb=ctypes.byref(n3)) == W4_OK and n3.value == 4096 * 8
 
 
 @pytest.mark.skipif(_has_gpu(), reason="checks the no-device error path")

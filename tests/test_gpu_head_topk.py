@@ -1,9 +1,8 @@
-"""GPU parity of w4_gemv_topk, the int4 LM head with token selection fused into its epilogue.
+"""GPU parity of w4_gemv_topk, the int4 LM head with token selection on the device in one call.
 
 Logits: each within 2e-3 * sum |w x| of the oracle's fp64 sum (every row of the small shapes,
-sampled rows of the vocabulary-sized ones); the fused path's GEMV is w4_gemv's M = 1 kernel, so
-for rows longer than 1024 elements (where w4_gemv takes that kernel too) its logits must equal
-w4_gemv's bit for bit.  Selection: exact on the logits the call wrote (the oracle's stable top-k of those f32
+sampled rows of the vocabulary-sized ones); the call's GEMV is w4_gemv's M = 1 kernel, so its
+logits must equal w4_gemv's bit for bit.  Selection: exact on the logits the call wrote (the oracle's stable top-k of those f32
 values, indices and value bits), and against the fp64 logits by the near-tie rule.  Also ties,
 a workspace full of garbage, two calls sharing one workspace, and sentinel bands around every
 output.
@@ -62,6 +61,9 @@ def head_case(w4, v, kdim, k, seed, rows=None, q=None, s=None, b=None, x=None, w
     torch.cuda.synchronize()
     assert bands_ok(fl, v, -77.0) and bands_ok(fi, k, -3) and bands_ok(fv, k, 55.5), "write outside an output"
     lg, ix, vl = logits.cpu().numpy(), idx.cpu().numpy(), val.cpu().numpy()
+    # logits: w4_gemv's at M = 1, bit for bit
+    y = w4.w4_gemv(qw, sd, bd, dev(x))
+    assert np.array_equal(y.cpu().numpy()[0].view(np.uint32), lg.view(np.uint32))
     # selection: exact on the logits the call wrote
     assert oracle.check_topk_selection(lg[None], ix[None], vl[None], k), (v, kdim, k)
     # logits against fp64 (every row, or a sample)
@@ -81,7 +83,7 @@ def test_head_topk_small_and_ragged(w4, v, kdim, k):
 
 
 @pytest.mark.parametrize("k", [1, 40, 64])
-def test_head_topk_qwen_head_equals_unfused_path(w4, k):
+def test_head_topk_qwen_head_equals_separate_calls(w4, k):
     # the Qwen2.5-3B-sized int4 head: [151936][2048], k = 40 as in the decode step
     v, kdim = synth.QWEN25_3B_VOCAB, synth.QWEN25_3B_HIDDEN
     rows = np.sort(np.random.default_rng(5).choice(v, 512, replace=False))

@@ -729,6 +729,8 @@ def topk_case(w4, logits, k):
     (2, 12293, 64), (3, 4099, 40), (1, 600000, 64), (1, 70000, 63), (2, 8191, 17),
     # either side of the switch to two offered keys per lane (k > 48)
     (1, 300000, 48), (3, 300000, 49), (2, 4096, 49),
+    # 8192 group keys after pre-reduction, the most the selection holds in registers
+    (1, 1048576, 64),
 ])
 def test_topk_random(w4, m, v, k):
     logits = (np.random.default_rng(m * v + k).standard_normal((m, v)) * 0.9).astype(np.float32)
@@ -803,6 +805,36 @@ def test_topk_deterministic(w4):
     a = [to_np(t) for t in w4.logits_argmax_topk(logits, 40)]
     b = [to_np(t) for t in w4.logits_argmax_topk(logits, 40)]
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
+def _bound_row(v, groups, per_group, seed):
+    # background far below 7; per_group[i] values of [7, 7.25) (ties among them) in group
+    # groups[i] (64 logits each)
+    r = np.random.default_rng(seed)
+    row = (r.standard_normal(v) * 0.1).astype(np.float32)
+    j = 0
+    for g, c in zip(groups, per_group):
+        pos = g * 64 + r.choice(64, c, replace=False)
+        row[pos] = 7.0 + (np.arange(j, j + c) % 8) / 32.0
+        j += c
+    return row
+
+
+@pytest.mark.parametrize("ngroups,total", [(256, 256), (257, 257), (40, 256), (40, 257)])
+def test_topk_group_bound_edges(w4, ngroups, total):
+    # the selection's switches on 151936-logit rows at k = 40: every value of [7, 7.5) has the
+    # same first radix digit, so the first-digit bound admits `ngroups` groups (up to 256 are
+    # taken as they are, more make it find the exact k-th group key) holding `total` candidates
+    # (up to 256 are ranked directly, more go through a second radix select); the second row is
+    # ordinary logits
+    v = 151936
+    r = np.random.default_rng(ngroups * 1000 + total)
+    groups = np.sort(r.choice(v // 64, ngroups, replace=False))
+    per = np.full(ngroups, total // ngroups)
+    per[: total % ngroups] += 1
+    rows = np.stack([_bound_row(v, groups, per, ngroups + total),
+                     (r.standard_normal(v) * 0.9).astype(np.float32)])
+    topk_case(w4, rows, 40)
 
 
 # ------------------------------------------------------------- a small decode step
