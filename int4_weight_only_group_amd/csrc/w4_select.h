@@ -205,17 +205,16 @@ __device__ void group_topk(const uint64_t (&key)[E], int k, unsigned char* smem,
 // radix select again.  Every step is exact; values come from the logits (-0.0 stays -0.0).
 constexpr int kGsThreads = 1024;   // threads of the selection workgroup
 constexpr int kGsBins = 4096;      // radix digits of 12 bits (4 bins per thread)
-constexpr int kGsHist = 64 * 65;   // ints of the histogram area (the first round pads rows to 65)
 constexpr int kGsRank = 256;       // matching keys ranked directly from this few on
 constexpr int kGsMaxKeys = 16384;  // group keys (after pre-reduction) / re-read keys in LDS
 constexpr int kGsSel = 256;        // groups admitted by the first-digit bound at most
 constexpr int kGsKeyRegs = 8;      // group keys per thread (held in registers)
 constexpr int kGsMaxGroups = kGsKeyRegs * kGsThreads;  // group keys after pre-reduction
 
-// LDS bytes of group_select_kernel for cap keys: keys, the rank pool, the histogram area, 8
-// ints and kGsThreads / 64 wave totals
+// LDS bytes of group_select_kernel for cap keys: keys, the rank pool, the histogram, 8 ints
+// and kGsThreads / 64 wave totals
 __host__ __device__ constexpr size_t gs_lds_bytes(int cap) {
-  return (size_t)(((cap + 15) & ~15) + kGsRank) * 8 + (size_t)(kGsHist + 8 + kGsThreads / 64) * 4;
+  return (size_t)(((cap + 15) & ~15) + kGsRank) * 8 + (size_t)(kGsBins + 8 + kGsThreads / 64) * 4;
 }
 
 // Keys group_select_kernel holds in LDS for G group keys of gsp logits each: the group keys,
@@ -295,31 +294,32 @@ __device__ __forceinline__ int wave_prefix_sum(int v) {
   return v;
 }
 
-// Slot of a key's first digit (its top 12 bits) in the first-round histogram, transposed and
-// padded: the digit of rank t from the top (t = 4095 - digit), i.e. bin i = t % 64 of lane
-// l = t / 64, sits at 65 i + l.  Lane l of one wave then reads its 64 bins at fixed offsets
-// without bank conflicts, and adjacent digits (where the counts of a row cluster) fall in
-// adjacent banks.
-__device__ __forceinline__ int first_slot(uint64_t x) {
-  const int t = 4095 - (int)(x >> 52);
-  return (t & 63) * 65 + (t >> 6);
-}
+// Slot of a key's first digit (its top 12 bits) in the first-round histogram: its rank from the
+// top, 4095 - digit, so that lane l of one wave holds the 64 slots 64 l .. 64 l + 63 (adjacent
+// digits, where the counts of a row cluster, are adjacent words in distinct banks).
+__device__ __forceinline__ int first_slot(uint64_t x) { return 4095 - (int)(x >> 52); }
 
 // The first round's crossing, by wave 0 alone (no workgroup barrier; hist in the first_slot
-// layout): lane l sums the bins of ranks 64 l .. 64 l + 63; the lane whose prefix sum from the top first reaches kk holds the
-// crossing digit, and the same over that lane's 64 bins (one per lane) finds it.  Writes
+// layout): lane l sums the bins of ranks 64 l .. 64 l + 63 (sixteen 16-byte reads, lane l
+// starting at its (l mod 16)-th, so that each 16 lanes of a read cover all 64 banks); the lane
+// whose prefix sum from the top first reaches kk holds the crossing digit, and the same over
+// that lane's 64 bins (one per lane) finds it.  Writes
 // misc[0] = digit, misc[1] = keys with higher digits, misc[2] = keys with this digit.  At least
 // kk keys must be counted.  Called by the 64 lanes of one wave.
 __device__ inline void first_crossing(const int* hist, int kk, int* misc) {
   const int lane = threadIdx.x & 63;
   int s = 0;
-#pragma unroll 16
-  for (int i = 0; i < 64; ++i) s += hist[i * 65 + lane];
+  const int4* row = reinterpret_cast<const int4*>(hist + lane * 64);
+  int4 v[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = row[(j + lane) & 15];  // the sum's order is free
+#pragma unroll
+  for (int j = 0; j < 16; ++j) s += v[j].x + v[j].y + v[j].z + v[j].w;
   const int pre = wave_prefix_sum(s);
   const uint64_t hit = __ballot(pre >= kk);
   const int L = (int)__builtin_ctzll(hit);  // hit != 0: the total is >= kk
   const int above = __builtin_amdgcn_readlane(pre - s, L);
-  const int c = hist[lane * 65 + L];  // rank 64 L + lane
+  const int c = hist[L * 64 + lane];  // rank 64 L + lane
   const int pre2 = above + wave_prefix_sum(c);
   const uint64_t hit2 = __ballot(pre2 >= kk);
   if (lane == (int)__builtin_ctzll(hit2)) {
@@ -442,7 +442,7 @@ __global__ __launch_bounds__(kGsThreads) void group_select_kernel(const float* _
   uint64_t* A = reinterpret_cast<uint64_t*>(gsmem);
   uint64_t* pool = A + ((cap + 15) & ~15);  // 128-byte aligned for the rank reads
   int* hist = reinterpret_cast<int*>(pool + kGsRank);
-  int* misc = hist + kGsHist;
+  int* misc = hist + kGsBins;
   int* wt = misc + 8;
   __shared__ int sel[kGsSel];
   __shared__ uint32_t vbits[kGsRank];  // values of the first kGsRank re-read candidates
@@ -452,7 +452,8 @@ __global__ __launch_bounds__(kGsThreads) void group_select_kernel(const float* _
   const float* row = logits + (int64_t)m * ldl;
   const int G = (G0 + P - 1) / P, gsp = gs * P;
   const bool some = k <= G;  // else every group is read again
-  for (int q = tid; q < kGsHist; q += kGsThreads) hist[q] = 0;
+#pragma unroll
+  for (int q = 0; q < kGsBins / kGsThreads; ++q) hist[q * kGsThreads + tid] = 0;
   if (tid == 0) {
     nsel = 0;
     npool = 0;
@@ -465,20 +466,28 @@ __global__ __launch_bounds__(kGsThreads) void group_select_kernel(const float* _
   uint64_t mine[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) mine[u] = 0;
-  for (int p0 = 0; p0 < P; p0 += 4) {
-    uint64_t y[U][4];
+  if (P == 1) {  // one key per group: U loads, no combining
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+      const int g = tid + u * kGsThreads;
+      if (g < G) mine[u] = gk[g];
+    }
+  } else {
+    for (int p0 = 0; p0 < P; p0 += 4) {
+      uint64_t y[U][4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int g = tid + u * kGsThreads;
-        const int64_t e = (int64_t)g * P + p0 + q;
-        y[u][q] = g < G && p0 + q < P && e < G0 ? gk[e] : 0ull;
-      }
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+        for (int q = 0; q < 4; ++q) {
+          const int g = tid + u * kGsThreads;
+          const int64_t e = (int64_t)g * P + p0 + q;
+          y[u][q] = g < G && p0 + q < P && e < G0 ? gk[e] : 0ull;
+        }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) mine[u] = y[u][q] > mine[u] ? y[u][q] : mine[u];
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) mine[u] = y[u][q] > mine[u] ? y[u][q] : mine[u];
+    }
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
