@@ -1402,7 +1402,7 @@ def main():
         log(f"single GEMV: lone launch {sg['lone_launch_us_median']} us, steady state {sg['steady_state_us']} us "
             f"({sg['steady_state_gbps']} GB/s)")
         log("heads: " + "; ".join(f"{k_} {v_['us']} us" for k_, v_ in hs.items()))
-        log(f"int4 head + top-{TOPK}: fused {ih['us']} us ({ih['gbps']} GB/s), unfused {ih['unfused_us']} us, "
+        log(f"int4 head + top-{TOPK}: one call {ih['us']} us ({ih['gbps']} GB/s), two calls {ih['two_calls_us']} us, "
             f"parity {'ok' if ih['parity_ok'] else 'FAILED'}")
         log(f"speculative verify: {sv['us']} us, parity {'ok' if sv['parity_ok'] else 'FAILED'}")
         qz = quantize_bench(torch, np, w4, synth, oracle)
