@@ -1,5 +1,5 @@
-// Device helpers for exact top-k selection on 64-bit keys, shared by the top-k kernels and the
-// int4 head's fused selection.
+// Device helpers for exact top-k selection on 64-bit keys: the wave and workgroup selections and
+// the group-maxima selection kernel of topk.hip.
 //
 // Order: value descending, ties to the lower index, -0.0 equal to +0.0.  Each candidate is a
 // 64-bit key (orderable(value) << 32) | ~index whose unsigned order is exactly that order (keys
