@@ -837,6 +837,19 @@ def test_topk_group_bound_edges(w4, ngroups, total):
     topk_case(w4, rows, 40)
 
 
+def test_topk_prereduced_groups_adversarial(w4):
+    # 600000 logits at k = 64: group keys combined in pairs (128-logit groups) before the
+    # selection; all-equal (exact k-th group key, then a second select over 8192 candidates),
+    # a ramp (the first-digit bound admits far more than k candidates) and a row whose top
+    # values are one repeated value in 70 groups, beside ordinary logits
+    v, r = 600000, np.random.default_rng(17)
+    ramp = (np.arange(v, dtype=np.float32) / v)[::-1].copy()
+    rep = (r.standard_normal(v) * 0.1).astype(np.float32)
+    rep[np.sort(r.choice(v // 128, 70, replace=False)) * 128 + 5] = 3.0
+    rows = np.stack([np.full(v, 0.25, np.float32), ramp, rep, (r.standard_normal(v) * 0.9).astype(np.float32)])
+    topk_case(w4, rows, 64)
+
+
 # ------------------------------------------------------------- a small decode step
 
 
