@@ -266,12 +266,11 @@ __global__ __launch_bounds__(kWG) void group_max_kernel(const float* __restrict_
     const uint64_t x = base + j < V ? make_key(v[j], (uint32_t)(base + j)) : 0ull;
     mx = x > mx ? x : mx;
   }
-#pragma unroll
-  for (int o = 1; o <= 2; o <<= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)mx, o), hi = __shfl_xor((uint32_t)(mx >> 32), o);
-    const uint64_t y = ((uint64_t)hi << 32) | lo;
-    mx = y > mx ? y : mx;
-  }
+  // the four lanes of a group are one quad
+  uint64_t y = quad_swap64<0xB1>(mx);
+  mx = y > mx ? y : mx;
+  y = quad_swap64<0x4E>(mx);
+  mx = y > mx ? y : mx;
   const int g = base / 64;
   if ((t & 3) == 0 && g < G) gkeys[(int64_t)m * G + g] = mx;
 }

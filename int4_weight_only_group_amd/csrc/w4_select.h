@@ -37,6 +37,17 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// The value of the lane whose index differs in bit 0 (CTRL 0xB1) or bit 1 (0x4E): a DPP
+// quad permute, every lane of the wave active.
+template <int CTRL>
+__device__ __forceinline__ uint32_t quad_swap(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t quad_swap64(uint64_t v) {
+  return ((uint64_t)quad_swap<CTRL>((uint32_t)(v >> 32)) << 32) | quad_swap<CTRL>((uint32_t)v);
+}
+
 __device__ __forceinline__ uint64_t readlane64(uint64_t v, int src) {
   const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, src);
   const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
@@ -543,8 +554,8 @@ __global__ __launch_bounds__(kGsThreads) void group_select_kernel(const float* _
         for (int q = 0; q < 16; ++q) r += j + q < n2 && v[q] > x ? 1 : 0;
       }
     }
-    r += __shfl_xor(r, 1);
-    r += __shfl_xor(r, 2);
+    r += (int)quad_swap<0xB1>((uint32_t)r);  // the four threads of a candidate are one quad
+    r += (int)quad_swap<0x4E>((uint32_t)r);
     if (c < n2 && part == 0 && r < k) {
       uint32_t j = key_index(x);
       if (j >= (uint32_t)V) j = (uint32_t)V - 1;  // unreachable: the keys are real logits
