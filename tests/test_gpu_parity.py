@@ -583,9 +583,18 @@ def test_gemm_small_m_path(w4, m, n, k):
     gemm_case(w4, m, n, k, seed=m + n + k)
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 1, 1), (16, 1, 2048), (3, 5, 7), (20, 3, 100), (2, 13, 64)])
+@pytest.mark.parametrize("m,n,k", [(1, 1, 1), (16, 1, 2048), (3, 5, 7), (20, 3, 100), (2, 13, 64),
+                                   # 8 consecutive k per thread: several row blocks, a partial
+                                   # second round of 2048 k, one thread's worth of k
+                                   (40, 2, 4104), (17, 1, 8)])
 def test_gemm_plain_path(w4, m, n, k):
     gemm_case(w4, m, n, k, seed=m + n + k)
+
+
+@pytest.mark.parametrize("lda_pad", [8, 1])
+def test_gemm_plain_path_strided_a(w4, lda_pad):
+    # rows of A 16-byte aligned (8 consecutive k per thread) or not (k strided by 256)
+    gemm_case(w4, 33, 3, 1000, seed=lda_pad, lda_pad=lda_pad, ldc_pad=1)
 
 
 def test_gemm_strided_operands(w4):
@@ -597,6 +606,24 @@ def test_gemm_identity_is_exact(w4):
     a = synth.activations(70, 64, seed=3)
     c = gemm_case(w4, 70, 64, 64, seed=3, a=a, bmat=np.eye(64, dtype=np.float16))
     assert np.array_equal(c, a.astype(np.float32))
+
+
+def test_gemm_head_column_slice_full_vocabulary(w4):
+    # the batched-classify step at full width: 16 rows x the yes/no columns of the
+    # [2048][151936] f16 head (B = H + id, ldb = 151936), then the per-row argmax over the two
+    k, v, m = synth.QWEN25_3B_HIDDEN, synth.QWEN25_3B_VOCAB, synth.CLASSIFY_ROWS
+    h = synth.head_f16(k, v, seed=5)
+    ids = synth.class_ids(v)
+    x = synth.activations(m, k, seed=5)
+    hd, xd = dev(h), dev(x)
+    out = torch.empty((m, 2), dtype=torch.float32, device="cuda")
+    for j, i in enumerate(ids):
+        w4.gemm_f16(xd, hd[:, i:i + 1], out=out[:, j:j + 1])
+    idx, _ = w4.logits_argmax_topk(out, 1)
+    c = to_np(out)
+    c_ref, bound = oracle.gemm_ref(x, h[:, list(ids)])
+    assert oracle.check_bound(c, c_ref, bound, RTOL)[0]
+    assert oracle.check_topk_vs_exact(c_ref, to_np(idx), 1)[0]
 
 
 def test_gemm_head_column_slice(w4):
